@@ -1,0 +1,554 @@
+/*
+ * oracle.c - TEST INFRASTRUCTURE ONLY: the plain fp64 CPU oracle.
+ *
+ * Only tests/, the smoke check and the bench's cpu_baseline leg may load this
+ * file's library. It is written for a reader checking it against the pages by
+ * eye: straight loops, fp64 arithmetic, no blocking or fusion. Work is split
+ * over threads only across independent rows, which changes no result.
+ *
+ * Sources (titles of the pages this follows):
+ *  [EAGLE-2 page] "EAGLE-2 심층 아키텍처 ..." (techknowgenie) - the three
+ *     pillars (tree mask injected into the attention kernel, longest accepted
+ *     path), the dynamic-tree section, the reference code's tree-mask loop,
+ *     and the production note on indexing tree masks over paged memory.
+ *  [Sonar page] "Accelerating Sonar through speculation" (Perplexity) - the
+ *     four stages of speculative sampling (longest acceptable prefix, bonus
+ *     token from the logits at the mismatch or the end), draft-target
+ *     acceptance by comparing full distributions.
+ *  [EAGLE-3 page] "論文解説: EAGLE-3 ..." - definition of tau.
+ * Readings where the pages are silent (scale, GQA grouping, root handling,
+ * tie-breaks, the rejection-sampling formula) are stated at each function.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------------ */
+/* small helpers                                                            */
+/* ------------------------------------------------------------------------ */
+
+static double bf16_to_double(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static int resolve_threads(int nthreads) {
+  if (nthreads > 0) return nthreads;
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+typedef void (*range_fn)(void *ctx, int64_t lo, int64_t hi);
+
+typedef struct {
+  range_fn fn;
+  void *ctx;
+  int64_t lo, hi;
+} range_job;
+
+static void *range_worker(void *p) {
+  range_job *j = (range_job *)p;
+  j->fn(j->ctx, j->lo, j->hi);
+  return NULL;
+}
+
+/* Runs fn over [0, n) split into contiguous chunks, one per thread. */
+static void parallel_for(int64_t n, int nthreads, range_fn fn, void *ctx) {
+  int T = resolve_threads(nthreads);
+  if (T > n) T = (int)(n > 0 ? n : 1);
+  if (T <= 1) {
+    fn(ctx, 0, n);
+    return;
+  }
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * T);
+  range_job *jobs = (range_job *)malloc(sizeof(range_job) * T);
+  for (int t = 0; t < T; ++t) {
+    jobs[t].fn = fn;
+    jobs[t].ctx = ctx;
+    jobs[t].lo = n * t / T;
+    jobs[t].hi = n * (t + 1) / T;
+    pthread_create(&th[t], NULL, range_worker, &jobs[t]);
+  }
+  for (int t = 0; t < T; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+}
+
+/* Tree rule shared by every call: parent[b][i] in {-1} U [0, i) (node ids are
+ * assigned in creation order on the EAGLE-2 page, so a parent always precedes
+ * its child); with need_root, parent[b][0] must be -1. */
+static int check_tree(const int32_t *parents, int32_t B, int32_t N, int need_root) {
+  for (int64_t b = 0; b < B; ++b)
+    for (int32_t i = 0; i < N; ++i) {
+      int32_t p = parents[b * N + i];
+      if (p < -1 || p >= i) return TVO_ERR_INVALID_TREE;
+      if (need_root && i == 0 && p != -1) return TVO_ERR_INVALID_TREE;
+    }
+  return TVO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1: ancestor-or-self mask ([EAGLE-2 page], reference code, tree-mask loop:
+ * start at the node itself, mark it, move to its parent, stop past the root) */
+/* ------------------------------------------------------------------------ */
+
+int tvo_build_mask(const int32_t *parents, int32_t B, int32_t N, uint64_t *mask, int32_t *depth) {
+  if (B < 0 || N < 0) return TVO_ERR_INVALID_ARG;
+  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if ((int64_t)B * N == 0) return TVO_OK;
+  if (!parents || !mask) return TVO_ERR_INVALID_ARG;
+  int st = check_tree(parents, B, N, 0);
+  if (st != TVO_OK) return st;
+  const int32_t W = (N + 63) / 64;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int32_t i = 0; i < N; ++i) {
+      uint64_t *row = mask + ((int64_t)b * N + i) * W;
+      for (int32_t w = 0; w < W; ++w) row[w] = 0;
+      int32_t d = -1;
+      int32_t c = i;
+      while (c != -1) {
+        row[c / 64] |= (uint64_t)1 << (c % 64);
+        d += 1;
+        c = parents[b * N + c];
+      }
+      if (depth) depth[b * N + i] = d;
+    }
+  }
+  return TVO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2: tree-masked attention over the paged KV cache                        */
+/*                                                                          */
+/* [EAGLE-2 page], third pillar: every tree node is verified in one target  */
+/* forward, seeing only its causal (ancestor) relations through a 2D tree   */
+/* mask; production note: the mask is indexed directly over paged memory.   */
+/* Readings where the pages are silent:                                     */
+/*  - score s_t = sm_scale * <q, k_t>, softmax over the visible keys, output */
+/*    sum_t w_t v_t (standard scaled dot-product attention);                */
+/*  - GQA: query head h reads KV head h / (Hq/Hkv) (contiguous groups);     */
+/*  - the prefix (L_b cached tokens) is visible to every node; tree node j  */
+/*    sits at token position L_b + j and is visible to node i iff bit j of */
+/*    mask[b][i] is set; node 0 is the root (last verified token, counted   */
+/*    in the tree as in the page's code), so prefix_lens exclude it;        */
+/*  - token t lives in page page_table[b][t/16] at slot t%16, KV layout     */
+/*    [page][kv_head][slot][d].                                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const uint16_t *q, *kp, *vp;
+  int64_t num_pages;
+  const int32_t *page_table;
+  int32_t maxp;
+  const int32_t *prefix_lens;
+  const uint64_t *mask;
+  int32_t B, N, Hq, Hkv, D;
+  double scale;
+  const int32_t *rows;
+  double *out;
+  int32_t max_keys;
+} attn_ctx;
+
+static const uint16_t *kv_row(const attn_ctx *a, const uint16_t *base, int64_t b, int32_t g, int64_t t) {
+  int64_t page = a->page_table[b * a->maxp + t / 16];
+  int64_t slot = t % 16;
+  return base + ((page * a->Hkv + g) * 16 + slot) * a->D;
+}
+
+static void attn_rows(void *vctx, int64_t lo, int64_t hi) {
+  const attn_ctx *a = (const attn_ctx *)vctx;
+  int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (a->max_keys > 0 ? a->max_keys : 1));
+  double *s = (double *)malloc(sizeof(double) * (a->max_keys > 0 ? a->max_keys : 1));
+  double *qd = (double *)malloc(sizeof(double) * a->D);
+  const int32_t W = (a->N + 63) / 64;
+  const int32_t G = a->Hq / a->Hkv;
+  for (int64_t r = lo; r < hi; ++r) {
+    int64_t b, i, h;
+    if (a->rows) {
+      b = a->rows[3 * r];
+      i = a->rows[3 * r + 1];
+      h = a->rows[3 * r + 2];
+    } else {
+      b = r / ((int64_t)a->N * a->Hq);
+      i = (r / a->Hq) % a->N;
+      h = r % a->Hq;
+    }
+    const int32_t g = (int32_t)(h / G);
+    const int64_t L = a->prefix_lens[b];
+    const uint16_t *qr = a->q + ((b * a->N + i) * a->Hq + h) * a->D;
+    for (int32_t d = 0; d < a->D; ++d) qd[d] = bf16_to_double(qr[d]);
+
+    /* visible key positions: the whole prefix, then the tree nodes on the mask */
+    int64_t nk = 0;
+    for (int64_t t = 0; t < L; ++t) keys[nk++] = t;
+    for (int32_t j = 0; j < a->N; ++j) {
+      int visible = 1;
+      if (a->mask) visible = (int)((a->mask[(b * a->N + i) * W + j / 64] >> (j % 64)) & 1u);
+      if (visible) keys[nk++] = L + j;
+    }
+
+    double m = -INFINITY;
+    for (int64_t n = 0; n < nk; ++n) {
+      const uint16_t *kr = kv_row(a, a->kp, b, g, keys[n]);
+      double dot = 0.0;
+      for (int32_t d = 0; d < a->D; ++d) dot += qd[d] * bf16_to_double(kr[d]);
+      s[n] = a->scale * dot;
+      if (s[n] > m) m = s[n];
+    }
+    double Z = 0.0;
+    for (int64_t n = 0; n < nk; ++n) {
+      s[n] = exp(s[n] - m);
+      Z += s[n];
+    }
+    double *o = a->out + r * a->D;
+    for (int32_t d = 0; d < a->D; ++d) o[d] = 0.0;
+    for (int64_t n = 0; n < nk; ++n) {
+      const uint16_t *vr = kv_row(a, a->vp, b, g, keys[n]);
+      const double w = s[n] / Z;
+      for (int32_t d = 0; d < a->D; ++d) o[d] += w * bf16_to_double(vr[d]);
+    }
+    if (nk == 0)
+      for (int32_t d = 0; d < a->D; ++d) o[d] = NAN;
+  }
+  free(keys);
+  free(s);
+  free(qd);
+}
+
+int tvo_attention(const uint16_t *q, const uint16_t *k_pages, const uint16_t *v_pages, int64_t num_pages,
+                  const int32_t *page_table, int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len,
+                  const uint64_t *tree_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                  float sm_scale, const int32_t *rows, int64_t n_rows, double *out, int nthreads) {
+  /* argument rules (same as the library's) */
+  if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_pages < 0 || maxp < 0 || max_prefix_len < 0)
+    return TVO_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return TVO_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return TVO_ERR_UNSUPPORTED;
+  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if (!isfinite(sm_scale)) return TVO_ERR_INVALID_ARG;
+  if ((int64_t)B * N == 0) return TVO_OK;
+  if ((int64_t)maxp * 16 < (int64_t)max_prefix_len + N) return TVO_ERR_INVALID_ARG;
+  if (!q || !k_pages || !v_pages || !page_table || !prefix_lens || !out) return TVO_ERR_INVALID_ARG;
+  /* data rules: prefix lengths within [0, max_prefix_len], every page the
+   * sequence touches inside [0, num_pages) */
+  for (int64_t b = 0; b < B; ++b) {
+    int32_t L = prefix_lens[b];
+    if (L < 0 || L > max_prefix_len) return TVO_ERR_INVALID_ARG;
+    int64_t np = ((int64_t)L + N + 15) / 16;
+    for (int64_t p = 0; p < np; ++p) {
+      int32_t id = page_table[b * maxp + p];
+      if (id < 0 || id >= num_pages) return TVO_ERR_INVALID_ARG;
+    }
+  }
+  if (!rows) n_rows = (int64_t)B * N * Hq;
+  for (int64_t r = 0; rows && r < n_rows; ++r)
+    if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= N || rows[3 * r + 2] < 0 ||
+        rows[3 * r + 2] >= Hq)
+      return TVO_ERR_INVALID_ARG;
+
+  attn_ctx a;
+  a.q = q;
+  a.kp = k_pages;
+  a.vp = v_pages;
+  a.num_pages = num_pages;
+  a.page_table = page_table;
+  a.maxp = maxp;
+  a.prefix_lens = prefix_lens;
+  a.mask = tree_mask;
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.scale = (double)sm_scale;
+  a.rows = rows;
+  a.out = out;
+  a.max_keys = max_prefix_len + N;
+  parallel_for(n_rows, nthreads, attn_rows, &a);
+  return TVO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3: greedy acceptance                                                    */
+/*                                                                          */
+/* [EAGLE-2 page]: the draft proposes tokens by argmax, and the verifier     */
+/* compares the target's logits with the draft tokens and keeps the longest */
+/* accepted path. [Sonar page], four stages: the longest acceptable prefix  */
+/* is kept and the logits at the mismatch (or after the last accepted token)*/
+/* give one more token, so n drafts yield up to n + 1 tokens.               */
+/* Readings:                                                                */
+/*  - y_j = argmax_x logits[b][j][x] in fp32, lowest x on ties, NaN below   */
+/*    every number;                                                         */
+/*  - node c >= 1 matches iff draft_tokens[b][c] == y_{parent[c]};          */
+/*  - result: the longest root path of matching nodes, lexicographically    */
+/*    smallest node sequence on ties; accept_len = path nodes (root + k     */
+/*    accepted) = k + 1, so it counts the bonus token y_{last};             */
+/*  - path[b] = [0, v_1, .., v_k, -1 ...].                                  */
+/* ------------------------------------------------------------------------ */
+
+/* NaN-aware "greater than": a NaN never wins, and anything beats a NaN. */
+static int f32_greater(float a, float b) {
+  if (isnan(a)) return 0;
+  if (isnan(b)) return 1;
+  return a > b;
+}
+
+typedef struct {
+  const float *logits;
+  int64_t V;
+  int32_t *y;
+} argmax_ctx;
+
+static void argmax_rows(void *vctx, int64_t lo, int64_t hi) {
+  const argmax_ctx *a = (const argmax_ctx *)vctx;
+  for (int64_t r = lo; r < hi; ++r) {
+    const float *row = a->logits + r * a->V;
+    int64_t best = 0;
+    for (int64_t x = 1; x < a->V; ++x)
+      if (f32_greater(row[x], row[best])) best = x;
+    a->y[r] = (int32_t)best;
+  }
+}
+
+static int check_tokens(const int32_t *tok, int32_t B, int32_t N, int32_t V) {
+  for (int64_t b = 0; b < B; ++b)
+    for (int32_t i = 1; i < N; ++i)
+      if (tok[b * N + i] < 0 || tok[b * N + i] >= V) return TVO_ERR_INVALID_ARG;
+  return TVO_OK;
+}
+
+int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, const int32_t *parents, int32_t B,
+                      int32_t N, int32_t V, int32_t *accept_len, int32_t *path, int32_t *bonus,
+                      int32_t *target_argmax, int nthreads) {
+  if (B < 0 || V <= 0) return TVO_ERR_INVALID_ARG;
+  if (B == 0) return TVO_OK;
+  if (N < 1) return TVO_ERR_INVALID_ARG;
+  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if (!target_logits || !draft_tokens || !parents || !accept_len || !path || !bonus) return TVO_ERR_INVALID_ARG;
+  int st = check_tree(parents, B, N, 1);
+  if (st != TVO_OK) return st;
+  st = check_tokens(draft_tokens, B, N, V);
+  if (st != TVO_OK) return st;
+
+  int32_t *y = (int32_t *)malloc(sizeof(int32_t) * (size_t)B * N);
+  argmax_ctx ac = {target_logits, V, y};
+  parallel_for((int64_t)B * N, nthreads, argmax_rows, &ac);
+
+  int32_t best[64], next[64];
+  for (int64_t b = 0; b < B; ++b) {
+    const int32_t *par = parents + b * N;
+    const int32_t *tok = draft_tokens + b * N;
+    const int32_t *yb = y + b * N;
+    /* bottom-up: best[i] = most matching nodes on a path below i,
+     * next[i] = the lowest child reaching it */
+    for (int32_t i = N - 1; i >= 0; --i) {
+      best[i] = 0;
+      next[i] = -1;
+      for (int32_t c = i + 1; c < N; ++c) {
+        if (par[c] != i) continue;
+        if (tok[c] != yb[i]) continue;
+        if (1 + best[c] > best[i]) {
+          best[i] = 1 + best[c];
+          next[i] = c;
+        }
+      }
+    }
+    int32_t *pb = path + b * N;
+    for (int32_t i = 0; i < N; ++i) pb[i] = -1;
+    int32_t v = 0, k = 0;
+    pb[0] = 0;
+    while (next[v] >= 0) {
+      v = next[v];
+      pb[++k] = v;
+    }
+    accept_len[b] = k + 1;
+    bonus[b] = yb[v];
+    if (target_argmax)
+      for (int32_t i = 0; i < N; ++i) target_argmax[b * N + i] = yb[i];
+  }
+  free(y);
+  return TVO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O4: stochastic acceptance on a chain                                     */
+/*                                                                          */
+/* [Sonar page], draft-target section: acceptance compares the full draft   */
+/* and target distributions, and the target always adds one token after the */
+/* accepted drafts. [EAGLE-2 page], benchmark discussion: verification is   */
+/* rejection sampling, so the output follows the target's distribution      */
+/* exactly (lossless). The pages cite Leviathan et al. and Chen et al. but  */
+/* print no formula; this is their standard rule, the plainest reading:     */
+/*  - p_j = softmax(target row j / T), q_i = softmax(draft row i / T), fp64;*/
+/*  - node i (i = 1..N-1, token t_i) is accepted iff u[i-1] < p_{i-1}(t_i) /*/
+/*    q_i(t_i); a ratio >= 1 always accepts since u < 1;                    */
+/*  - at the first rejection the next token is drawn from                   */
+/*    r = max(0, p_{i-1} - q_i) by inverse CDF in token order with          */
+/*    theta = u[N-1] * sum(r): the smallest x whose running sum exceeds     */
+/*    theta (the last x with r > 0 if rounding leaves none; p_{i-1} itself  */
+/*    if sum(r) = 0);                                                       */
+/*  - if all drafts are accepted the bonus is the same draw from p_{N-1}.   */
+/* Multi-branch trees are not covered: the pages give no tree rule.         */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const float *logits;
+  int64_t V;
+  double T; /* temperature; z = logit / T */
+  double *m, *Z;
+} softmax_ctx;
+
+static void softmax_stats(void *vctx, int64_t lo, int64_t hi) {
+  const softmax_ctx *a = (const softmax_ctx *)vctx;
+  for (int64_t r = lo; r < hi; ++r) {
+    const float *row = a->logits + r * a->V;
+    double m = -INFINITY;
+    for (int64_t x = 0; x < a->V; ++x) {
+      double z = (double)row[x] / a->T;
+      if (z > m) m = z;
+    }
+    double Z = 0.0;
+    for (int64_t x = 0; x < a->V; ++x) Z += exp((double)row[x] / a->T - m);
+    a->m[r] = m;
+    a->Z[r] = Z;
+  }
+}
+
+static double prob(const float *row, int64_t x, double T, double m, double Z) {
+  return exp((double)row[x] / T - m) / Z;
+}
+
+/* Inverse-CDF draw from weights w(x) (given by the callback) with theta = u * W. */
+typedef double (*weight_fn)(const void *ctx, int64_t x);
+
+static int32_t inverse_cdf(weight_fn w, const void *ctx, int64_t V, double u, double *margin_out) {
+  double W = 0.0;
+  for (int64_t x = 0; x < V; ++x) W += w(ctx, x);
+  double theta = u * W;
+  double cum = 0.0;
+  int32_t pick = -1, last_pos = -1;
+  double margin = INFINITY;
+  for (int64_t x = 0; x < V; ++x) {
+    double wx = w(ctx, x);
+    cum += wx;
+    if (wx > 0.0) last_pos = (int32_t)x;
+    double dist = fabs(cum - theta);
+    if (dist < margin) margin = dist;
+    if (pick < 0 && cum > theta) pick = (int32_t)x;
+  }
+  if (pick < 0) pick = last_pos;
+  if (margin_out) *margin_out = W > 0.0 ? margin / W : 0.0;
+  return pick;
+}
+
+typedef struct {
+  const float *prow, *qrow;
+  double T, mp, Zp, mq, Zq;
+} resid_ctx;
+
+static double residual_w(const void *vc, int64_t x) {
+  const resid_ctx *c = (const resid_ctx *)vc;
+  double d = prob(c->prow, x, c->T, c->mp, c->Zp) - prob(c->qrow, x, c->T, c->mq, c->Zq);
+  return d > 0.0 ? d : 0.0;
+}
+
+static double target_w(const void *vc, int64_t x) {
+  const resid_ctx *c = (const resid_ctx *)vc;
+  return prob(c->prow, x, c->T, c->mp, c->Zp);
+}
+
+int tvo_accept_stochastic(const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
+                          const int32_t *parents, const float *uniforms, int32_t B, int32_t N, int32_t V,
+                          float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus, double *margins,
+                          int nthreads) {
+  if (B < 0 || V <= 0) return TVO_ERR_INVALID_ARG;
+  if (!(temperature > 0.0f) || !isfinite(temperature)) return TVO_ERR_INVALID_ARG;
+  if (B == 0) return TVO_OK;
+  if (N < 1) return TVO_ERR_INVALID_ARG;
+  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if (!target_logits || !draft_logits || !draft_tokens || !parents || !uniforms || !accept_len || !path || !bonus)
+    return TVO_ERR_INVALID_ARG;
+  int st = check_tree(parents, B, N, 1);
+  if (st != TVO_OK) return st;
+  for (int64_t b = 0; b < B; ++b)
+    for (int32_t i = 1; i < N; ++i)
+      if (parents[b * N + i] != i - 1) return TVO_ERR_UNSUPPORTED;
+  st = check_tokens(draft_tokens, B, N, V);
+  if (st != TVO_OK) return st;
+
+  const double T = (double)temperature;
+  const int64_t R = (int64_t)B * N;
+  double *mp = (double *)malloc(sizeof(double) * R), *Zp = (double *)malloc(sizeof(double) * R);
+  double *mq = (double *)malloc(sizeof(double) * R), *Zq = (double *)malloc(sizeof(double) * R);
+  softmax_ctx sp = {target_logits, V, T, mp, Zp};
+  softmax_ctx sq = {draft_logits, V, T, mq, Zq};
+  parallel_for(R, nthreads, softmax_stats, &sp);
+  parallel_for(R, nthreads, softmax_stats, &sq);
+
+  for (int64_t b = 0; b < B; ++b) {
+    const int32_t *tok = draft_tokens + b * N;
+    const float *u = uniforms + b * N;
+    double *mg = margins ? margins + b * N : NULL;
+    if (mg)
+      for (int32_t i = 0; i < N; ++i) mg[i] = INFINITY;
+    int32_t k = 0; /* accepted drafts */
+    int rejected_at = -1;
+    for (int32_t i = 1; i < N; ++i) {
+      const int64_t rp = b * N + (i - 1), rq = b * N + i;
+      double p = prob(target_logits + rp * V, tok[i], T, mp[rp], Zp[rp]);
+      double qv = prob(draft_logits + rq * V, tok[i], T, mq[rq], Zq[rq]);
+      double a = p / qv;
+      if (mg) mg[i - 1] = fabs((double)u[i - 1] - a);
+      if ((double)u[i - 1] < a) {
+        k += 1;
+      } else {
+        rejected_at = i;
+        break;
+      }
+    }
+    double smargin = INFINITY;
+    int32_t pick;
+    if (rejected_at > 0) {
+      const int64_t rp = b * N + (rejected_at - 1), rq = b * N + rejected_at;
+      resid_ctx c = {target_logits + rp * V, draft_logits + rq * V, T, mp[rp], Zp[rp], mq[rq], Zq[rq]};
+      double Rsum = 0.0;
+      for (int64_t x = 0; x < V; ++x) Rsum += residual_w(&c, x);
+      if (Rsum > 0.0)
+        pick = inverse_cdf(residual_w, &c, V, (double)u[N - 1], &smargin);
+      else
+        pick = inverse_cdf(target_w, &c, V, (double)u[N - 1], &smargin);
+    } else {
+      const int64_t rp = b * N + (N - 1);
+      resid_ctx c = {target_logits + rp * V, NULL, T, mp[rp], Zp[rp], 0.0, 1.0};
+      pick = inverse_cdf(target_w, &c, V, (double)u[N - 1], &smargin);
+    }
+    if (mg) mg[N - 1] = smargin;
+    int32_t *pb = path + b * N;
+    for (int32_t i = 0; i < N; ++i) pb[i] = i <= k ? i : -1;
+    accept_len[b] = k + 1;
+    bonus[b] = pick;
+  }
+  free(mp);
+  free(Zp);
+  free(mq);
+  free(Zq);
+  return TVO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O5: tau ([EAGLE-3 page], tree acceptance rate): mean accepted tokens per */
+/* verification cycle; a cycle is one sequence in one accept call.          */
+/* ------------------------------------------------------------------------ */
+
+double tvo_tau(const int32_t *accept_len, int64_t M) {
+  if (M <= 0) return 0.0;
+  int64_t sum = 0;
+  for (int64_t j = 0; j < M; ++j) sum += accept_len[j];
+  return (double)sum / (double)M;
+}
