@@ -1,0 +1,217 @@
+"""Benchmark of the tree-verify hot path on one MI355X.
+
+One step = one verification pass over one batch: tv_build_mask, tv_attention
+(one attention layer) and tv_accept (greedy, or stochastic for the MTP chain
+workload). Inputs are seeded synthetic tensors of the workload's shapes,
+resident in HBM before timing starts. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+--config picks the workload (1..5, default 2: the Llama-3-8B layer shape with
+an EAGLE-2 64-node tree). Only one GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def workload_name(w, c):
+    L = f"L{w.max_prefix_len}" if c["L"] if not isinstance(c["L"], tuple) else False else \
+        f"L~U[{c['L'][0]},{c['L'][1]}]"
+    return (f"cfg{w.cfg} {c['name']}: B{w.B} Hq{w.Hq}/Hkv{w.Hkv} D{w.D} {L} N{w.N} tree={c['tree']} "
+            f"V{w.V} {w.mode}")
+
+
+def attention_bytes(w):
+    """Algorithmic HBM bytes of one tv_attention call: every visible K/V row
+    once, Q once, the output once, masks, page-table entries, prefix lengths."""
+    toks = int((w.prefix_lens.astype(np.int64) + w.N).sum())
+    kv = toks * w.Hkv * w.D * 2 * 2
+    q = w.B * w.N * w.Hq * w.D * 2
+    out = w.B * w.N * w.Hq * w.D * 4
+    pages = int(((w.prefix_lens.astype(np.int64) + w.N + 15) // 16).sum()) * 4
+    return kv + q + out + w.B * w.N * 8 + pages + w.B * 4
+
+
+def attention_flops(w, depth):
+    """4*D flops (QK^T and PV) per visible (query row, key) pair."""
+    vis = (w.prefix_lens.astype(np.int64)[:, None] + depth + 1).sum()  # keys seen by each node
+    return 4 * w.D * w.Hq * int(vis)
+
+
+def accept_bytes(w):
+    if w.mode == "greedy":
+        return w.B * w.N * w.V * 4 + w.B * w.N * 4 * 3
+    # target rows, draft rows 1..N-1, and one re-read of a target and a draft row for the final draw
+    return (w.B * w.N + w.B * (w.N - 1)) * w.V * 4 + 2 * w.B * w.V * 4 + w.B * w.N * 4 * 3
+
+
+def cpu_baseline(w, depth, target_s, threads):
+    """Times the fp64 oracle (attention for every head of the sampled nodes,
+    then their acceptance) on the host, on whole sequences, growing the
+    sample until it takes about `target_s` seconds or covers the batch."""
+    import oracle
+
+    omask, _ = oracle.build_mask(w.parents)
+    nseq, elapsed, done = 1, 0.0, 0
+    while True:
+        rows = np.array([[b, i, h] for b in range(nseq) for i in range(w.N) for h in range(w.Hq)], np.int32)
+        t0 = time.perf_counter()
+        oracle.attention(w, omask, rows=rows, nthreads=threads)
+        if w.mode == "greedy":
+            oracle.accept_greedy(w.target_logits[:nseq], w.draft_tokens[:nseq], w.parents[:nseq], nthreads=threads)
+        else:
+            oracle.accept_stochastic(w.target_logits[:nseq], w.draft_logits[:nseq], w.draft_tokens[:nseq],
+                                     w.parents[:nseq], w.uniforms[:nseq], w.temperature, nthreads=threads)
+        elapsed = time.perf_counter() - t0
+        done = nseq
+        if elapsed >= target_s or nseq >= w.B:
+            break
+        nseq = min(w.B, max(nseq + 1, int(nseq * min(8.0, 1.2 * target_s / max(elapsed, 1e-3)))))
+    return dict(value=done * w.N / elapsed, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{done} of {w.B} sequences ({done * w.N} tree tokens, {done * w.N * w.Hq} attention rows "
+                       f"+ acceptance), {elapsed:.1f} s wall, fp64 C oracle, {threads} threads")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tvgen
+    import tree_verify_attention_attn_amd as tv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    c = tvgen.CONFIGS[args.config]
+    w = tvgen.make_workload(args.config)
+    depth = np.stack([tvgen.tree_depths(p) for p in w.parents])
+
+    def d(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(dtype) if dtype is not None else t).to(dev)
+
+    parents, tokens = d(w.parents), d(w.draft_tokens)
+    q, kp, vp = d(w.q, torch.bfloat16), d(w.k_pages, torch.bfloat16), d(w.v_pages, torch.bfloat16)
+    table, plens = d(w.page_table), d(w.prefix_lens)
+    tl = d(w.target_logits)
+    dl = d(w.draft_logits) if w.draft_logits is not None else None
+    un = d(w.uniforms) if w.uniforms is not None else None
+    mode = tv.GREEDY if w.mode == "greedy" else tv.STOCHASTIC
+    mask = torch.empty((w.B, w.N, 1), dtype=torch.int64, device=dev)
+    dep = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.N, w.Hq, w.D), dtype=torch.float32, device=dev)
+    aws = tv.tv_attention_workspace_bytes(dev, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
+    attn_ws = torch.empty(max(aws, 1), dtype=torch.uint8, device=dev)
+    acc_ws = torch.empty(max(tv.tv_accept_workspace_bytes(w.B, w.N, w.V, mode), 1), dtype=torch.uint8, device=dev)
+    outs = dict(accept_len=torch.empty(w.B, dtype=torch.int32, device=dev),
+                path=torch.empty((w.B, w.N), dtype=torch.int32, device=dev),
+                bonus=torch.empty(w.B, dtype=torch.int32, device=dev))
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        tv.tv_build_mask(parents, mask, dep)
+        if ev:
+            ev[1].record()
+        tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, mask, float(w.sm_scale), out=out,
+                        workspace=attn_ws)
+        if ev:
+            ev[2].record()
+        tv.tv_accept(tl, tokens, parents, mode=mode, draft_logits=dl, uniforms=un, temperature=w.temperature,
+                     outputs=outs, workspace=acc_ws)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tv.tv_tau_reset(dev)
+    if tv.tv_device_error(dev) != 0:
+        raise RuntimeError("device error during warm-up")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tau, cycles = tv.tv_tau(dev)
+    assert tv.tv_device_error(dev) == 0
+
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs]) * 1e-3  # seconds
+    t_mask, t_attn, t_acc = per.mean(0)
+    ms_per_step = wall / args.steps * 1e3
+    tokens = w.B * w.N
+    a_bytes, a_flops, c_bytes = attention_bytes(w), attention_flops(w, depth), accept_bytes(w)
+    kernels = {
+        "tv_build_mask": dict(avg_us=t_mask * 1e6),
+        "tv_attention": dict(avg_us=t_attn * 1e6, bytes=a_bytes, flops=a_flops, gbs=a_bytes / t_attn / 1e9,
+                             hbm_frac=a_bytes / t_attn / 1e9 / HBM_PEAK_GBS,
+                             mfma_frac=a_flops / t_attn / 1e12 / BF16_DENSE_TFLOPS,
+                             tokens_per_s=tokens / t_attn),
+        "tv_accept": dict(avg_us=t_acc * 1e6, bytes=c_bytes, gbs=c_bytes / t_acc / 1e9,
+                          hbm_frac=c_bytes / t_acc / 1e9 / HBM_PEAK_GBS),
+    }
+    dom = "tv_attention" if t_attn >= t_acc else "tv_accept"
+    dk = kernels[dom]
+    result = {
+        "metric": "verified tree tokens/sec per attention layer; achieved HBM GB/s vs peak",
+        "value": tokens * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_name(w, c), "batch": w.B, "tree_nodes": w.N, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "max_prefix_len": w.max_prefix_len, "vocab": w.V,
+                   "accept": w.mode, "page_size": 16, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "note": "achieved = algorithmic bytes per call / mean call duration (HIP events on the "
+                             "launch stream over the timed steps)"},
+        "kernels": kernels,
+        "tau": tau,
+        "tau_cycles": cycles,
+    }
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        result["cpu_baseline"] = cpu_baseline(w, depth, args.cpu_seconds, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * treeverify.h - C ABI of libtreeverify: the verification pass of tree
+ * speculative decoding (EAGLE-2 / EAGLE-3 style) on one AMD Instinct MI355X.
+ *
+ * Sources, by page title:
+ *  [EAGLE-2 page]  "EAGLE-2 심층 아키텍처: 특징 공간(Feature Space) 자동회귀와 동적
+ *                  초안 트리..." (techknowgenie) - third pillar (one target
+ *                  forward verifies every tree node through a 2D tree mask
+ *                  injected into the attention kernel; the longest accepted
+ *                  path is kept), the reference code's tree-mask loop, the
+ *                  benchmark discussion (rejection sampling keeps the output
+ *                  lossless) and the production note on indexing tree masks
+ *                  directly over paged KV memory.
+ *  [Sonar page]    "Accelerating Sonar through speculation" (Perplexity) -
+ *                  four stages of speculative sampling (longest acceptable
+ *                  prefix; the target's logits at the mismatch or the end give
+ *                  one more token), draft-target acceptance by comparing full
+ *                  distributions, and the device-side insertion that avoids a
+ *                  CPU-GPU sync on the accepted length.
+ *  [EAGLE-3 page]  "論文解説: EAGLE-3 - Training-Time Test-Scaling..." - tau,
+ *                  the mean number of tokens accepted per draft/verify cycle.
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless marked (host). The caller allocates
+ *    and owns every buffer, workspaces included; the library never allocates
+ *    device memory in these calls (only tv_create does, 64 bytes).
+ *  - Calls are asynchronous on the context's HIP stream, except tv_tau and
+ *    tv_device_error, which synchronise that stream.
+ *  - Host-detected errors return a status and launch nothing; outputs are
+ *    left untouched.
+ *  - Device-detected bad data (a parent not earlier than its child, a page id
+ *    outside [0, num_pages), a token outside [0, V), a prefix length outside
+ *    [0, max_prefix_len], a non-chain tree in stochastic mode) sets a sticky
+ *    per-context flag read by tv_device_error; the affected outputs are
+ *    written as NaN (attention) or -1 (masks: 0 with depth -1; acceptance).
+ *  - Tree numbering: node ids are topological (parent[i] < i), as in the
+ *    EAGLE-2 page's reference code which numbers nodes in creation order.
+ *    Node 0 is the root: the last verified token, counted in the tree.
+ *  - A context is not thread-safe; use one per stream/thread.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tv_status {
+  TV_OK = 0,
+  TV_ERR_INVALID_ARG = 1,  /* bad scalar, NULL pointer, bad page id / token / prefix length */
+  TV_ERR_INVALID_TREE = 2, /* parent[b][i] outside {-1} U [0, i), or accept root with a parent */
+  TV_ERR_UNSUPPORTED = 3,  /* shape outside what the kernels implement (N > 64, D not 64/128,
+                              stochastic acceptance on a non-chain tree) */
+  TV_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the *_workspace_bytes figure */
+  TV_ERR_HIP = 5           /* HIP runtime error (launch failure, bad device) */
+} tv_status;
+
+typedef enum tv_dtype { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+typedef enum tv_accept_mode { TV_GREEDY = 0, TV_STOCHASTIC = 1 } tv_accept_mode;
+
+typedef struct tv_ctx tv_ctx;
+
+/* Creates a context on `device` bound to `hip_stream` (a hipStream_t; NULL =
+ * the default stream). Allocates 64 bytes of device memory for the tau
+ * counters and the sticky error flag, zeroed. *ctx is host memory. */
+tv_status tv_create(tv_ctx **ctx, int device, void *hip_stream);
+tv_status tv_destroy(tv_ctx *ctx);
+/* Rebinds the context to another stream of the same device. */
+tv_status tv_set_stream(tv_ctx *ctx, void *hip_stream);
+
+/* Ancestor-or-self bitmask of every tree node ([EAGLE-2 page], reference
+ * code, tree-mask assembly: a node's row marks the node, then each parent up
+ * to the root).
+ *   parents  int32 [B][N]: parent id, or -1 for a root (forests allowed).
+ *   mask     uint64 [B][N][W], W = ceil(N/64) (= 1, since N <= 64): bit j
+ *            (position j % 64 of word j / 64, least significant bit = node 0)
+ *            of row (b, i) is set iff j is i or an ancestor of i.
+ *   depth    int32 [B][N] or NULL: number of ancestors (root = 0); a node's
+ *            position id would be prefix_len + depth.
+ * Requires 0 <= N <= 64, B >= 0. Bad parents: sticky TV_ERR_INVALID_TREE and
+ * that sequence's rows are written as mask 0, depth -1. */
+tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, int32_t B, int32_t N, uint64_t *mask,
+                        int32_t *depth);
+
+/* Workspace (bytes) tv_attention needs for these host scalars: fp32 partial
+ * results when one sequence's keys are split over several workgroups. The
+ * split plan depends only on these arguments and the device's CU count, so
+ * repeated calls are bitwise reproducible. May be 0. */
+size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t max_prefix_len);
+
+/* Tree-masked attention over a paged GQA KV cache ([EAGLE-2 page], third
+ * pillar and the production note on paged tree masks).
+ * For sequence b, node i, query head h (KV head g = h / (Hq/Hkv)):
+ *   keys  = prefix tokens t in [0, L_b) and tree tokens t = L_b + j for every
+ *           j whose bit is set in tree_mask[b][i] (all j when tree_mask is
+ *           NULL: the unmasked baseline);
+ *   s_t   = sm_scale * <q, k_t>,  out = sum_t softmax(s)_t v_t.
+ * Token t of sequence b lives in page page_table[b][t / 16], slot t % 16.
+ *   q            bf16 [B][N][Hq][D]
+ *   k_pages      bf16 [num_pages][Hkv][16][D]; v_pages likewise. The tree
+ *                nodes' own K/V are already written at positions L_b..L_b+N-1.
+ *   page_table   int32 [B][maxp]; entries past a sequence's last page unused
+ *   prefix_lens  int32 [B], L_b in [0, max_prefix_len] (root excluded)
+ *   max_prefix_len (host) bound used for planning; maxp * 16 >= max_prefix_len + N
+ *   tree_mask    uint64 [B][N][W] as written by tv_build_mask, or NULL
+ *   out          [B][N][Hq][D] in out_dtype (TV_F32 or TV_BF16)
+ *   workspace    >= tv_attention_workspace_bytes(...) bytes (may be NULL if 0)
+ * Requires D in {64, 128}, Hq % Hkv == 0, 0 <= N <= 64. Accumulates in fp32. */
+tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const void *v_pages, int64_t num_pages,
+                       const int32_t *page_table, int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len,
+                       const uint64_t *tree_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                       float sm_scale, void *out, tv_dtype out_dtype, void *workspace, size_t workspace_bytes);
+
+/* Workspace (bytes) tv_accept needs: per-row partial vocab reductions. */
+size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode mode);
+
+/* Acceptance and bonus token ([EAGLE-2 page], third pillar: longest
+ * accepted path; [Sonar page], four stages: n drafts give up to n + 1 tokens,
+ * the last from the target's logits after the accepted prefix; draft-target
+ * section: acceptance compares the full distributions; [EAGLE-2 page]
+ * benchmark discussion: rejection sampling keeps the output distribution).
+ *   target_logits  fp32 [B][N][V]: row j = target's next-token logits after node j
+ *   draft_logits   fp32 [B][N][V] (stochastic only, else NULL): row i >= 1 =
+ *                  the draft distribution that produced node i's token
+ *   draft_tokens   int32 [B][N]; [b][0] is the root's token (not verified)
+ *   parents        int32 [B][N]; parents[b][0] must be -1
+ *   uniforms       fp32 [B][N] in [0, 1) (stochastic only, else NULL):
+ *                  u[i-1] tests node i, u[N-1] drives the final draw
+ *   temperature    > 0; logits are divided by it (stochastic only)
+ *   accept_len     int32 [B]: root + accepted nodes = accepted drafts + 1
+ *                  (counts the bonus token)
+ *   path           int32 [B][N]: accepted node ids from the root, -1 padded
+ *   bonus_token    int32 [B]
+ *   target_argmax  int32 [B][N] or NULL (greedy only): per-row argmax
+ * GREEDY: y_j = argmax of row j (fp32 compare, lowest index on ties, NaN
+ *   below every number); node c matches iff draft_tokens[c] == y_parent(c);
+ *   the longest root path of matching nodes wins, lexicographically smallest
+ *   node sequence on ties; bonus = y at its last node.
+ * STOCHASTIC (chains only, parents[i] = i-1): p_j = softmax(target row j / T),
+ *   q_i = softmax(draft row i / T) in fp64; node i accepted iff
+ *   u[i-1] < p_{i-1}(t_i) / q_i(t_i), stop at the first rejection; the next
+ *   token is the inverse-CDF draw (token order, theta = u[N-1] * total mass,
+ *   smallest token whose running sum exceeds theta) from max(0, p - q) at the
+ *   rejection (from p if that mass is 0), or from p_{N-1} when all pass.
+ * Adds sum(accept_len) and B to the context's tau counters. Requires
+ * 1 <= N <= 64 when B > 0, V >= 1. */
+tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
+                    const int32_t *parents, const float *uniforms, int32_t B, int32_t N, int32_t V,
+                    tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus_token,
+                    int32_t *target_argmax, void *workspace, size_t workspace_bytes);
+
+/* tau = (sum of accept_len) / (number of sequences verified) since the last
+ * reset ([EAGLE-3 page], tree acceptance rate); 0 when no cycle was counted.
+ * tau and cycles are host pointers (cycles may be NULL). Synchronises. */
+tv_status tv_tau(tv_ctx *ctx, double *tau, uint64_t *cycles);
+tv_status tv_tau_reset(tv_ctx *ctx);
+
+/* Reads and clears the sticky device error flag into *code (host). Synchronises. */
+tv_status tv_device_error(tv_ctx *ctx, int32_t *code);
+
+const char *tv_status_string(tv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

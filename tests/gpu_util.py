@@ -1,0 +1,76 @@
+"""Shared helpers for the GPU parity tests (device transfer, tolerances)."""
+import numpy as np
+import torch
+
+import tree_verify_attention_attn_amd as tv
+
+DEV = torch.device("cuda:0")
+
+# Attention tolerance: an element passes if |got - ref| <= ATOL or
+# |got - ref| <= RTOL * |ref| (bf16 inputs, fp32 accumulation, fp64 oracle).
+ATOL, RTOL = 1e-2, 2e-2
+# Tighter guard for rows with long key lists (prefix >= 64): bf16-rounded
+# probabilities in the P.V product perturb each weight by <= 2^-9 relative,
+# so with weights spread over hundreds of keys and N(0, 1) values the output
+# moves by ~2^-9 * sqrt(sum_t w_t^2 v_t^2) << 1e-3; 2e-3 still flags real
+# indexing errors, which shift outputs by O(0.1).
+TIGHT = 2e-3
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+class DevWorkload:
+    """Device copies of a tvgen.Workload's tensors."""
+
+    def __init__(self, w, kv=True, logits=True):
+        self.w = w
+        self.parents = dev(w.parents)
+        self.draft_tokens = dev(w.draft_tokens)
+        self.page_table = dev(w.page_table)
+        self.prefix_lens = dev(w.prefix_lens)
+        if kv:
+            self.q = dev(w.q, torch.bfloat16)
+            self.k = dev(w.k_pages, torch.bfloat16)
+            self.v = dev(w.v_pages, torch.bfloat16)
+        if logits and w.target_logits is not None:
+            self.target_logits = dev(w.target_logits)
+            self.draft_logits = dev(w.draft_logits) if w.draft_logits is not None else None
+            self.uniforms = dev(w.uniforms) if w.uniforms is not None else None
+
+    def attention(self, mask, out_dtype=torch.float32):
+        w = self.w
+        return tv.tv_attention(self.q, self.k, self.v, self.page_table, self.prefix_lens, w.max_prefix_len, mask,
+                               float(w.sm_scale), out_dtype=out_dtype)
+
+    def accept(self, mode=tv.GREEDY):
+        w = self.w
+        if mode == tv.GREEDY:
+            return tv.tv_accept(self.target_logits, self.draft_tokens, self.parents)
+        return tv.tv_accept(self.target_logits, self.draft_tokens, self.parents, mode=tv.STOCHASTIC,
+                            draft_logits=self.draft_logits, uniforms=self.uniforms, temperature=w.temperature)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def mask_np(mask_t):
+    return host(mask_t).view(np.uint64)
+
+
+def check_attention(got, ref, tight=None, what=""):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    ok = (err <= ATOL) | (err <= RTOL * np.abs(ref))
+    big = np.abs(ref) > 1e-3
+    max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert ok.all(), f"{what}: {int((~ok).sum())} elements out of tolerance, max abs err {err.max():.3e}"
+    if tight is not None:
+        assert err.max() <= tight, f"{what}: max abs err {err.max():.3e} above the {tight} guard"
+    return dict(max_abs=float(err.max()), max_rel=max_rel, pass_frac=float(ok.mean()))

@@ -1,0 +1,183 @@
+"""GPU parity: tv_accept (greedy and stochastic) and tv_tau against the oracle.
+
+Greedy outputs (accept_len, path, bonus, per-row argmax) must be bit-exact.
+Stochastic decisions are taken in fp64 on both sides; they must agree
+exactly wherever the oracle's decision margin exceeds 1e-9 (every seeded case
+here), and the test reports the margins so a near-tie is visible.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tvgen
+import tree_verify_attention_attn_amd as tv
+from gpu_util import DEV, DevWorkload, dev, host
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("accept_len", "path", "bonus", "target_argmax")
+
+
+def greedy_compare(w, what):
+    dw = DevWorkload(w, kv=False)
+    got = dw.accept(tv.GREEDY)
+    assert tv.tv_device_error(DEV) == 0
+    ref = oracle.accept_greedy(w.target_logits, w.draft_tokens, w.parents)
+    for k in KEYS:
+        g = host(got[k])
+        assert (g == ref[k]).all(), f"{what}: {k} differs at {np.argwhere(g != ref[k])[:5].tolist()}"
+    return ref
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("variant", ["random", "planted-full", "planted-partial"])
+def test_greedy_full_size(cfg, variant):
+    w = tvgen.make_workload(cfg, with_kv=False)
+    print(f"[accept] cfg{cfg} {variant} B={w.B} N={w.N} V={w.V}", flush=True)
+    if variant == "planted-full":
+        for b in range(w.B):
+            d = tvgen.tree_depths(w.parents[b])
+            tvgen.plant_full_path(w, b, int(np.argmax(d)))
+    elif variant == "planted-partial":
+        tvgen.plant_random(w, 0.5, seed=cfg)
+    ref = greedy_compare(w, f"cfg{cfg}-{variant}")
+    if variant == "planted-full":
+        depth = np.stack([tvgen.tree_depths(p) for p in w.parents])
+        assert (ref["accept_len"] == depth.max(1) + 1).all()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_greedy_ties_and_duplicate_siblings(seed):
+    # tiny vocab and half-integer logits: exact ties, repeated sibling tokens
+    w = tvgen.make_workload(1, seed=900 + seed, with_kv=False,
+                            overrides=dict(B=200, N=3 + 15 * seed, V=6, max_depth=4))
+    w.target_logits = np.round(w.target_logits * 2) / 2
+    greedy_compare(w, f"ties-{seed}")
+
+
+def test_greedy_odd_vocab_and_nan():
+    # V not a multiple of 4 takes the scalar path; NaN ranks below every number
+    w = tvgen.make_workload(2, with_kv=False, overrides=dict(B=3, V=10007))
+    w.target_logits[0, 0, :50] = np.nan
+    w.target_logits[1, 3, :] = np.nan
+    tvgen.plant_random(w, 0.6)
+    greedy_compare(w, "odd-V-nan")
+
+
+def test_greedy_forest_nodes_never_accepted():
+    w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=8, N=12, tree="forest", V=64))
+    w.parents[:, 0] = -1
+    w.parents[:, 1] = 0
+    w.parents[:, 2] = 1
+    greedy_compare(w, "forest")
+
+
+def test_stochastic_cfg5_full_size():
+    w = tvgen.make_workload(5, with_kv=False)
+    dw = DevWorkload(w, kv=False)
+    got = dw.accept(tv.STOCHASTIC)
+    assert tv.tv_device_error(DEV) == 0
+    ref = oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms,
+                                   w.temperature)
+    m = ref["margins"]
+    print(f"[accept] cfg5 stochastic: min decision margin {np.nanmin(m):.3e}, "
+          f"accept_len histogram {np.bincount(ref['accept_len']).tolist()}", flush=True)
+    assert (m > 1e-9).all()
+    for k in ("accept_len", "path", "bonus"):
+        assert (host(got[k]) == ref[k]).all(), k
+
+
+@pytest.mark.parametrize("variant", ["p-equals-q", "small-vocab", "temperature", "odd-vocab"])
+def test_stochastic_variants(variant):
+    over = dict(B=64)
+    T = 1.0
+    if variant == "small-vocab":
+        over.update(V=7, N=9)
+    if variant == "odd-vocab":
+        over.update(V=12345, N=3)
+    if variant == "temperature":
+        over.update(V=5000)
+    w = tvgen.make_workload(5, seed=55, with_kv=False, overrides=over)
+    if variant == "p-equals-q":
+        w.draft_logits[:, 1:] = w.target_logits[:, :-1]
+    if variant == "temperature":
+        T = 0.7
+        w.temperature = T
+    dw = DevWorkload(w, kv=False)
+    got = dw.accept(tv.STOCHASTIC)
+    assert tv.tv_device_error(DEV) == 0
+    ref = oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms, T)
+    near = (ref["margins"] <= 1e-9).any(1)
+    for k in ("accept_len", "path", "bonus"):
+        g = host(got[k])
+        assert (g[~near] == ref[k][~near]).all(), k
+    if variant == "p-equals-q":
+        assert (ref["accept_len"] == w.N).all()
+
+
+def test_tau_accumulates_over_calls():
+    tv.tv_tau_reset(DEV)
+    lens = []
+    for cfg, seed in ((1, 3), (2, 4), (1, 5)):
+        w = tvgen.make_workload(cfg, seed=seed, with_kv=False, overrides=dict(V=512))
+        tvgen.plant_random(w, 0.7, seed=seed)
+        lens.append(greedy_compare(w, f"tau-{cfg}")["accept_len"])
+    w = tvgen.make_workload(5, with_kv=False, overrides=dict(B=16, V=300))
+    DevWorkload(w, kv=False).accept(tv.STOCHASTIC)
+    lens.append(oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms,
+                                         1.0)["accept_len"])
+    tau, cycles = tv.tv_tau(DEV)
+    all_lens = np.concatenate(lens)
+    assert cycles == all_lens.size
+    assert tau == oracle.tau(all_lens)
+    tv.tv_tau_reset(DEV)
+    assert tv.tv_tau(DEV) == (0.0, 0)
+
+
+def test_device_detected_errors():
+    w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=2, V=100))
+    # bad parent
+    p = w.parents.copy()
+    p[1, 4] = 9
+    st, _ = oracle.status_accept_greedy(w.target_logits, w.draft_tokens, p, w.B, w.N, w.V)
+    dw = DevWorkload(w, kv=False)
+    dw.parents = dev(p)
+    got = dw.accept(tv.GREEDY)
+    assert tv.tv_device_error(DEV) == st == oracle.INVALID_TREE
+    assert host(got["accept_len"])[1] == -1
+    # token out of range
+    t = w.draft_tokens.copy()
+    t[0, 2] = w.V
+    st, _ = oracle.status_accept_greedy(w.target_logits, t, w.parents, w.B, w.N, w.V)
+    dw = DevWorkload(w, kv=False)
+    dw.draft_tokens = dev(t)
+    dw.accept(tv.GREEDY)
+    assert tv.tv_device_error(DEV) == st == oracle.INVALID_ARG
+    # stochastic on a tree
+    w5 = tvgen.make_workload(5, with_kv=False, overrides=dict(B=2, V=100))
+    p5 = w5.parents.copy()
+    p5[:, 3] = 1
+    st, _ = oracle.status_accept_stochastic(w5.target_logits, w5.draft_logits, w5.draft_tokens, p5, w5.uniforms,
+                                            w5.B, w5.N, w5.V, 1.0)
+    dw = DevWorkload(w5, kv=False)
+    dw.parents = dev(p5)
+    got = dw.accept(tv.STOCHASTIC)
+    assert tv.tv_device_error(DEV) == st == oracle.UNSUPPORTED
+    assert (host(got["accept_len"]) == -1).all()
+
+
+def test_host_detected_errors():
+    w = tvgen.make_workload(5, with_kv=False, overrides=dict(B=2, V=100))
+    dw = DevWorkload(w, kv=False)
+    with pytest.raises(tv.TVError) as e:
+        tv.tv_accept(dw.target_logits, dw.draft_tokens, dw.parents, mode=tv.STOCHASTIC, draft_logits=dw.draft_logits,
+                     uniforms=dw.uniforms, temperature=0.0)
+    assert e.value.status == tv.INVALID_ARG
+    with pytest.raises(tv.TVError) as e:
+        tv.tv_accept(dw.target_logits, dw.draft_tokens, dw.parents, mode=tv.STOCHASTIC)
+    assert e.value.status == tv.INVALID_ARG
+    import torch
+    with pytest.raises(tv.TVError) as e:
+        tv.tv_accept(dw.target_logits, dw.draft_tokens, dw.parents,
+                     workspace=torch.empty(8, dtype=torch.uint8, device=DEV))
+    assert e.value.status == tv.WORKSPACE

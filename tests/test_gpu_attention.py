@@ -1,0 +1,154 @@
+"""GPU parity: tv_attention against the fp64 oracle on the same seeded inputs.
+
+Small cases are compared in full (several tiles, ragged tails, special
+trees, edge shapes); the five full-size configurations are compared on
+sampled rows in the launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tvgen
+import tree_verify_attention_attn_amd as tv
+from gpu_util import DEV, TIGHT, DevWorkload, check_attention, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def small(tree, *, B=3, Hq=8, Hkv=2, D=128, L=(0, 300), N=20, seed=5, max_depth=5):
+    return tvgen.make_workload(1, seed=seed, with_logits=False,
+                               overrides=dict(B=B, Hq=Hq, Hkv=Hkv, D=D, L=L, N=N, tree=tree, pages="permuted",
+                                              max_depth=max_depth))
+
+
+def run_full(w, use_mask=True, out_dtype=torch.float32):
+    dw = DevWorkload(w, logits=False)
+    mask = tv.tv_build_mask(dw.parents)[0] if use_mask else None
+    out = dw.attention(mask, out_dtype=out_dtype)
+    om = oracle.build_mask(w.parents)[0] if use_mask else None
+    ref = oracle.attention(w, om)
+    assert tv.tv_device_error(DEV) == 0
+    return host(out.float()), ref
+
+
+SMALL_CASES = [
+    ("random-D128-G4", dict(tree="random")),
+    ("random-D64-G1", dict(tree="random", D=64, Hq=4, Hkv=4)),
+    ("random-D64-G8", dict(tree="random", D=64, Hq=16, Hkv=2, N=33)),
+    ("chain", dict(tree="chain", N=16)),
+    ("star", dict(tree="star", N=31)),
+    ("forest", dict(tree="forest", N=12)),
+    ("dynamic-N64", dict(tree="random", N=64, max_depth=8, L=(100, 700))),
+    ("prefix-0", dict(tree="random", L=0)),
+    ("decode-N1", dict(tree="chain", N=1, L=(1, 200))),
+    ("ragged-long", dict(tree="random", B=5, L=(1, 3000), N=7)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_small_cases_full_compare(name, kw):
+    w = small(**kw)
+    print(f"[attn] {name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} D={w.D} L={w.prefix_lens.tolist()}", flush=True)
+    got, ref = run_full(w)
+    check_attention(got, ref, what=name)
+
+
+def test_all_visible_baseline():
+    w = small("random", N=24)
+    got, ref = run_full(w, use_mask=False)
+    check_attention(got, ref, what="mask=NULL")
+
+
+def test_bf16_output():
+    w = small("random", N=24)
+    got, ref = run_full(w, out_dtype=torch.bfloat16)
+    check_attention(got, ref, what="bf16 out")
+
+
+def test_deterministic_and_page_permutation_invariant():
+    w = small("random", N=30, L=(500, 900), seed=8)
+    dw = DevWorkload(w, logits=False)
+    mask = tv.tv_build_mask(dw.parents)[0]
+    a = host(dw.attention(mask))
+    b = host(dw.attention(mask))
+    assert np.array_equal(a, b), "two identical calls differ"
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(w.num_pages).astype(np.int32)
+    k2, v2 = np.empty_like(w.k_pages), np.empty_like(w.v_pages)
+    k2[perm], v2[perm] = w.k_pages, w.v_pages
+    w.k_pages, w.v_pages = k2, v2
+    w.page_table = np.where(w.page_table >= 0, perm[np.maximum(w.page_table, 0)], -1).astype(np.int32)
+    c = host(DevWorkload(w, logits=False).attention(mask))
+    assert np.array_equal(a, c), "page relocation changed the result"
+
+
+def sample_rows(w, n, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.stack([rng.integers(0, w.B, n), rng.integers(0, w.N, n), rng.integers(0, w.Hq, n)], 1)
+    # always include the first and last row of every sequence's tree
+    extra = [[b, i, h] for b in range(w.B) for i in (0, w.N - 1) for h in (0, w.Hq - 1)]
+    return np.concatenate([rows, np.array(extra)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("cfg,n", [(1, None), (2, 3000), (3, 2000), (4, 300), (5, 3000)])
+def test_full_size_configs_sampled(cfg, n):
+    w = tvgen.make_workload(cfg, with_logits=False)
+    print(f"[attn] cfg{cfg} full size, sampled rows {n}", flush=True)
+    dw = DevWorkload(w, logits=False)
+    mask = tv.tv_build_mask(dw.parents)[0]
+    out = host(dw.attention(mask))
+    assert tv.tv_device_error(DEV) == 0
+    om = oracle.build_mask(w.parents)[0]
+    if n is None:
+        check_attention(out, oracle.attention(w, om), tight=TIGHT, what=f"cfg{cfg}")
+        return
+    rows = sample_rows(w, n, seed=cfg)
+    ref = oracle.attention(w, om, rows=rows)
+    got = out[rows[:, 0], rows[:, 1], rows[:, 2]]
+    check_attention(got, ref, tight=TIGHT, what=f"cfg{cfg}")
+
+
+def test_device_detected_bad_page_and_length():
+    w = small("random", N=10, L=(40, 90), B=2)
+    bad = w.page_table.copy()
+    bad[1, 1] = w.num_pages + 5
+    st, _ = oracle.status_attention(w.q, w.k_pages, w.v_pages, bad, w.prefix_lens, None, B=w.B, N=w.N, Hq=w.Hq,
+                                    Hkv=w.Hkv, D=w.D, sm_scale=w.sm_scale)
+    dw = DevWorkload(w, logits=False)
+    dw.page_table = dev(bad)
+    out = host(dw.attention(None))
+    assert tv.tv_device_error(DEV) == st == oracle.INVALID_ARG
+    assert np.isnan(out[1]).all()
+    assert np.isfinite(out[0]).all()
+    dw = DevWorkload(w, logits=False)
+    pl = w.prefix_lens.copy()
+    pl[0] = w.max_prefix_len + 1
+    dw.prefix_lens = dev(pl)
+    out = host(dw.attention(None))
+    assert tv.tv_device_error(DEV) == oracle.INVALID_ARG
+    assert np.isnan(out[0]).all()
+
+
+def test_host_detected_errors():
+    w = small("random", N=10, L=(40, 90), B=2)
+    dw = DevWorkload(w, logits=False)
+
+    def call(**kw):
+        args = dict(q=dw.q, k_pages=dw.k, v_pages=dw.v, page_table=dw.page_table, prefix_lens=dw.prefix_lens,
+                    max_prefix_len=w.max_prefix_len, tree_mask=None, sm_scale=float(w.sm_scale))
+        args.update(kw)
+        with pytest.raises(tv.TVError) as e:
+            tv.tv_attention(**args)
+        return e.value.status
+
+    assert call(max_prefix_len=w.page_table.shape[1] * 16) == tv.INVALID_ARG  # pages cannot hold L + N
+    assert call(q=dw.q[:, :, :7].contiguous()) == tv.INVALID_ARG  # Hq % Hkv != 0
+    q96 = torch.zeros((w.B, w.N, w.Hq, 96), dtype=torch.bfloat16, device=DEV)
+    k96 = torch.zeros((w.num_pages, w.Hkv, 16, 96), dtype=torch.bfloat16, device=DEV)
+    assert call(q=q96, k_pages=k96, v_pages=k96) == tv.UNSUPPORTED
+    assert call(sm_scale=float("nan")) == tv.INVALID_ARG
+    need = tv.tv_attention_workspace_bytes(DEV, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
+    if need > 0:
+        assert call(workspace=torch.empty(need - 1, dtype=torch.uint8, device=DEV)) == tv.WORKSPACE
+    assert tv.tv_device_error(DEV) == 0

@@ -1,0 +1,48 @@
+"""CPU-only checks of the C ABI library: it loads, exports every function
+include/treeverify.h declares, answers host-only queries, and the product
+path never reaches the oracle. No compute call is made (no GPU here)."""
+import glob
+import os
+import re
+
+import tree_verify_attention_attn_amd as tv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        names |= set(re.findall(r"\b(tv_[a-z_]+)\s*\(", open(h).read()))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tv.library()
+    names = declared_functions()
+    assert {"tv_create", "tv_build_mask", "tv_attention", "tv_accept", "tv_tau"} <= names
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_host_queries():
+    lib = tv.library()
+    for s in range(6):
+        assert lib.tv_status_string(s)
+    # accept workspace: greedy = B*N*chunks 64-bit keys, stochastic = B*N*2*chunks*(m, Z) doubles
+    chunks = (128256 + 8191) // 8192
+    assert tv.tv_accept_workspace_bytes(8, 64, 128256, tv.GREEDY) == 8 * 64 * chunks * 8
+    assert tv.tv_accept_workspace_bytes(128, 5, 32000, tv.STOCHASTIC) == 128 * 5 * 2 * 4 * 16
+    assert tv.tv_accept_workspace_bytes(0, 5, 32000, tv.GREEDY) == 0
+    # a NULL context is rejected before anything touches a device
+    assert lib.tv_build_mask(None, None, 1, 1, None, None) == tv.INVALID_ARG
+    assert lib.tv_tau_reset(None) == tv.INVALID_ARG
+
+
+def test_product_path_never_loads_the_oracle():
+    pkg = os.path.join(ROOT, "tree_verify_attention_attn_amd")
+    for f in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if f.endswith((".py", ".hip", ".h", ".cpp")):
+            text = open(f).read()
+            assert not re.search(r"\boracle\b", text), f
+            assert "tvgen" not in text, f

@@ -1,0 +1,408 @@
+// accept.hip - acceptance of the draft tree and the bonus token.
+//
+// Greedy (EAGLE-2 deep-dive page, third pillar: compare the target's logits
+// with the draft tokens and keep the longest accepted path; Sonar page, four
+// stages: the logits after the accepted prefix give one more token):
+//   pass 1  vocab-chunked argmax per (sequence, node) row. Each workgroup
+//           reduces a 8192-entry chunk to one packed 64-bit key
+//           (order-preserving float bits << 32 | ~index), so a plain max picks
+//           the largest value and, among equal values, the lowest index.
+//   pass 2  one wavefront per sequence, lane = node: merge the chunk keys,
+//           rebuild ancestor masks by pointer doubling, and mark a node ok
+//           when every node on its root path matches. The accepted path ends
+//           at the deepest ok node; among equally deep ones the
+//           lexicographically smallest root path is the one whose ancestor
+//           mask has the larger bit-reversed value (node ids increase along a
+//           path, so the first differing path element is the lowest
+//           differing mask bit). Path, length, bonus and tau counters follow.
+// Stochastic (Sonar page, draft-target section: acceptance compares the full
+// draft and target distributions; EAGLE-2 page: rejection sampling keeps the
+// target distribution) on chains:
+//   pass 1  per-chunk max and sum of exp (fp64) of logits / T, target and draft
+//   pass 2  one workgroup per sequence: merge the chunk statistics, test
+//           u[i-1] < p_{i-1}(t_i) / q_i(t_i) node by node, then one
+//           inverse-CDF draw over max(0, p - q) (or p) with theta = u[N-1] * mass.
+#include <math.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+
+namespace {
+
+constexpr int kChunk = 8192;  // vocab entries per pass-1 workgroup
+constexpr int kThreads = 256;
+
+__device__ inline uint32_t orderable(float f) {
+  if (isnan(f)) return 0u;  // NaN ranks below every number
+  // -0 and +0 compare equal in fp32, so they must map to one key (the tie then
+  // goes to the lower index)
+  const uint32_t u = f == 0.0f ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline unsigned long long pack_key(float v, int x) {
+  return (static_cast<unsigned long long>(orderable(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(x));
+}
+
+__device__ inline unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+template <bool kVec>
+__global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__restrict__ logits, int V, int chunks,
+                                                                unsigned long long *__restrict__ keys) {
+  __shared__ unsigned long long red[kThreads / 64];
+  const int chunk = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const float *p = logits + row * V;
+  const int x0 = chunk * kChunk;
+  const int x1 = min(x0 + kChunk, V);
+  unsigned long long best = 0ull;
+  if (kVec) {
+    for (int x = x0 + threadIdx.x * 4; x < x1; x += kThreads * 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(p + x);
+      best = umax64(best, pack_key(v.x, x));
+      best = umax64(best, pack_key(v.y, x + 1));
+      best = umax64(best, pack_key(v.z, x + 2));
+      best = umax64(best, pack_key(v.w, x + 3));
+    }
+  } else {
+    for (int x = x0 + threadIdx.x; x < x1; x += kThreads) best = umax64(best, pack_key(p[x], x));
+  }
+  for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kThreads / 64; ++i) best = umax64(best, red[i]);
+    keys[row * chunks + chunk] = best;
+  }
+}
+
+// One wavefront per sequence; lane = node.
+__global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long long *__restrict__ keys, int chunks,
+                                                          const int32_t *__restrict__ draft_tokens,
+                                                          const int32_t *__restrict__ parents, int B, int N, int V,
+                                                          int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+                                                          int32_t *__restrict__ bonus,
+                                                          int32_t *__restrict__ target_argmax,
+                                                          unsigned long long *state) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const bool live = lane < N;
+  const int64_t idx = static_cast<int64_t>(b) * N + lane;
+  int y = 0;
+  if (live) {
+    unsigned long long best = 0ull;
+    for (int c = 0; c < chunks; ++c) best = umax64(best, keys[idx * chunks + c]);
+    y = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
+  }
+  const int par = live ? parents[idx] : -1;
+  const int tok = live ? draft_tokens[idx] : 0;
+  const bool bad_tree = live && (par < -1 || par >= lane || (lane == 0 && par != -1));
+  const bool bad_tok = live && lane > 0 && (tok < 0 || tok >= V);
+  const bool tree_err = __ballot(bad_tree) != 0;
+  const bool tok_err = __ballot(bad_tok) != 0;
+  if (tree_err || tok_err) {
+    if (lane == 0) raise_error(state, tree_err ? TV_ERR_INVALID_TREE : TV_ERR_INVALID_ARG);
+    if (live) {
+      path[idx] = -1;
+      if (target_argmax) target_argmax[idx] = y;
+    }
+    if (lane == 0) {
+      accept_len[b] = -1;
+      bonus[b] = -1;
+    }
+    return;
+  }
+  // ancestor-or-self masks by pointer doubling (parents precede children)
+  unsigned long long anc = live ? (1ull << lane) : 0ull;
+  int jump = live ? par : -1;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = jump >= 0 ? jump : lane;
+    const unsigned long long a_src = shfl_u64(anc, src);
+    const int j_src = __shfl(jump, src);
+    if (jump >= 0) {
+      anc |= a_src;
+      jump = j_src;
+    }
+  }
+  // node c >= 1 matches iff its token is the target's argmax at its parent
+  const int y_par = __shfl(y, par >= 0 ? par : 0);
+  const bool match = live && (lane == 0 || (par >= 0 && tok == y_par));
+  const unsigned long long match_bits = __ballot(match);
+  const bool ok = live && (anc & 1ull) && ((anc & ~match_bits) == 0ull);
+  // deepest ok node; ties -> lexicographically smallest root path
+  int depth = ok ? __popcll(anc) : 0;
+  int dmax = depth;
+  for (int m = 32; m >= 1; m >>= 1) dmax = max(dmax, __shfl_xor(dmax, m));
+  unsigned long long key = (ok && depth == dmax) ? __brevll(anc) : 0ull;
+  for (int m = 32; m >= 1; m >>= 1) key = umax64(key, shfl_xor_u64(key, m));
+  const unsigned long long chosen = __brevll(key);  // the chosen path's node set; always holds node 0
+  const int len = __popcll(chosen);
+  const int last = 63 - __clzll(static_cast<long long>(chosen));
+  const int y_last = __shfl(y, last);
+  if (live) {
+    // lane p writes the p-th node of the path (the p-th set bit of `chosen`)
+    int node = -1;
+    if (lane < len) {
+      unsigned long long rest = chosen;
+      for (int q = 0; q < lane; ++q) rest &= rest - 1ull;
+      node = __ffsll(static_cast<long long>(rest)) - 1;
+    }
+    path[idx] = node;
+    if (target_argmax) target_argmax[idx] = y;
+  }
+  if (lane == 0) {
+    accept_len[b] = len;
+    bonus[b] = y_last;
+    atomicAdd(state + 0, static_cast<unsigned long long>(len));
+    atomicAdd(state + 1, 1ull);
+  }
+}
+
+// ---------------------------------------------------------------- stochastic
+
+template <bool kVec>
+__global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__restrict__ target,
+                                                                 const float *__restrict__ draft, int N, int V,
+                                                                 int chunks, double T,
+                                                                 double *__restrict__ stats) {
+  __shared__ double red[kThreads / 64];
+  const int chunk = blockIdx.x;
+  const int64_t row = blockIdx.y;  // b * N + j
+  const int which = blockIdx.z;    // 0 = target, 1 = draft
+  const int j = static_cast<int>(row % N);
+  double *out = stats + ((row * 2 + which) * chunks + chunk) * 2;
+  if (which == 1 && j == 0) {  // draft row 0 is never used
+    if (threadIdx.x == 0) {
+      out[0] = 0.0;
+      out[1] = 0.0;
+    }
+    return;
+  }
+  const float *p = (which ? draft : target) + row * V;
+  const int x0 = chunk * kChunk;
+  const int x1 = min(x0 + kChunk, V);
+  constexpr int kPer = kChunk / kThreads;  // 32 values per thread, kept in registers
+  float vals[kPer];
+  int cnt = 0;
+  if (kVec) {
+#pragma unroll
+    for (int it = 0; it < kPer / 4; ++it) {
+      const int x = x0 + (it * kThreads + threadIdx.x) * 4;
+      float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (x < x1) v = *reinterpret_cast<const float4 *>(p + x);
+      vals[it * 4 + 0] = v.x;
+      vals[it * 4 + 1] = v.y;
+      vals[it * 4 + 2] = v.z;
+      vals[it * 4 + 3] = v.w;
+    }
+    cnt = kPer;
+  } else {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int x = x0 + it * kThreads + threadIdx.x;
+      vals[it] = x < x1 ? p[x] : -INFINITY;
+    }
+    cnt = kPer;
+  }
+  double mx = -INFINITY;
+  for (int it = 0; it < cnt; ++it) mx = fmax(mx, static_cast<double>(vals[it]) / T);
+  for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int i = 1; i < kThreads / 64; ++i) mx = fmax(mx, red[i]);
+  __syncthreads();
+  double z = 0.0;
+  for (int it = 0; it < cnt; ++it) {
+    if (vals[it] != -INFINITY) z += exp(static_cast<double>(vals[it]) / T - mx);
+  }
+  for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = z;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < kThreads / 64; ++i) tot += red[i];
+    out[0] = mx;
+    out[1] = tot;
+  }
+}
+
+struct RowStat {
+  double m, Z;
+};
+
+__device__ inline RowStat merge_stats(const double *stats, int64_t row, int which, int chunks) {
+  const double *s = stats + (row * 2 + which) * chunks * 2;
+  double M = -INFINITY;
+  for (int c = 0; c < chunks; ++c) M = fmax(M, s[2 * c]);
+  double Z = 0.0;
+  for (int c = 0; c < chunks; ++c) {
+    if (s[2 * c + 1] > 0.0) Z += s[2 * c + 1] * exp(s[2 * c] - M);
+  }
+  return RowStat{M, Z};
+}
+
+__device__ inline double prob_at(const float *row, int x, double T, RowStat st) {
+  return exp(static_cast<double>(row[x]) / T - st.m) / st.Z;
+}
+
+__global__ void __launch_bounds__(kThreads) stochastic_path_kernel(
+    const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
+    const int32_t *__restrict__ parents, const float *__restrict__ uniforms, int B, int N, int V, int chunks,
+    double T, const double *__restrict__ stats, int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+    int32_t *__restrict__ bonus, unsigned long long *state) {
+  __shared__ int s_err, s_k, s_rej;
+  __shared__ double s_part[kThreads];
+  __shared__ int s_pick, s_lastpos;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t base = static_cast<int64_t>(b) * N;
+  if (tid == 0) {
+    int err = 0;
+    for (int i = 0; i < N && !err; ++i) {
+      const int p = parents[base + i];
+      if (p < -1 || p >= i || (i == 0 && p != -1)) err = TV_ERR_INVALID_TREE;
+    }
+    for (int i = 1; i < N && !err; ++i)
+      if (parents[base + i] != i - 1) err = TV_ERR_UNSUPPORTED;
+    for (int i = 1; i < N && !err; ++i) {
+      const int t = draft_tokens[base + i];
+      if (t < 0 || t >= V) err = TV_ERR_INVALID_ARG;
+    }
+    s_err = err;
+    if (!err) {
+      // sequential chain test: node i accepted iff u[i-1] < p_{i-1}(t_i) / q_i(t_i)
+      int k = 0, rej = -1;
+      for (int i = 1; i < N; ++i) {
+        const int t = draft_tokens[base + i];
+        const RowStat sp = merge_stats(stats, base + i - 1, 0, chunks);
+        const RowStat sq = merge_stats(stats, base + i, 1, chunks);
+        const double pa = prob_at(target + (base + i - 1) * V, t, T, sp);
+        const double qa = prob_at(draft + (base + i) * V, t, T, sq);
+        if (static_cast<double>(uniforms[base + i - 1]) < pa / qa) {
+          ++k;
+        } else {
+          rej = i;
+          break;
+        }
+      }
+      s_k = k;
+      s_rej = rej;
+    }
+    s_pick = 0x7FFFFFFF;
+    s_lastpos = -1;
+  }
+  __syncthreads();
+  if (s_err) {
+    if (tid == 0) {
+      raise_error(state, s_err);
+      accept_len[b] = -1;
+      bonus[b] = -1;
+    }
+    for (int i = tid; i < N; i += kThreads) path[base + i] = -1;
+    return;
+  }
+  const int k = s_k, rej = s_rej;
+  const int prow = rej > 0 ? rej - 1 : N - 1;
+  const float *P = target + (base + prow) * V;
+  const float *Q = rej > 0 ? draft + (base + rej) * V : nullptr;
+  const RowStat sp = merge_stats(stats, base + prow, 0, chunks);
+  const RowStat sq = Q ? merge_stats(stats, base + rej, 1, chunks) : RowStat{0.0, 1.0};
+  const double u = static_cast<double>(uniforms[base + N - 1]);
+  // contiguous segment per thread, in token order
+  const int seg = (V + kThreads - 1) / kThreads;
+  const int x0 = min(tid * seg, V), x1 = min(x0 + seg, V);
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool residual = Q != nullptr && pass == 0;
+    double local = 0.0;
+    int lastpos = -1;
+    for (int x = x0; x < x1; ++x) {
+      double w = prob_at(P, x, T, sp);
+      if (residual) w = fmax(0.0, w - prob_at(Q, x, T, sq));
+      local += w;
+      if (w > 0.0) lastpos = x;
+    }
+    s_part[tid] = local;
+    __syncthreads();
+    // exclusive prefix of the thread partials (sequential over threads, fixed order)
+    double prefix = 0.0, total = 0.0;
+    for (int i = 0; i < kThreads; ++i) {
+      if (i < tid) prefix += s_part[i];
+      total += s_part[i];
+    }
+    if (residual && !(total > 0.0)) {
+      __syncthreads();
+      continue;  // no residual mass: draw from p instead
+    }
+    const double theta = u * total;
+    double run = prefix;
+    for (int x = x0; x < x1; ++x) {
+      double w = prob_at(P, x, T, sp);
+      if (residual) w = fmax(0.0, w - prob_at(Q, x, T, sq));
+      run += w;
+      if (run > theta) {
+        atomicMin(&s_pick, x);
+        break;
+      }
+    }
+    if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
+    __syncthreads();
+    break;
+  }
+  if (tid == 0) {
+    const int pick = s_pick != 0x7FFFFFFF ? s_pick : s_lastpos;
+    accept_len[b] = k + 1;
+    bonus[b] = pick;
+    atomicAdd(state + 0, static_cast<unsigned long long>(k + 1));
+    atomicAdd(state + 1, 1ull);
+  }
+  for (int i = tid; i < N; i += kThreads) path[base + i] = i <= k ? i : -1;
+}
+
+}  // namespace
+
+size_t accept_ws_bytes(int B, int N, int V, tv_accept_mode mode) {
+  const int chunks = (V + kChunk - 1) / kChunk;
+  const size_t rows = static_cast<size_t>(B) * N;
+  return mode == TV_GREEDY ? rows * chunks * sizeof(unsigned long long) : rows * 2 * chunks * 2 * sizeof(double);
+}
+
+tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits,
+                        const int32_t *draft_tokens, const int32_t *parents, const float *uniforms, int B, int N,
+                        int V, tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path,
+                        int32_t *bonus, int32_t *target_argmax, void *workspace) {
+  const int chunks = (V + kChunk - 1) / kChunk;
+  const dim3 blk(kThreads);
+  const bool vec = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0 &&
+                   (draft_logits == nullptr || (reinterpret_cast<uintptr_t>(draft_logits) & 15) == 0);
+  if (mode == TV_GREEDY) {
+    auto *keys = static_cast<unsigned long long *>(workspace);
+    const dim3 g1(chunks, B * N);
+    if (vec)
+      hipLaunchKernelGGL(argmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, V, chunks, keys);
+    else
+      hipLaunchKernelGGL(argmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, V, chunks, keys);
+    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+    hipLaunchKernelGGL(greedy_path_kernel, dim3((B + 3) / 4), dim3(256), 0, ctx->stream, keys, chunks, draft_tokens,
+                       parents, B, N, V, accept_len, path, bonus, target_argmax, ctx->d_state);
+    return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+  }
+  auto *stats = static_cast<double *>(workspace);
+  const dim3 g1(chunks, B * N, 2);
+  if (vec)
+    hipLaunchKernelGGL(softmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
+                       chunks, static_cast<double>(temperature), stats);
+  else
+    hipLaunchKernelGGL(softmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
+                       chunks, static_cast<double>(temperature), stats);
+  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  hipLaunchKernelGGL(stochastic_path_kernel, dim3(B), blk, 0, ctx->stream, target_logits, draft_logits, draft_tokens,
+                     parents, uniforms, B, N, V, chunks, static_cast<double>(temperature), stats, accept_len, path,
+                     bonus, ctx->d_state);
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+}  // namespace tv

@@ -1,0 +1,81 @@
+// tv_internal.h - shared internals of libtreeverify (device code for gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/treeverify.h"
+
+struct tv_ctx {
+  int device;
+  hipStream_t stream;
+  int cu_count;
+  // d_state[0] = tau sum, d_state[1] = tau cycles, d_state[2] low 32 bits = sticky error code
+  unsigned long long *d_state;
+};
+
+namespace tv {
+
+constexpr int kPage = 16;
+
+// Records the first device-detected error of a context (later ones are dropped).
+__device__ inline void raise_error(unsigned long long *state, int code) {
+  atomicCAS(reinterpret_cast<int *>(state + 2), 0, code);
+}
+
+__device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+__device__ inline uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ inline unsigned long long shfl_u64(unsigned long long v, int src) {
+  int lo = __shfl(static_cast<int>(v & 0xFFFFFFFFull), src);
+  int hi = __shfl(static_cast<int>(v >> 32), src);
+  return (static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ inline unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  int lo = __shfl_xor(static_cast<int>(v & 0xFFFFFFFFull), m);
+  int hi = __shfl_xor(static_cast<int>(v >> 32), m);
+  return (static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ inline float wave_max(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Host-side launchers (defined in the kernels' translation units).
+tv_status launch_build_mask(tv_ctx *ctx, const int32_t *parents, int B, int N, uint64_t *mask, int32_t *depth);
+
+struct AttnPlan {
+  int S;            // key splits per (sequence, KV head, row block)
+  int chunk_tiles;  // 64-key tiles per split
+  int row_block;    // query rows (node, head-in-group) per workgroup
+  int row_blocks;   // ceil(G*N / row_block)
+  size_t ws_bytes;  // fp32 partials + (m, l)
+};
+AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int max_prefix_len);
+tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, const void *k_pages,
+                           const void *v_pages, int64_t num_pages, const int32_t *page_table, int maxp,
+                           const int32_t *prefix_lens, int max_prefix_len, const uint64_t *tree_mask, int B, int N,
+                           int Hq, int Hkv, int D, float sm_scale, void *out, tv_dtype out_dtype, void *workspace);
+
+size_t accept_ws_bytes(int B, int N, int V, tv_accept_mode mode);
+tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits,
+                        const int32_t *draft_tokens, const int32_t *parents, const float *uniforms, int B, int N,
+                        int V, tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path,
+                        int32_t *bonus, int32_t *target_argmax, void *workspace);
+
+tv_status launch_clear_state(tv_ctx *ctx, int first_word, int n_words);
+
+}  // namespace tv
