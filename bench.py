@@ -39,8 +39,7 @@ def parse():
 
 
 def workload_name(w, c):
-    L = f"L{w.max_prefix_len}" if c["L"] if not isinstance(c["L"], tuple) else False else \
-        f"L~U[{c['L'][0]},{c['L'][1]}]"
+    L = f"L~U[{c['L'][0]},{c['L'][1]}]" if isinstance(c["L"], tuple) else f"L{c['L']}"
     return (f"cfg{w.cfg} {c['name']}: B{w.B} Hq{w.Hq}/Hkv{w.Hkv} D{w.D} {L} N{w.N} tree={c['tree']} "
             f"V{w.V} {w.mode}")
 

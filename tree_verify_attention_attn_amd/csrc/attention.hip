@@ -1,15 +1,27 @@
-// attention.hip - tree-masked attention over a paged GQA KV cache.
+// attention.hip - tree-masked attention over a paged GQA KV cache (gfx950).
 //
 // What is computed (EAGLE-2 deep-dive page, third pillar; production note on
-// indexing tree masks over paged memory): every tree node's query rows attend
-// to the whole cached prefix of their sequence plus the tree positions whose
-// bit is set in the node's ancestor mask. Work unit: one (sequence, KV head,
-// block of query rows, key split). All query heads of a GQA group share the
-// KV head, so a workgroup stages each 64-key K/V tile once in LDS and reuses
-// it for every (node, head-in-group) row it owns. Only the tiles that overlap
-// the tree positions [L, L + N) evaluate the mask; prefix tiles never do.
-// Softmax is the online (running max / running sum) form in base 2; long key
-// ranges are split across workgroups and merged by a combine kernel.
+// indexing tree masks directly over paged memory): every tree node's query
+// rows attend to the whole cached prefix of their sequence plus the tree
+// positions whose bit is set in the node's ancestor mask.
+//
+// Work unit: one (sequence b, KV head g, row group, key split). The G query
+// heads of a GQA group share the KV head, so the G*N (node, head) rows of a
+// (b, g) pair form the query side of one dense product and each 64-key K/V
+// tile is read from HBM once per row group, staged in LDS and shared by the
+// four wavefronts of the workgroup.
+//
+// Matrix cores: S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16
+// d from LDS, B = 16 d x 32 queries held in VGPRs). In the 32x32 result a lane
+// owns one query column and 16 of the 32 keys (rows 8i + 4*(lane/32) + j), so
+// the softmax row reductions are in-lane plus one permlane32 swap. The same
+// accumulator, packed to bf16, is the B operand of O^T = V^T . P^T; its A
+// operand (32 d x 16 keys of V^T) comes from the row-major V tile through the
+// LDS transpose read (ds_read_b64_tr_b16), so V is never transposed in memory.
+// Softmax is online in base 2 with lazy rescaling: O and l are rescaled only
+// when a row's running max grows by more than 2^8, which bounds p <= 256.
+// Only tiles that reach the tree positions or the sequence tail evaluate the
+// mask; prefix tiles never do.
 #include <math.h>
 
 #include "tv_internal.h"
@@ -18,10 +30,16 @@ namespace tv {
 
 namespace {
 
-constexpr int kRows = 64;       // query rows per workgroup
-constexpr int kKeys = 64;       // keys per tile
-constexpr int kWaveRows = 16;   // rows per wavefront (4 wavefronts)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int kKeys = 64;      // keys per tile
+constexpr int kWaves = 4;      // wavefronts per workgroup
+constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 
 struct AttnArgs {
   const uint16_t *q, *k, *v;
@@ -30,150 +48,288 @@ struct AttnArgs {
   int64_t num_pages;
   int maxp, max_prefix_len;
   int B, N, Hq, Hkv, G, rows, rows_pad;
-  float scale_log2;
+  int row_groups;
+  float c;         // |sm_scale| * log2(e)
+  int negate_q;    // sm_scale < 0: negate Q (exact) and use |sm_scale|
   void *out;
   int out_bf16;
   float *ws_o, *ws_ml;
   int S, chunk_tiles;
+  int xcd_remap;   // block ids are laid out so one (b, g) stays on one XCD
   unsigned long long *state;
 };
 
-template <int D>
-__global__ void __launch_bounds__(256) attn_fma_kernel(AttnArgs a) {
-  constexpr int DC = D / 64;  // output columns per lane
-  __shared__ float Qs[kRows][D];
-  __shared__ float Ks[kKeys][D + 1];
-  __shared__ float Vs[kKeys][D];
-  __shared__ float Ps[4][kWaveRows][kKeys];
-  __shared__ int bad_page;
+__device__ inline float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+__device__ inline float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+__device__ inline bf16x4 lds_read_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)p));
+}
+
+__device__ inline void store_out(const AttnArgs &a, int64_t base, int d, const float *v4) {
+  if (a.out_bf16) {
+    uint16_t *o = static_cast<uint16_t *>(a.out) + base + d;
+    uint2 pk;
+    pk.x = float_to_bf16_bits(v4[0]) | (static_cast<uint32_t>(float_to_bf16_bits(v4[1])) << 16);
+    pk.y = float_to_bf16_bits(v4[2]) | (static_cast<uint32_t>(float_to_bf16_bits(v4[3])) << 16);
+    *reinterpret_cast<uint2 *>(o) = pk;
+  } else {
+    *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base + d) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+  }
+}
+
+template <int D, int QB>
+__global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
+  constexpr int KS = D / 16;               // 16-wide d steps of S^T = K Q^T
+  constexpr int DB = D / 32;               // 32-wide d blocks of O^T
+  constexpr int RS = D + 8;                // LDS row stride in bf16 (keeps both read patterns conflict-free)
+  constexpr int CPR = D / 8;               // 16-byte chunks per key row
+  constexpr int LPT = kKeys * CPR / kThreads;  // 16-byte loads per thread per K (and per V) tile
+  constexpr int ROWS_WG = 32 * QB * kWaves;
+
+  __shared__ __align__(16) uint16_t Ks[2][kKeys * RS];
+  __shared__ __align__(16) uint16_t Vs[2][kKeys * RS];
+  __shared__ int s_bad;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv, s = blockIdx.z, rb = blockIdx.x;
+  const int h = lane >> 5, n = lane & 31;
+
+  // block -> (b, g, row group, split); consecutive logical ids share an XCD
+  int id = blockIdx.x;
+  if (a.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+  const int s = id % a.S;
+  const int rg = (id / a.S) % a.row_groups;
+  const int bh = id / (a.S * a.row_groups);
+  const int b = bh / a.Hkv, g = bh % a.Hkv;
+
   const int L = a.prefix_lens[b];
   const bool bad_len = L < 0 || L > a.max_prefix_len;
   const int T = bad_len ? 0 : L + a.N;
   const int tiles_b = (T + kKeys - 1) / kKeys;
   const int t_begin = s * a.chunk_tiles;
   const int t_end = min(t_begin + a.chunk_tiles, tiles_b);
-  if (tid == 0) bad_page = 0;
+  if (tid == 0) s_bad = 0;
 
-  for (int e = tid; e < kRows * D; e += 256) {
-    const int r = e / D, d = e % D, row = rb * kRows + r;
-    float val = 0.f;
-    if (row < a.rows) {
-      const int i = row / a.G, h = g * a.G + row % a.G;
-      val = bf16_bits_to_float(a.q[((static_cast<int64_t>(b) * a.N + i) * a.Hq + h) * D + d]);
+  // ---- query rows of this wavefront: B operands of S^T, kept in VGPRs
+  const int row0 = rg * ROWS_WG + w * 32 * QB;
+  const bool wave_active = row0 < a.rows;
+  bf16x8 qf[QB][KS];
+  uint64_t mword[QB];
+  int node[QB], head[QB];
+  bool row_ok[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = row0 + qb * 32 + n;
+    row_ok[qb] = row < a.rows;
+    node[qb] = row_ok[qb] ? row / a.G : 0;
+    head[qb] = g * a.G + (row_ok[qb] ? row % a.G : 0);
+    mword[qb] = (row_ok[qb] && a.mask) ? a.mask[static_cast<int64_t>(b) * a.N + node[qb]] : ~0ull;
+    const uint16_t *qrow = a.q + ((static_cast<int64_t>(b) * a.N + node[qb]) * a.Hq + head[qb]) * D;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row_ok[qb]) v = *reinterpret_cast<const uint4 *>(qrow + 16 * t + 8 * h);
+      if (a.negate_q) {
+        v.x ^= 0x80008000u;
+        v.y ^= 0x80008000u;
+        v.z ^= 0x80008000u;
+        v.w ^= 0x80008000u;
+      }
+      qf[qb][t] = __builtin_bit_cast(bf16x8, v);
     }
-    Qs[r][d] = val;
-  }
-  uint64_t mrow[kWaveRows];
-#pragma unroll
-  for (int r = 0; r < kWaveRows; ++r) {
-    const int row = rb * kRows + w * kWaveRows + r;
-    const int i = row < a.rows ? row / a.G : 0;
-    mrow[r] = a.mask ? a.mask[static_cast<int64_t>(b) * a.N + i] : ~0ull;
-  }
-  float m[kWaveRows], l[kWaveRows], o[kWaveRows][DC];
-#pragma unroll
-  for (int r = 0; r < kWaveRows; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) o[r][c] = 0.f;
   }
 
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    const int t0 = tile * kKeys;
-    __syncthreads();
-    // gather the 64-token K/V tile: 4 pages of 16 tokens, 16-byte loads
-    for (int e = tid * 8; e < kKeys * D; e += 256 * 8) {
-      const int tok = e / D, d = e % D, t = t0 + tok;
-      uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+  float m_ref[QB], l[QB];
+  f32x16 o[QB][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
+  }
+
+  // ---- K/V tile staging: thread tid moves chunks c = tid + 256 u (key c / CPR)
+  uint4 kr[LPT], vr[LPT];
+  bool load_bad = false;
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int c = tid + kThreads * u, key = c / CPR, ch = c % CPR;
+      const int t = tile * kKeys + key;
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
       if (t < T) {
         const int pid = a.page_table[static_cast<int64_t>(b) * a.maxp + t / kPage];
         if (pid >= 0 && pid < a.num_pages) {
-          const int64_t off = ((static_cast<int64_t>(pid) * a.Hkv + g) * kPage + t % kPage) * D + d;
-          kk = *reinterpret_cast<const uint4 *>(a.k + off);
-          vv = *reinterpret_cast<const uint4 *>(a.v + off);
+          const int64_t off = ((static_cast<int64_t>(pid) * a.Hkv + g) * kPage + t % kPage) * D + ch * 8;
+          kr[u] = *reinterpret_cast<const uint4 *>(a.k + off);
+          vr[u] = *reinterpret_cast<const uint4 *>(a.v + off);
         } else {
-          bad_page = 1;
+          load_bad = true;
         }
       }
-      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Ks[tok][d + 2 * j] = __uint_as_float(kw[j] << 16);
-        Ks[tok][d + 2 * j + 1] = __uint_as_float(kw[j] & 0xFFFF0000u);
-        Vs[tok][d + 2 * j] = __uint_as_float(vw[j] << 16);
-        Vs[tok][d + 2 * j + 1] = __uint_as_float(vw[j] & 0xFFFF0000u);
-      }
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int c = tid + kThreads * u, key = c / CPR, ch = c % CPR;
+      *reinterpret_cast<uint4 *>(&Ks[buf][key * RS + ch * 8]) = kr[u];
+      *reinterpret_cast<uint4 *>(&Vs[buf][key * RS + ch * 8]) = vr[u];
+    }
+  };
 
-    // scores: lane = key
-    float sacc[kWaveRows];
-#pragma unroll
-    for (int r = 0; r < kWaveRows; ++r) sacc[r] = 0.f;
-    for (int d = 0; d < D; ++d) {
-      const float kd = Ks[lane][d];
-#pragma unroll
-      for (int r = 0; r < kWaveRows; ++r) sacc[r] = fmaf(Qs[w * kWaveRows + r][d], kd, sacc[r]);
-    }
-    const int t = t0 + lane;
-    const bool key_ok = t < T;
-    const bool is_tree = t >= L;
-    const int j = t - L;
-#pragma unroll
-    for (int r = 0; r < kWaveRows; ++r) {
-      const bool vis = key_ok && (!is_tree || ((mrow[r] >> (j & 63)) & 1ull));
-      const float sv = vis ? sacc[r] * a.scale_log2 : -INFINITY;
-      const float mnew = fmaxf(m[r], wave_max(sv));
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m[r] - mref);
-      const float p = exp2f(sv - mref);
-      l[r] = l[r] * alpha + wave_sum(p);
-      m[r] = mnew;
-      Ps[w][r][lane] = p;
-#pragma unroll
-      for (int c = 0; c < DC; ++c) o[r][c] *= alpha;
-    }
-    __syncthreads();
-    for (int k = 0; k < kKeys; ++k) {
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const float vk = Vs[k][c * 64 + lane];
-#pragma unroll
-        for (int r = 0; r < kWaveRows; ++r) o[r][c] = fmaf(Ps[w][r][k], vk, o[r][c]);
-      }
-    }
+  // transpose-read lane pattern for the V^T operand: lane (group grp, slot sl)
+  // addresses key 4*(grp/2) + sl/4 and d 16*(grp%2) + 4*(sl%4) of a 16-key block
+  const int grp = lane >> 4, sl = lane & 15;
+  const int tr_off = (4 * (grp >> 1) + (sl >> 2)) * RS + 16 * (grp & 1) + 4 * (sl & 3);
+
+  if (t_begin < t_end) {
+    load_tile(t_begin);
+    store_tile(0);
   }
   __syncthreads();
-  const bool bad = bad_len || bad_page;
+
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    const int cur = (tile - t_begin) & 1;
+    const bool has_next = tile + 1 < t_end;
+    if (has_next) load_tile(tile + 1);
+
+    if (wave_active) {
+      const uint16_t *Kb = Ks[cur];
+      const uint16_t *Vb = Vs[cur];
+      // S^T = K Q^T for 64 keys (two 32-key blocks)
+      f32x16 sc[QB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sc[qb][kb][e] = 0.f;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kb[(kb * 32 + n) * RS + 16 * t + 8 * h]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][t], sc[qb][kb], 0, 0, 0);
+        }
+      }
+
+      // visibility (only tiles that reach the tree positions or the tail)
+      const int tile0 = tile * kKeys;
+      const bool need_mask = tile0 + kKeys > L;
+      bf16x8 pk[QB][2][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int t = tile0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+              const bool vis = t < T && (t < L || ((mword[qb] >> ((t - L) & 63)) & 1ull));
+              if (!vis) sc[qb][kb][e] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[qb][kb][e]);
+        mx = swap_halves_max(mx);
+        const float mt = mx == -INFINITY ? -INFINITY : mx * a.c;
+        // lazy rescale: only when some row's max grows by more than 2^kRescale
+        if (__builtin_amdgcn_ballot_w64(mt > m_ref[qb] + kRescale) != 0ull) {
+          const float m_new = fmaxf(m_ref[qb], mt);
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+          m_ref[qb] = m_new;
+        }
+        const float mu = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float p = __builtin_amdgcn_exp2f(fmaf(sc[qb][kb][e], a.c, -mu));
+            if (need_mask && sc[qb][kb][e] == -INFINITY) p = 0.f;
+            l[qb] += p;
+            pk[qb][kb][e >> 3][e & 7] = static_cast<__bf16>(p);
+          }
+        }
+      }
+
+      // O^T += V^T P^T: A = V^T fragments through the LDS transpose read
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2) {
+            const uint16_t *vp = Vb + (kb * 32 + 16 * m2) * RS + db * 32 + tr_off;
+            const bf16x4 lo = lds_read_tr16(vp);
+            const bf16x4 hi = lds_read_tr16(vp + 8 * RS);
+            const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[qb][kb][m2], o[qb][db], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (has_next) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+  if (load_bad) s_bad = 1;
+  __syncthreads();
+  const bool bad = bad_len || s_bad;
   if (bad && tid == 0) raise_error(a.state, TV_ERR_INVALID_ARG);
+  if (!wave_active) return;
 
 #pragma unroll
-  for (int r = 0; r < kWaveRows; ++r) {
-    const int row = rb * kRows + w * kWaveRows + r;
-    if (row >= a.rows) continue;
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = swap_halves_sum(l[qb]);
+    if (!row_ok[qb]) continue;
+    const int row = row0 + qb * 32 + n;
     if (a.S == 1) {
-      const int i = row / a.G, h = g * a.G + row % a.G;
-      const int64_t base = ((static_cast<int64_t>(b) * a.N + i) * a.Hq + h) * D;
-      const float inv = 1.f / l[r];
+      const int64_t base = ((static_cast<int64_t>(b) * a.N + node[qb]) * a.Hq + head[qb]) * D;
+      const float inv = 1.f / l_tot;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const float val = bad ? NAN : o[r][c] * inv;
-        if (a.out_bf16)
-          static_cast<uint16_t *>(a.out)[base + c * 64 + lane] = float_to_bf16_bits(val);
-        else
-          static_cast<float *>(a.out)[base + c * 64 + lane] = val;
-      }
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = bad ? NAN : o[qb][db][4 * i + j] * inv;
+          store_out(a, base, db * 32 + 8 * i + 4 * h, v4);
+        }
     } else {
-      const int64_t slot = (static_cast<int64_t>(b * a.Hkv + g) * a.S + s) * a.rows_pad + row;
+      const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) a.ws_o[slot * D + c * 64 + lane] = o[r][c];
-      if (lane == 0) {
-        a.ws_ml[slot * 2] = bad ? NAN : m[r];
-        a.ws_ml[slot * 2 + 1] = l[r];
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4 *>(a.ws_o + slot * D + db * 32 + 8 * i + 4 * h) =
+              make_float4(o[qb][db][4 * i], o[qb][db][4 * i + 1], o[qb][db][4 * i + 2], o[qb][db][4 * i + 3]);
+      if (h == 0) {
+        a.ws_ml[slot * 2] = bad ? NAN : m_ref[qb];
+        a.ws_ml[slot * 2 + 1] = l_tot;
       }
     }
   }
@@ -194,7 +350,8 @@ __global__ void __launch_bounds__(D) attn_combine_kernel(AttnArgs a) {
   float lsum = 0.f, acc = 0.f;
   for (int s = 0; s < a.S; ++s) {
     const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
-    const float wgt = exp2f(a.ws_ml[slot * 2] - M);
+    const float ms = a.ws_ml[slot * 2];
+    const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
     lsum = fmaf(wgt, a.ws_ml[slot * 2 + 1], lsum);
     acc = fmaf(wgt, a.ws_o[slot * D + d], acc);
   }
@@ -213,19 +370,23 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
   AttnPlan p{};
   const int G = Hq / Hkv;
   const int rows = G * N;
-  p.row_block = kRows;
-  p.row_blocks = (rows + kRows - 1) / kRows;
+  p.qb = rows > 32 * kWaves ? 2 : 1;
+  p.row_block = 32 * p.qb * kWaves;
+  p.row_blocks = (rows + p.row_block - 1) / p.row_block;
   const int tiles = (max_prefix_len + N + kKeys - 1) / kKeys;
   const int64_t base = static_cast<int64_t>(B) * Hkv * p.row_blocks;
-  const int64_t target = 2ll * cu_count;
-  int S = static_cast<int>((target + base - 1) / (base > 0 ? base : 1));
-  S = S < 1 ? 1 : (S > tiles ? tiles : S);
+  // one workgroup per CU at a time for 64-row wavefronts (VGPR-bound), two otherwise
+  const int64_t target = static_cast<int64_t>(cu_count) * (p.qb == 2 ? 1 : 2);
+  int64_t S = base > 0 ? (target + base / 2) / base : 1;
   if (S < 1) S = 1;
-  p.chunk_tiles = (tiles + S - 1) / S;
+  if (S > tiles) S = tiles;
+  if (S < 1) S = 1;
+  p.chunk_tiles = static_cast<int>((tiles + S - 1) / S);
   if (p.chunk_tiles < 1) p.chunk_tiles = 1;
   p.S = (tiles + p.chunk_tiles - 1) / p.chunk_tiles;
   if (p.S < 1) p.S = 1;
-  p.ws_bytes = p.S > 1 ? static_cast<size_t>(B) * Hkv * p.S * p.row_blocks * kRows * (D + 2) * sizeof(float) : 0;
+  p.ws_bytes =
+      p.S > 1 ? static_cast<size_t>(B) * Hkv * p.S * p.row_blocks * p.row_block * (D + 2) * sizeof(float) : 0;
   return p;
 }
 
@@ -249,8 +410,10 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   a.Hkv = Hkv;
   a.G = Hq / Hkv;
   a.rows = a.G * N;
-  a.rows_pad = plan.row_blocks * kRows;
-  a.scale_log2 = sm_scale * kLog2e;
+  a.rows_pad = plan.row_blocks * plan.row_block;
+  a.row_groups = plan.row_blocks;
+  a.c = fabsf(sm_scale) * kLog2e;
+  a.negate_q = sm_scale < 0.f;
   a.out = out;
   a.out_bf16 = out_dtype == TV_BF16;
   a.S = plan.S;
@@ -260,11 +423,20 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
     a.ws_o = static_cast<float *>(workspace);
     a.ws_ml = a.ws_o + static_cast<int64_t>(B) * Hkv * plan.S * a.rows_pad * D;
   }
-  const dim3 grid(plan.row_blocks, B * Hkv, plan.S);
-  if (D == 128)
-    hipLaunchKernelGGL(attn_fma_kernel<128>, grid, dim3(256), 0, ctx->stream, a);
-  else
-    hipLaunchKernelGGL(attn_fma_kernel<64>, grid, dim3(256), 0, ctx->stream, a);
+  const int blocks = B * Hkv * plan.row_blocks * plan.S;
+  a.xcd_remap = (blocks % 8) == 0;
+  const dim3 grid(blocks);
+  if (D == 128) {
+    if (plan.qb == 2)
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, dim3(kThreads), 0, ctx->stream, a);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(kThreads), 0, ctx->stream, a);
+  } else {
+    if (plan.qb == 2)
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, dim3(kThreads), 0, ctx->stream, a);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 1>), grid, dim3(kThreads), 0, ctx->stream, a);
+  }
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
     const dim3 cgrid(B * Hkv * a.rows);
