@@ -36,8 +36,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kKeys = 64;      // keys per tile
-constexpr int kWaves = 4;      // wavefronts per workgroup
-constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -85,14 +83,23 @@ __device__ inline void store_out(const AttnArgs &a, int64_t base, int d, const f
   }
 }
 
-template <int D, int QB>
-__global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
+// Buffer resource over one KV page (all KV heads): loads outside [0, bytes)
+// return zeros, so an unused or invalid page costs no branch.
+__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t *base, int64_t pid, int page_elems, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base + pid * page_elems), static_cast<short>(0),
+                                           bytes, 0x00020000);
+}
+
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) attn_mfma_kernel(AttnArgs a) {
+  constexpr int NT = 64 * NW;              // threads per workgroup
   constexpr int KS = D / 16;               // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;               // 32-wide d blocks of O^T
   constexpr int RS = D + 8;                // LDS row stride in bf16 (keeps both read patterns conflict-free)
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
-  constexpr int LPT = kKeys * CPR / kThreads;  // 16-byte loads per thread per K (and per V) tile
-  constexpr int ROWS_WG = 32 * QB * kWaves;
+  constexpr int LPT = kKeys * CPR / NT;    // 16-byte loads per thread per K (and per V) tile
+  constexpr int ROWS_WG = 32 * NW;
+  static_assert(LPT >= 1, "tile too small for the workgroup");
 
   __shared__ __align__(16) uint16_t Ks[2][kKeys * RS];
   __shared__ __align__(16) uint16_t Vs[2][kKeys * RS];
@@ -117,73 +124,68 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   const int t_end = min(t_begin + a.chunk_tiles, tiles_b);
   if (tid == 0) s_bad = 0;
 
-  // ---- query rows of this wavefront: B operands of S^T, kept in VGPRs
-  const int row0 = rg * ROWS_WG + w * 32 * QB;
-  const bool wave_active = row0 < a.rows;
-  bf16x8 qf[QB][KS];
-  uint64_t mword[QB];
-  int node[QB], head[QB];
-  bool row_ok[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = row0 + qb * 32 + n;
-    row_ok[qb] = row < a.rows;
-    node[qb] = row_ok[qb] ? row / a.G : 0;
-    head[qb] = g * a.G + (row_ok[qb] ? row % a.G : 0);
-    mword[qb] = (row_ok[qb] && a.mask) ? a.mask[static_cast<int64_t>(b) * a.N + node[qb]] : ~0ull;
-    const uint16_t *qrow = a.q + ((static_cast<int64_t>(b) * a.N + node[qb]) * a.Hq + head[qb]) * D;
+  // ---- the wavefront's 32 query rows: B operands of S^T, kept in VGPRs
+  const int row = rg * ROWS_WG + w * 32 + n;
+  const bool wave_active = rg * ROWS_WG + w * 32 < a.rows;
+  const bool row_ok = row < a.rows;
+  const int node = row_ok ? row / a.G : 0;
+  const int head = g * a.G + (row_ok ? row % a.G : 0);
+  const uint64_t mword = (row_ok && a.mask) ? a.mask[static_cast<int64_t>(b) * a.N + node] : ~0ull;
+  bf16x8 qf[KS];
+  {
+    const uint16_t *qrow = a.q + ((static_cast<int64_t>(b) * a.N + node) * a.Hq + head) * D;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row_ok[qb]) v = *reinterpret_cast<const uint4 *>(qrow + 16 * t + 8 * h);
+      if (row_ok) v = *reinterpret_cast<const uint4 *>(qrow + 16 * t + 8 * h);
       if (a.negate_q) {
         v.x ^= 0x80008000u;
         v.y ^= 0x80008000u;
         v.z ^= 0x80008000u;
         v.w ^= 0x80008000u;
       }
-      qf[qb][t] = __builtin_bit_cast(bf16x8, v);
+      qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  float m_ref[QB], l[QB];
-  f32x16 o[QB][DB];
+  float m_ref = -INFINITY, l = 0.f;
+  f32x16 o[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_ref[qb] = -INFINITY;
-    l[qb] = 0.f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
-  }
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
-  // ---- K/V tile staging: thread tid moves chunks c = tid + 256 u (key c / CPR)
+  // ---- K/V tile staging. Thread tid moves chunks c = tid + NT u (key c / CPR,
+  // 16-byte chunk c % CPR). A wavefront's 64 chunks always lie in one page, so
+  // the page id is wave-uniform.
+  const int page_elems = a.Hkv * kPage * D;
+  const int page_bytes = page_elems * 2;
+  const int64_t pt_row = static_cast<int64_t>(b) * a.maxp;
   uint4 kr[LPT], vr[LPT];
   bool load_bad = false;
   auto load_tile = [&](int tile) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
-      const int c = tid + kThreads * u, key = c / CPR, ch = c % CPR;
+      const int c = tid + NT * u, key = c / CPR, ch = c % CPR;
+      const int key0 = __builtin_amdgcn_readfirstlane((w * 64 + NT * u) / CPR);
+      const int t0 = tile * kKeys + key0;  // first key of this wavefront's chunk group
+      int pid = -1;
+      if (t0 < T) pid = __builtin_amdgcn_readfirstlane(a.page_table[pt_row + t0 / kPage]);
+      const bool ok = pid >= 0 && pid < a.num_pages;
+      load_bad |= (t0 < T) && !ok;
       const int t = tile * kKeys + key;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (t < T) {
-        const int pid = a.page_table[static_cast<int64_t>(b) * a.maxp + t / kPage];
-        if (pid >= 0 && pid < a.num_pages) {
-          const int64_t off = ((static_cast<int64_t>(pid) * a.Hkv + g) * kPage + t % kPage) * D + ch * 8;
-          kr[u] = *reinterpret_cast<const uint4 *>(a.k + off);
-          vr[u] = *reinterpret_cast<const uint4 *>(a.v + off);
-        } else {
-          load_bad = true;
-        }
-      }
+      const int voff = t < T ? ((g * kPage + t % kPage) * D + ch * 8) * 2 : 0x7FFFFFF0;
+      const int bytes = ok ? page_bytes : 0;
+      const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.k, ok ? pid : 0, page_elems, bytes);
+      const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.v, ok ? pid : 0, page_elems, bytes);
+      kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0));
+      vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
-      const int c = tid + kThreads * u, key = c / CPR, ch = c % CPR;
+      const int c = tid + NT * u, key = c / CPR, ch = c % CPR;
       *reinterpret_cast<uint4 *>(&Ks[buf][key * RS + ch * 8]) = kr[u];
       *reinterpret_cast<uint4 *>(&Vs[buf][key * RS + ch * 8]) = vr[u];
     }
@@ -208,89 +210,88 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
     if (wave_active) {
       const uint16_t *Kb = Ks[cur];
       const uint16_t *Vb = Vs[cur];
-      // S^T = K Q^T for 64 keys (two 32-key blocks)
-      f32x16 sc[QB][2];
+      // S^T = K Q^T for 64 keys (two 32-key blocks); all K fragments are
+      // read first so the LDS latency overlaps instead of serialising MFMAs
+      bf16x8 kf[2][KS];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+          kf[kb][t] = *reinterpret_cast<const bf16x8 *>(&Kb[(kb * 32 + n) * RS + 16 * t + 8 * h]);
+      f32x16 sc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][t], qf[t], sc[kb], 0, 0, 0);
+      }
+      // V^T fragments for the PV product, issued now so they land during the softmax
+      bf16x8 vf[DB][2][2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sc[qb][kb][e] = 0.f;
-#pragma unroll
-      for (int t = 0; t < KS; ++t) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kb[(kb * 32 + n) * RS + 16 * t + 8 * h]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][t], sc[qb][kb], 0, 0, 0);
-        }
-      }
-
-      // visibility (only tiles that reach the tree positions or the tail)
-      const int tile0 = tile * kKeys;
-      const bool need_mask = tile0 + kKeys > L;
-      bf16x8 pk[QB][2][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int t = tile0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-              const bool vis = t < T && (t < L || ((mword[qb] >> ((t - L) & 63)) & 1ull));
-              if (!vis) sc[qb][kb][e] = -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[qb][kb][e]);
-        mx = swap_halves_max(mx);
-        const float mt = mx == -INFINITY ? -INFINITY : mx * a.c;
-        // lazy rescale: only when some row's max grows by more than 2^kRescale
-        if (__builtin_amdgcn_ballot_w64(mt > m_ref[qb] + kRescale) != 0ull) {
-          const float m_new = fmaxf(m_ref[qb], mt);
-          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-          l[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
-          m_ref[qb] = m_new;
-        }
-        const float mu = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float p = __builtin_amdgcn_exp2f(fmaf(sc[qb][kb][e], a.c, -mu));
-            if (need_mask && sc[qb][kb][e] == -INFINITY) p = 0.f;
-            l[qb] += p;
-            pk[qb][kb][e >> 3][e & 7] = static_cast<__bf16>(p);
-          }
-        }
-      }
-
-      // O^T += V^T P^T: A = V^T fragments through the LDS transpose read
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int m2 = 0; m2 < 2; ++m2) {
             const uint16_t *vp = Vb + (kb * 32 + 16 * m2) * RS + db * 32 + tr_off;
             const bf16x4 lo = lds_read_tr16(vp);
             const bf16x4 hi = lds_read_tr16(vp + 8 * RS);
-            const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[qb][kb][m2], o[qb][db], 0, 0, 0);
+            vf[db][kb][m2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
+
+      // visibility (only tiles that reach the tree positions or the tail)
+      const int tile0 = tile * kKeys;
+      const bool need_mask = tile0 + kKeys > L;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int t = tile0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const bool vis = t < T && (t < L || ((mword >> ((t - L) & 63)) & 1ull));
+            if (!vis) sc[kb][e] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+      mx = swap_halves_max(mx);
+      const float mt = mx == -INFINITY ? -INFINITY : mx * a.c;
+      // lazy rescale: only when some row's max grows by more than 2^kRescale
+      if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescale) != 0ull) {
+        const float m_new = fmaxf(m_ref, mt);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        m_ref = m_new;
+      }
+      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+      bf16x8 pk[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], a.c, -mu));
+          if (need_mask && sc[kb][e] == -INFINITY) p = 0.f;
+          l += p;
+          pk[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
         }
       }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][kb][m2], pk[kb][m2], o[db], 0, 0, 0);
     }
 
     if (has_next) store_tile(cur ^ 1);
@@ -302,35 +303,31 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(AttnArgs a) {
   if (bad && tid == 0) raise_error(a.state, TV_ERR_INVALID_ARG);
   if (!wave_active) return;
 
+  const float l_tot = swap_halves_sum(l);
+  if (!row_ok) return;
+  if (a.S == 1) {
+    const int64_t base = ((static_cast<int64_t>(b) * a.N + node) * a.Hq + head) * D;
+    const float inv = 1.f / l_tot;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = swap_halves_sum(l[qb]);
-    if (!row_ok[qb]) continue;
-    const int row = row0 + qb * 32 + n;
-    if (a.S == 1) {
-      const int64_t base = ((static_cast<int64_t>(b) * a.N + node[qb]) * a.Hq + head[qb]) * D;
-      const float inv = 1.f / l_tot;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int i = 0; i < 4; ++i) {
+        float v4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v4[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v4[j] = bad ? NAN : o[qb][db][4 * i + j] * inv;
-          store_out(a, base, db * 32 + 8 * i + 4 * h, v4);
-        }
-    } else {
-      const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<float4 *>(a.ws_o + slot * D + db * 32 + 8 * i + 4 * h) =
-              make_float4(o[qb][db][4 * i], o[qb][db][4 * i + 1], o[qb][db][4 * i + 2], o[qb][db][4 * i + 3]);
-      if (h == 0) {
-        a.ws_ml[slot * 2] = bad ? NAN : m_ref[qb];
-        a.ws_ml[slot * 2 + 1] = l_tot;
+        for (int j = 0; j < 4; ++j) v4[j] = bad ? NAN : o[db][4 * i + j] * inv;
+        store_out(a, base, db * 32 + 8 * i + 4 * h, v4);
       }
+  } else {
+    const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4 *>(a.ws_o + slot * D + db * 32 + 8 * i + 4 * h) =
+            make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
+    if (h == 0) {
+      a.ws_ml[slot * 2] = bad ? NAN : m_ref;
+      a.ws_ml[slot * 2 + 1] = l_tot;
     }
   }
 }
@@ -370,13 +367,14 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
   AttnPlan p{};
   const int G = Hq / Hkv;
   const int rows = G * N;
-  p.qb = rows > 32 * kWaves ? 2 : 1;
-  p.row_block = 32 * p.qb * kWaves;
+  // 32 query rows per wavefront; 8, 4 or 2 wavefronts per workgroup
+  p.qb = rows > 128 ? 8 : (rows > 64 ? 4 : 2);
+  p.row_block = 32 * p.qb;
   p.row_blocks = (rows + p.row_block - 1) / p.row_block;
   const int tiles = (max_prefix_len + N + kKeys - 1) / kKeys;
   const int64_t base = static_cast<int64_t>(B) * Hkv * p.row_blocks;
-  // one workgroup per CU at a time for 64-row wavefronts (VGPR-bound), two otherwise
-  const int64_t target = static_cast<int64_t>(cu_count) * (p.qb == 2 ? 1 : 2);
+  // about one workgroup per CU (LDS: two K/V tile buffers per workgroup)
+  const int64_t target = static_cast<int64_t>(cu_count) * (p.qb == 8 ? 1 : 2);
   int64_t S = base > 0 ? (target + base / 2) / base : 1;
   if (S < 1) S = 1;
   if (S > tiles) S = tiles;
@@ -426,16 +424,21 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   const int blocks = B * Hkv * plan.row_blocks * plan.S;
   a.xcd_remap = (blocks % 8) == 0;
   const dim3 grid(blocks);
+  const dim3 block(64 * plan.qb);
   if (D == 128) {
-    if (plan.qb == 2)
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, dim3(kThreads), 0, ctx->stream, a);
+    if (plan.qb == 8)
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 8>), grid, block, 0, ctx->stream, a);
+    else if (plan.qb == 4)
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, block, 0, ctx->stream, a);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 1>), grid, dim3(kThreads), 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, block, 0, ctx->stream, a);
   } else {
-    if (plan.qb == 2)
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, dim3(kThreads), 0, ctx->stream, a);
+    if (plan.qb == 8)
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 8>), grid, block, 0, ctx->stream, a);
+    else if (plan.qb == 4)
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 4>), grid, block, 0, ctx->stream, a);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 1>), grid, dim3(kThreads), 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, block, 0, ctx->stream, a);
   }
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {

@@ -60,7 +60,7 @@ tv_status launch_build_mask(tv_ctx *ctx, const int32_t *parents, int B, int N, u
 struct AttnPlan {
   int S;            // key splits per (sequence, KV head, row block)
   int chunk_tiles;  // 64-key tiles per split
-  int qb;           // 32-row query blocks per wavefront (1 or 2)
+  int qb;           // wavefronts per workgroup (32 query rows each): 2, 4 or 8
   int row_block;    // query rows (node, head-in-group) per workgroup
   int row_blocks;   // ceil(G*N / row_block)
   size_t ws_bytes;  // fp32 partials + (m, l)
