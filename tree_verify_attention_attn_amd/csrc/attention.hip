@@ -83,29 +83,85 @@ __device__ inline void store_out(const AttnArgs &a, int64_t base, int d, const f
   }
 }
 
-// Buffer resource over one KV page (all KV heads): loads outside [0, bytes)
-// return zeros, so an unused or invalid page costs no branch.
-__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t *base, int64_t pid, int page_elems, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base + pid * page_elems), static_cast<short>(0),
-                                           bytes, 0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over one KV page (all KV heads, `bytes` long): loads outside
+// [0, bytes) return zeros, so an unused or invalid page costs no branch.
+__device__ inline i32x4 page_rsrc(const uint16_t *base, int64_t pid, int page_elems, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base + pid * page_elems);
+  i32x4 r;
+  r[0] = static_cast<int>(p & 0xFFFFFFFFull);
+  r[1] = static_cast<int>((p >> 32) & 0xFFFFull);  // stride 0
+  r[2] = bytes;
+  r[3] = 0x00020000;
+  return r;
 }
 
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, 8 / NW) attn_mfma_kernel(AttnArgs a) {
-  constexpr int NT = 64 * NW;              // threads per workgroup
-  constexpr int KS = D / 16;               // 16-wide d steps of S^T = K Q^T
-  constexpr int DB = D / 32;               // 32-wide d blocks of O^T
-  constexpr int RS = D + 8;                // LDS row stride in bf16 (keeps both read patterns conflict-free)
-  constexpr int CPR = D / 8;               // 16-byte chunks per key row
-  constexpr int LPT = kKeys * CPR / NT;    // 16-byte loads per thread per K (and per V) tile
-  constexpr int ROWS_WG = 32 * NW;
-  static_assert(LPT >= 1, "tile too small for the workgroup");
+// 16-byte-per-lane load from a buffer straight into LDS: lane i's data lands
+// at lds_addr + 16 i. Issued as inline assembly so that the compiler does not
+// serialise the multi-stage pipeline with conservative waits; completion is
+// tracked by the explicit vmcnt waits in the tile loop.
+__device__ inline void dma16(uint32_t lds_addr, int voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 
-  __shared__ __align__(16) uint16_t Ks[2][kKeys * RS];
-  __shared__ __align__(16) uint16_t Vs[2][kKeys * RS];
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ inline void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wave-uniform read through the constant address space: a scalar load, so it
+// never waits behind the vector-memory counter that tracks the tile DMA.
+__device__ inline int32_t load_uniform(const int32_t *p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t *>(
+      reinterpret_cast<uintptr_t>(p));
+}
+
+// LDS chunk swizzle of key row r: 16-byte chunk c is stored at position
+// c ^ swz(r). The gfx950 LDS has 64 four-byte banks (256 bytes per cycle);
+// a 16-byte read is served 16 lanes per cycle and an 8-byte transpose read 32
+// lanes per cycle. For the K fragment reads (16 consecutive rows, one chunk
+// each) swz must spread 16 rows over all 64 banks; for the V^T transpose
+// reads (4 consecutive rows x 4 consecutive chunks per 32 lanes) it must move
+// each row's 64-byte group to its own banks. D = 128 (256-byte rows) and
+// D = 64 (128-byte rows, two rows per bank sweep) need different bits.
+template <int D>
+__device__ inline int swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+__device__ inline uint32_t lds_addr_of(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
+}
+
+template <int D, int NW, int STAGES>
+__global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_mfma_kernel(AttnArgs a) {
+  constexpr int KS = D / 16;             // 16-wide d steps of S^T = K Q^T
+  constexpr int DB = D / 32;             // 32-wide d blocks of O^T
+  constexpr int RB = D * 2;              // bytes per key row in LDS (no padding: rows are XOR-swizzled)
+  constexpr int CPR = D / 8;             // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;          // key rows per 1 KB DMA instruction
+  constexpr int IPW = CPR / NW;          // K (and V) DMA instructions per wavefront per tile
+  constexpr int DPW = 2 * IPW;           // DMA instructions per wavefront per tile
+  constexpr int TILE_BYTES = kKeys * RB; // one K (or V) tile
+  constexpr int ROWS_WG = 32 * NW;
+  static_assert(IPW >= 1 && CPR % NW == 0, "workgroup too wide for the tile");
+
+  // stage s: K tile at [s][0], V tile at [s][1]; rows are 2*D bytes with
+  // swizzled chunk positions (see swz), conflict-free without padding
+  __shared__ __align__(1024) uint8_t smem[STAGES][2][TILE_BYTES];
   __shared__ int s_bad;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so DMA operands stay scalar
   const int h = lane >> 5, n = lane & 31;
 
   // block -> (b, g, row group, split); consecutive logical ids share an XCD
@@ -122,6 +178,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_mfma_kernel(AttnArgs a) 
   const int tiles_b = (T + kKeys - 1) / kKeys;
   const int t_begin = s * a.chunk_tiles;
   const int t_end = min(t_begin + a.chunk_tiles, tiles_b);
+  const int ntiles = max(t_end - t_begin, 0);
   if (tid == 0) s_bad = 0;
 
   // ---- the wavefront's 32 query rows: B operands of S^T, kept in VGPRs
@@ -155,69 +212,80 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
-  // ---- K/V tile staging. Thread tid moves chunks c = tid + NT u (key c / CPR,
-  // 16-byte chunk c % CPR). A wavefront's 64 chunks always lie in one page, so
-  // the page id is wave-uniform.
+  // ---- DMA of one tile into one stage. Instruction j moves key rows
+  // [j*RPI, (j+1)*RPI), all inside one page; lane i fills chunk position
+  // i % CPR of row j*RPI + i / CPR with logical chunk (i % CPR) ^ (row & 7).
   const int page_elems = a.Hkv * kPage * D;
   const int page_bytes = page_elems * 2;
   const int64_t pt_row = static_cast<int64_t>(b) * a.maxp;
-  uint4 kr[LPT], vr[LPT];
+  const uint32_t smem_base = lds_addr_of(&smem[0][0][0]);
   bool load_bad = false;
-  auto load_tile = [&](int tile) {
+  auto issue = [&](int tile, int stage) {
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int c = tid + NT * u, key = c / CPR, ch = c % CPR;
-      const int key0 = __builtin_amdgcn_readfirstlane((w * 64 + NT * u) / CPR);
-      const int t0 = tile * kKeys + key0;  // first key of this wavefront's chunk group
+    for (int q = 0; q < IPW; ++q) {
+      const int j = w + NW * q;
+      const int r = j * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(r);
+      const int t0 = tile * kKeys + j * RPI;  // first key of the instruction (wave-uniform)
       int pid = -1;
-      if (t0 < T) pid = __builtin_amdgcn_readfirstlane(a.page_table[pt_row + t0 / kPage]);
+      if (t0 < T) pid = load_uniform(a.page_table + pt_row + t0 / kPage);
       const bool ok = pid >= 0 && pid < a.num_pages;
       load_bad |= (t0 < T) && !ok;
-      const int t = tile * kKeys + key;
-      const int voff = t < T ? ((g * kPage + t % kPage) * D + ch * 8) * 2 : 0x7FFFFFF0;
+      const int t = tile * kKeys + r;
+      const int voff = t < T ? ((g * kPage + t % kPage) * D + c * 8) * 2 : 0x7FFFFFF0;
       const int bytes = ok ? page_bytes : 0;
-      const __amdgpu_buffer_rsrc_t rk = page_rsrc(a.k, ok ? pid : 0, page_elems, bytes);
-      const __amdgpu_buffer_rsrc_t rv = page_rsrc(a.v, ok ? pid : 0, page_elems, bytes);
-      kr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0));
-      vr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0));
+      const uint32_t dst = smem_base + (stage * 2) * TILE_BYTES + j * 1024;
+      dma16(dst, voff, page_rsrc(a.k, ok ? pid : 0, page_elems, bytes));
+      dma16(dst + TILE_BYTES, voff, page_rsrc(a.v, ok ? pid : 0, page_elems, bytes));
     }
   };
-  auto store_tile = [&](int buf) {
+
+  // per-lane LDS byte offsets of the fragment reads (swizzled chunk positions)
+  int koff[KS];
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int c = tid + NT * u, key = c / CPR, ch = c % CPR;
-      *reinterpret_cast<uint4 *>(&Ks[buf][key * RS + ch * 8]) = kr[u];
-      *reinterpret_cast<uint4 *>(&Vs[buf][key * RS + ch * 8]) = vr[u];
-    }
-  };
-
-  // transpose-read lane pattern for the V^T operand: lane (group grp, slot sl)
-  // addresses key 4*(grp/2) + sl/4 and d 16*(grp%2) + 4*(sl%4) of a 16-key block
+  for (int t = 0; t < KS; ++t) koff[t] = n * RB + (((2 * t + h) ^ swz<D>(n)) << 4);
+  // V^T transpose read: lane (group grp, slot sl) addresses key row
+  // 4h + sl/4 (+16 m2, +8, +32 kb) and d 32 db + 16 (grp % 2) + 4 (sl % 4)
   const int grp = lane >> 4, sl = lane & 15;
-  const int tr_off = (4 * (grp >> 1) + (sl >> 2)) * RS + 16 * (grp & 1) + 4 * (sl & 3);
-
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
+  const int vr = 4 * h + (sl >> 2);  // key row (within 16) of the low half; the high half reads vr + 8
+  int voff_lo[DB], voff_hi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int c = 4 * db + 2 * (grp & 1) + ((sl & 3) >> 1);
+    voff_lo[db] = vr * RB + ((c ^ swz<D>(vr)) << 4) + ((sl & 1) << 3);
+    voff_hi[db] = (vr + 8) * RB + ((c ^ swz<D>(vr + 8)) << 4) + ((sl & 1) << 3);
   }
-  __syncthreads();
 
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    const int cur = (tile - t_begin) & 1;
-    const bool has_next = tile + 1 < t_end;
-    if (has_next) load_tile(tile + 1);
+#pragma unroll
+  for (int k = 0; k < STAGES - 1; ++k)
+    if (k < ntiles) issue(t_begin + k, k);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int tile = t_begin + it;
+    // wait for this tile's DMA (younger groups may stay in flight), then make
+    // every wavefront's part visible; the barrier also retires the stage that
+    // the next issue overwrites
+    const int younger = min(STAGES - 2, ntiles - 1 - it);
+    if (younger >= 2)
+      wait_vmcnt<2 * DPW>();
+    else if (younger == 1)
+      wait_vmcnt<DPW>();
+    else
+      wait_vmcnt<0>();
+    barrier_only();
+    if (it + STAGES - 1 < ntiles) issue(tile + STAGES - 1, (it + STAGES - 1) % STAGES);
 
     if (wave_active) {
-      const uint16_t *Kb = Ks[cur];
-      const uint16_t *Vb = Vs[cur];
-      // S^T = K Q^T for 64 keys (two 32-key blocks); all K fragments are
-      // read first so the LDS latency overlaps instead of serialising MFMAs
+      const int stage = it % STAGES;
+      const uint8_t *Kb = &smem[stage][0][0];
+      const uint8_t *Vb = &smem[stage][1][0];
+      // S^T = K Q^T for 64 keys (two 32-key blocks); all K fragments first
       bf16x8 kf[2][KS];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int t = 0; t < KS; ++t)
-          kf[kb][t] = *reinterpret_cast<const bf16x8 *>(&Kb[(kb * 32 + n) * RS + 16 * t + 8 * h]);
+          kf[kb][t] = *reinterpret_cast<const bf16x8 *>(Kb + kb * 32 * RB + koff[t]);
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -234,9 +302,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_mfma_kernel(AttnArgs a) 
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int m2 = 0; m2 < 2; ++m2) {
-            const uint16_t *vp = Vb + (kb * 32 + 16 * m2) * RS + db * 32 + tr_off;
-            const bf16x4 lo = lds_read_tr16(vp);
-            const bf16x4 hi = lds_read_tr16(vp + 8 * RS);
+            const uint8_t *vb = Vb + (kb * 32 + 16 * m2) * RB;
+            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + voff_lo[db]));
+            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + voff_hi[db]));
             vf[db][kb][m2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
 
@@ -277,8 +345,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_mfma_kernel(AttnArgs a) 
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], a.c, -mu));
-          if (need_mask && sc[kb][e] == -INFINITY) p = 0.f;
+          // masked scores are -inf and c > 0, so p is exactly 0 for them
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], a.c, -mu));
           l += p;
           pk[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
         }
@@ -293,9 +361,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_mfma_kernel(AttnArgs a) 
           for (int m2 = 0; m2 < 2; ++m2)
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][kb][m2], pk[kb][m2], o[db], 0, 0, 0);
     }
-
-    if (has_next) store_tile(cur ^ 1);
-    __syncthreads();
   }
   if (load_bad) s_bad = 1;
   __syncthreads();
@@ -410,7 +475,9 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   a.rows = a.G * N;
   a.rows_pad = plan.row_blocks * plan.row_block;
   a.row_groups = plan.row_blocks;
-  a.c = fabsf(sm_scale) * kLog2e;
+  // c > 0 keeps exp2(-inf * c) = 0 for masked keys; a zero scale becomes a
+  // negligible positive one (every score then rounds to the same value)
+  a.c = fmaxf(fabsf(sm_scale) * kLog2e, 1e-30f);
   a.negate_q = sm_scale < 0.f;
   a.out = out;
   a.out_bf16 = out_dtype == TV_BF16;
@@ -425,20 +492,21 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   a.xcd_remap = (blocks % 8) == 0;
   const dim3 grid(blocks);
   const dim3 block(64 * plan.qb);
+  constexpr int kStages = 4;
   if (D == 128) {
     if (plan.qb == 8)
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 8>), grid, block, 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 8, kStages>), grid, block, 0, ctx->stream, a);
     else if (plan.qb == 4)
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, block, 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 4, kStages>), grid, block, 0, ctx->stream, a);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 2>), grid, block, 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<128, 2, kStages>), grid, block, 0, ctx->stream, a);
   } else {
     if (plan.qb == 8)
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 8>), grid, block, 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 8, kStages>), grid, block, 0, ctx->stream, a);
     else if (plan.qb == 4)
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 4>), grid, block, 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 4, kStages>), grid, block, 0, ctx->stream, a);
     else
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 2>), grid, block, 0, ctx->stream, a);
+      hipLaunchKernelGGL((attn_mfma_kernel<64, 2, kStages>), grid, block, 0, ctx->stream, a);
   }
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
