@@ -36,6 +36,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kKeys = 64;      // keys per tile
+constexpr int kMaxChunkTiles = 256;  // tiles per key split (bounds the LDS copy of its page ids)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -117,13 +118,6 @@ __device__ inline void wait_vmcnt() {
 
 __device__ inline void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-// Wave-uniform read through the constant address space: a scalar load, so it
-// never waits behind the vector-memory counter that tracks the tile DMA.
-__device__ inline int32_t load_uniform(const int32_t *p) {
-  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t *>(
-      reinterpret_cast<uintptr_t>(p));
-}
-
 // LDS chunk swizzle of key row r: 16-byte chunk c is stored at position
 // c ^ swz(r). The gfx950 LDS has 64 four-byte banks (256 bytes per cycle);
 // a 16-byte read is served 16 lanes per cycle and an 8-byte transpose read 32
@@ -159,6 +153,7 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   // swizzled chunk positions (see swz), conflict-free without padding
   __shared__ __align__(1024) uint8_t smem[STAGES][2][TILE_BYTES];
   __shared__ int s_bad;
+  __shared__ int s_pid[kMaxChunkTiles * (kKeys / kPage)];  // page ids of this split's tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so DMA operands stay scalar
@@ -187,7 +182,8 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   const bool row_ok = row < a.rows;
   const int node = row_ok ? row / a.G : 0;
   const int head = g * a.G + (row_ok ? row % a.G : 0);
-  const uint64_t mword = (row_ok && a.mask) ? a.mask[static_cast<int64_t>(b) * a.N + node] : ~0ull;
+  const uint64_t node_bits = a.N >= 64 ? ~0ull : ((1ull << a.N) - 1ull);  // tree positions that exist
+  const uint64_t mword = ((row_ok && a.mask) ? a.mask[static_cast<int64_t>(b) * a.N + node] : ~0ull) & node_bits;
   bf16x8 qf[KS];
   {
     const uint16_t *qrow = a.q + ((static_cast<int64_t>(b) * a.N + node) * a.Hq + head) * D;
@@ -228,7 +224,7 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
       const int c = (lane % CPR) ^ swz<D>(r);
       const int t0 = tile * kKeys + j * RPI;  // first key of the instruction (wave-uniform)
       int pid = -1;
-      if (t0 < T) pid = load_uniform(a.page_table + pt_row + t0 / kPage);
+      if (t0 < T) pid = __builtin_amdgcn_readfirstlane(s_pid[(tile - t_begin) * (kKeys / kPage) + j * RPI / kPage]);
       const bool ok = pid >= 0 && pid < a.num_pages;
       load_bad |= (t0 < T) && !ok;
       const int t = tile * kKeys + r;
@@ -239,6 +235,15 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
       dma16(dst + TILE_BYTES, voff, page_rsrc(a.v, ok ? pid : 0, page_elems, bytes));
     }
   };
+
+  // page ids of this split's tiles, copied once into LDS so that the DMA issue
+  // path never waits on a memory round trip (-1 past the sequence's pages)
+  {
+    const int p0 = t_begin * (kKeys / kPage);
+    const int used = min(t_end * (kKeys / kPage), (T + kPage - 1) / kPage) - p0;
+    for (int i = tid; i < ntiles * (kKeys / kPage); i += 64 * NW) s_pid[i] = i < used ? a.page_table[pt_row + p0 + i] : -1;
+    __syncthreads();
+  }
 
   // per-lane LDS byte offsets of the fragment reads (swizzled chunk positions)
   int koff[KS];
@@ -256,16 +261,136 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     voff_hi[db] = (vr + 8) * RB + ((c ^ swz<D>(vr + 8)) << 4) + ((sl & 1) << 3);
   }
 
+  // One tile for this wavefront, as an explicit interleaved schedule. A
+  // wavefront can keep at most 15 LDS reads outstanding, so issuing all 48
+  // fragment reads of a tile in one burst stalls instruction issue; instead
+  // the reads are spread over the matrix products and the softmax VALU work
+  // that precede their use (sched_barrier fences pin the order):
+  //   K block 0 reads | S block 0 MFMAs + K block 1 reads | S block 1 MFMAs +
+  //   V^T d-block 0 reads | row max, rescale | exp work + V^T d-blocks 1, 2 |
+  //   PV d-block 0 MFMAs + V^T d-block 3 | PV d-blocks 1..3 MFMAs.
+  auto tile_step = [&](int stage, int tile) {
+    const uint8_t *Kb = &smem[stage][0][0];
+    const uint8_t *Vb = &smem[stage][1][0];
+    auto kread = [&](int kb, int t) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8 *>(Kb + kb * 32 * RB + koff[t]);
+    };
+    // V^T fragment (db, kb, m2) is two transpose reads; index f = kb * 2 + m2
+    auto vread = [&](int db, int f, int half) -> bf16x4 {
+      const uint8_t *vb = Vb + ((f >> 1) * 32 + 16 * (f & 1)) * RB;
+      return lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + (half ? voff_hi[db] : voff_lo[db])));
+    };
+    bf16x8 kf[2][KS];
+    bf16x4 vh[DB][4][2];
+    f32x16 sc[2];
 #pragma unroll
-  for (int k = 0; k < STAGES - 1; ++k)
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < KS; ++t) kf[0][t] = kread(0, t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][t], qf[t], sc[0], 0, 0, 0);
+      kf[1][t] = kread(1, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // V^T d-block 0 (8 transpose reads) under the S block 1 products
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][t], qf[t], sc[1], 0, 0, 0);
+#pragma unroll
+      for (int r = (t * 8) / KS; r < ((t + 1) * 8) / KS; ++r) vh[0][r >> 1][r & 1] = vread(0, r >> 1, r & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // visibility (only tiles that reach the tree positions or the tail): one
+    // 64-bit word per tile, bit k = key tile0 + k is visible to this row
+    const int tile0 = tile * kKeys;
+    if (tile0 + kKeys > L) {
+      const int off = tile0 - L;  // key k of the tile is tree node off + k; -64 < off < N
+      const uint64_t tree = off >= 0 ? (mword >> off) : (mword << -off);
+      const int pre = L - tile0;  // keys k < pre belong to the prefix
+      const uint64_t prefix = pre <= 0 ? 0ull : ((1ull << pre) - 1ull);
+      const uint64_t vis64 = prefix | tree;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t vb = static_cast<uint32_t>(vis64 >> (kb * 32 + 4 * h));
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          sc[kb][e] = ((vb >> (8 * (e >> 2) + (e & 3))) & 1u) ? sc[kb][e] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+    mx = swap_halves_max(mx);
+    const float mt = mx == -INFINITY ? -INFINITY : mx * a.c;
+    // lazy rescale: only when some row's max grows by more than 2^kRescale
+    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescale) != 0ull) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      m_ref = m_new;
+    }
+    const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+
+    // exp work, with the V^T reads of d-blocks 1 and 2 spread through it
+    // (masked scores are -inf and c > 0, so their p is exactly 0)
+    constexpr int VMID = DB > 2 ? 2 : DB - 1;  // d-blocks read during the exps
+    bf16x8 pk[2][2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = g * 4 + u, kb = q >> 4, e = q & 15;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], a.c, -mu));
+        l += p;
+        pk[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
+      }
+#pragma unroll
+      for (int r = (g * 8 * VMID) / 8; r < ((g + 1) * 8 * VMID) / 8; ++r)
+        vh[1 + r / 8][(r & 7) >> 1][r & 1] = vread(1 + r / 8, (r & 7) >> 1, r & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // PV: d-block 0 under the reads of the remaining d-blocks, then the rest
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const bf16x8 va = __builtin_shufflevector(vh[db][f][0], vh[db][f][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[f >> 1][f & 1], o[db], 0, 0, 0);
+        if (db == 0) {
+#pragma unroll
+          for (int r = 2 * f; r < 2 * f + 2; ++r)
+#pragma unroll
+            for (int dd = 1 + VMID; dd < DB; ++dd) vh[dd][r >> 1][r & 1] = vread(dd, r >> 1, r & 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  constexpr int PD = STAGES - 1;  // tiles of DMA in flight ahead of the one computed
+#pragma unroll
+  for (int k = 0; k < PD; ++k)
     if (k < ntiles) issue(t_begin + k, k);
 
   for (int it = 0; it < ntiles; ++it) {
-    const int tile = t_begin + it;
-    // wait for this tile's DMA (younger groups may stay in flight), then make
-    // every wavefront's part visible; the barrier also retires the stage that
-    // the next issue overwrites
-    const int younger = min(STAGES - 2, ntiles - 1 - it);
+    // wait for this tile's DMA (younger groups may stay in flight), make every
+    // wavefront's part visible, then refill the stage that the barrier retired
+    const int younger = min(PD - 1, ntiles - 1 - it);
     if (younger >= 2)
       wait_vmcnt<2 * DPW>();
     else if (younger == 1)
@@ -273,94 +398,8 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     else
       wait_vmcnt<0>();
     barrier_only();
-    if (it + STAGES - 1 < ntiles) issue(tile + STAGES - 1, (it + STAGES - 1) % STAGES);
-
-    if (wave_active) {
-      const int stage = it % STAGES;
-      const uint8_t *Kb = &smem[stage][0][0];
-      const uint8_t *Vb = &smem[stage][1][0];
-      // S^T = K Q^T for 64 keys (two 32-key blocks); all K fragments first
-      bf16x8 kf[2][KS];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < KS; ++t)
-          kf[kb][t] = *reinterpret_cast<const bf16x8 *>(Kb + kb * 32 * RB + koff[t]);
-      f32x16 sc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
-#pragma unroll
-        for (int t = 0; t < KS; ++t) sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][t], qf[t], sc[kb], 0, 0, 0);
-      }
-      // V^T fragments for the PV product, issued now so they land during the softmax
-      bf16x8 vf[DB][2][2];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int m2 = 0; m2 < 2; ++m2) {
-            const uint8_t *vb = Vb + (kb * 32 + 16 * m2) * RB;
-            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + voff_lo[db]));
-            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + voff_hi[db]));
-            vf[db][kb][m2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-
-      // visibility (only tiles that reach the tree positions or the tail)
-      const int tile0 = tile * kKeys;
-      const bool need_mask = tile0 + kKeys > L;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int t = tile0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-            const bool vis = t < T && (t < L || ((mword >> ((t - L) & 63)) & 1ull));
-            if (!vis) sc[kb][e] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-      mx = swap_halves_max(mx);
-      const float mt = mx == -INFINITY ? -INFINITY : mx * a.c;
-      // lazy rescale: only when some row's max grows by more than 2^kRescale
-      if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescale) != 0ull) {
-        const float m_new = fmaxf(m_ref, mt);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-        m_ref = m_new;
-      }
-      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-      bf16x8 pk[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          // masked scores are -inf and c > 0, so p is exactly 0 for them
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], a.c, -mu));
-          l += p;
-          pk[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
-        }
-      }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int m2 = 0; m2 < 2; ++m2)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][kb][m2], pk[kb][m2], o[db], 0, 0, 0);
-    }
+    if (it + PD < ntiles) issue(t_begin + it + PD, (it + PD) % STAGES);
+    if (wave_active) tile_step(it % STAGES, t_begin + it);
   }
   if (load_bad) s_bad = 1;
   __syncthreads();
@@ -443,6 +482,7 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
   int64_t S = base > 0 ? (target + base / 2) / base : 1;
   if (S < 1) S = 1;
   if (S > tiles) S = tiles;
+  if (S < (tiles + kMaxChunkTiles - 1) / kMaxChunkTiles) S = (tiles + kMaxChunkTiles - 1) / kMaxChunkTiles;
   if (S < 1) S = 1;
   p.chunk_tiles = static_cast<int>((tiles + S - 1) / S);
   if (p.chunk_tiles < 1) p.chunk_tiles = 1;
