@@ -30,11 +30,14 @@ BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published peak
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run one device-to-device copy of this many MiB (an HBM counter "
+                         "calibration point for rocprofv3 --pmc runs)")
     return ap.parse_args()
 
 
@@ -66,6 +69,36 @@ def accept_bytes(w):
         return w.B * w.N * w.V * 4 + w.B * w.N * 4 * 3
     # target rows, draft rows 1..N-1, and one re-read of a target and a draft row for the final draw
     return (w.B * w.N + w.B * (w.N - 1)) * w.V * 4 + 2 * w.B * w.V * 4 + w.B * w.N * 4 * 3
+
+
+KERNEL_SOURCES = {"tv_attention": "attention.hip", "tv_accept": "accept.hip", "tv_build_mask": "mask.hip"}
+CALL_KERNELS = {"tv_attention": "attn_mfma_kernel (+ attn_combine_kernel when the keys are split)",
+                "tv_accept": "argmax_chunk_kernel + greedy_path_kernel (greedy) or softmax_chunk_kernel + "
+                             "stochastic_path_kernel (stochastic)",
+                "tv_build_mask": "build_mask_kernel"}
+
+
+def measured_traffic(call, cfg):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summaries (already scaled by the copy-kernel calibration), used only while
+    the source hash recorded with them matches the current kernel source."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[call], "tv_internal.h"):
+        with open(os.path.join(ROOT, "tree_verify_attention_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    src = h.hexdigest()[:16]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.txt"))):
+        with open(path) as fh:
+            for line in fh:
+                parts = line.split()
+                if len(parts) == 6 and parts[0] == "traffic" and parts[1] == call:
+                    kv = dict(p.split("=", 1) for p in parts[2:])
+                    if int(kv["config"]) == cfg and kv["src"] == src:
+                        return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def cpu_baseline(w, depth, target_s, threads):
@@ -198,14 +231,24 @@ def main():
         "config": {"workload": workload_name(w, c), "batch": w.B, "tree_nodes": w.N, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.D, "max_prefix_len": w.max_prefix_len, "vocab": w.V,
                    "accept": w.mode, "page_size": 16, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": None,
+        "roofline": {"bound": "hbm", "kernel": f"{dom}: {CALL_KERNELS[dom]}", "achieved": dk["gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["gbs"] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(dom, args.config),
+                     "algorithmic_bytes": dk["bytes"],
                      "note": "achieved = algorithmic bytes per call / mean call duration (HIP events on the "
-                             "launch stream over the timed steps)"},
+                             "launch stream over the timed steps); traffic = calibrated rocprofv3 "
+                             "FETCH_SIZE + WRITE_SIZE bytes per call, null when not measured for this source"},
         "kernels": kernels,
         "tau": tau,
         "tau_cycles": cycles,
     }
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(w, depth, args.cpu_seconds, threads)
