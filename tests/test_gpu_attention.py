@@ -83,6 +83,28 @@ def test_deterministic_and_page_permutation_invariant():
     assert np.array_equal(a, c), "page relocation changed the result"
 
 
+@pytest.mark.parametrize("D,Hkv,Hq", [(128, 2, 8), (64, 4, 16)])
+def test_kv_pool_above_2gib(D, Hkv, Hq):
+    """Pages placed past the first 2 GiB of a KV pool take the per-page buffer
+    resource path (smaller pools share one resource with 32-bit offsets)."""
+    w = small("random", N=24, L=(300, 700), D=D, Hkv=Hkv, Hq=Hq, seed=12)
+    page_bytes = Hkv * 16 * D * 2
+    offset = (2 ** 31) // page_bytes + 3000
+    print(f"[attn] KV pool above 2 GiB, D{D} Hkv{Hkv}, page offset {offset}", flush=True)
+    dw = DevWorkload(w, logits=False)
+    big_k = torch.empty((offset + w.num_pages, Hkv, 16, D), dtype=torch.bfloat16, device=DEV)
+    big_v = torch.empty_like(big_k)
+    big_k[offset:] = dw.k
+    big_v[offset:] = dw.v
+    table = torch.where(dw.page_table >= 0, dw.page_table + offset, dw.page_table)
+    mask = tv.tv_build_mask(dw.parents)[0]
+    out = tv.tv_attention(dw.q, big_k, big_v, table, dw.prefix_lens, w.max_prefix_len, mask, float(w.sm_scale))
+    assert tv.tv_device_error(DEV) == 0
+    ref = oracle.attention(w, oracle.build_mask(w.parents)[0])
+    check_attention(host(out), ref, tight=TIGHT, what=f"pool above 2 GiB, D{D}")
+    del big_k, big_v
+
+
 def sample_rows(w, n, seed=0):
     rng = np.random.default_rng(seed)
     rows = np.stack([rng.integers(0, w.B, n), rng.integers(0, w.N, n), rng.integers(0, w.Hq, n)], 1)

@@ -8,8 +8,9 @@
 // Work unit: one (sequence b, KV head g, row group, key split). The G query
 // heads of a GQA group share the KV head, so the G*N (node, head) rows of a
 // (b, g) pair form the query side of one dense product and each 64-key K/V
-// tile is read from HBM once per row group, staged in LDS and shared by the
-// four wavefronts of the workgroup.
+// tile is read from HBM once per row group, staged in LDS by LDS-DMA
+// (buffer_load ... lds) through a four-stage ring per K and V, and shared by
+// the workgroup's wavefronts (32 query rows each).
 //
 // Matrix cores: S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16
 // d from LDS, B = 16 d x 32 queries held in VGPRs). In the 32x32 result a lane
@@ -22,6 +23,11 @@
 // when a row's running max grows by more than 2^8, which bounds p <= 256.
 // Only tiles that reach the tree positions or the sequence tail evaluate the
 // mask; prefix tiles never do.
+//
+// Schedule: the two halves of the workgroup share SIMDs (wavefront w and
+// w + NW/2) and run the same code offset by one barrier, so while one half
+// runs a tile's matrix products (X phase) the other runs the softmax of the
+// previous tile (Y phase) on the vector ALU.
 #include <math.h>
 
 #include "tv_internal.h"
@@ -136,7 +142,7 @@ __device__ inline uint32_t lds_addr_of(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
 }
 
-template <int D, int NW, int STAGES>
+template <int D, int NW, int STAGES, bool FLAT>
 __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 16;             // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;             // 32-wide d blocks of O^T
@@ -208,32 +214,78 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
-  // ---- DMA of one tile into one stage. Instruction j moves key rows
-  // [j*RPI, (j+1)*RPI), all inside one page; lane i fills chunk position
-  // i % CPR of row j*RPI + i / CPR with logical chunk (i % CPR) ^ (row & 7).
+  // ---- DMA. K tiles and V tiles have rings of their own (tile j of the
+  // split uses stage j % STAGES of each). A tile's 16-byte chunks are moved
+  // by 1 KB instructions: instruction jj covers key rows [jj*RPI, (jj+1)*RPI)
+  // (inside one page) and lane i fills chunk position i % CPR of row
+  // jj*RPI + i / CPR with logical chunk (i % CPR) ^ swz(row). Wavefront w
+  // issues the IPW consecutive instructions jj = w*IPW + q, which share one
+  // page whenever IPW*RPI <= 16, so a page id is looked up once per page.
+  // FLAT: the whole K (and V) pool is below 2 GiB, so one buffer resource per
+  // pool serves every page and the page's byte offset goes into the VGPR
+  // offset; an invalid page or a key past the sequence gets an offset past
+  // the resource's size, which loads zeros. Otherwise each page gets its own
+  // resource (size 0 when the page id is invalid).
+  constexpr int PPW = (IPW * RPI + kPage - 1) / kPage;  // pages per wavefront per tile
   const int page_elems = a.Hkv * kPage * D;
   const int page_bytes = page_elems * 2;
+  const uint32_t npages32 = static_cast<uint32_t>(min(a.num_pages, static_cast<int64_t>(0x7FFFFFFF)));
   const int64_t pt_row = static_cast<int64_t>(b) * a.maxp;
   const uint32_t smem_base = lds_addr_of(&smem[0][0][0]);
   bool load_bad = false;
-  auto issue = [&](int tile, int stage) {
+  int dma_off[IPW];  // byte offset of the lane's chunk inside its page (row slot, KV head, chunk)
 #pragma unroll
-    for (int q = 0; q < IPW; ++q) {
-      const int j = w + NW * q;
-      const int r = j * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ swz<D>(r);
-      const int t0 = tile * kKeys + j * RPI;  // first key of the instruction (wave-uniform)
-      int pid = -1;
-      if (t0 < T) pid = __builtin_amdgcn_readfirstlane(s_pid[(tile - t_begin) * (kKeys / kPage) + j * RPI / kPage]);
-      const bool ok = pid >= 0 && pid < a.num_pages;
-      load_bad |= (t0 < T) && !ok;
-      const int t = tile * kKeys + r;
-      const int voff = t < T ? ((g * kPage + t % kPage) * D + c * 8) * 2 : 0x7FFFFFF0;
-      const int bytes = ok ? page_bytes : 0;
-      const uint32_t dst = smem_base + (stage * 2) * TILE_BYTES + j * 1024;
-      dma16(dst, voff, page_rsrc(a.k, ok ? pid : 0, page_elems, bytes));
-      dma16(dst + TILE_BYTES, voff, page_rsrc(a.v, ok ? pid : 0, page_elems, bytes));
+  for (int q = 0; q < IPW; ++q) {
+    const int r = (w * IPW + q) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(r);
+    dma_off[q] = ((g * kPage + r % kPage) * D + c * 8) * 2;
+  }
+  const int lane_row = lane / CPR;
+  i32x4 pool_rsrc[2];
+  if constexpr (FLAT) {
+    const int pool_bytes = static_cast<int>(a.num_pages * page_bytes);
+    pool_rsrc[0] = page_rsrc(a.k, 0, 0, pool_bytes);
+    pool_rsrc[1] = page_rsrc(a.v, 0, 0, pool_bytes);
+  }
+  // page ids of tile j for this wavefront, read from LDS (the value is
+  // uniform; it is read ahead of the issue so that the LDS latency is hidden)
+  auto fetch = [&](int j, int (&pid)[PPW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) pid[p] = s_pid[j * (kKeys / kPage) + (w * IPW * RPI) / kPage + p];
+  };
+  auto issue = [&](int j, int part, const int (&pidv)[PPW]) __attribute__((always_inline)) {
+    const int tile0 = (t_begin + j) * kKeys;
+    const int row0 = w * IPW * RPI;  // first key row of this wavefront's instructions
+    const bool full = tile0 + row0 + IPW * RPI <= T;
+    const uint32_t dst0 = smem_base + ((j % STAGES) * 2 + part) * TILE_BYTES + w * IPW * 1024;
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+      const int pid = __builtin_amdgcn_readfirstlane(pidv[p]);
+      const bool ok = static_cast<uint32_t>(pid) < npages32;
+      if (part == 0) load_bad |= (tile0 + row0 + p * kPage < T) && !ok;
+      if constexpr (FLAT) {
+        const int poff = ok ? pid * page_bytes : static_cast<int>(0x80000000u);
+#pragma unroll
+        for (int q = p * IPW / PPW; q < (p + 1) * IPW / PPW; ++q) {
+          int voff = poff + dma_off[q];
+          if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = static_cast<int>(0x80000000u);
+          dma16(dst0 + q * 1024, voff, pool_rsrc[part]);
+        }
+      } else {
+        const i32x4 rs = page_rsrc(part ? a.v : a.k, ok ? pid : 0, page_elems, ok ? page_bytes : 0);
+#pragma unroll
+        for (int q = p * IPW / PPW; q < (p + 1) * IPW / PPW; ++q) {
+          int voff = dma_off[q];
+          if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = 0x7FFFFFF0;
+          dma16(dst0 + q * 1024, voff, rs);
+        }
+      }
     }
+  };
+  auto issue_now = [&](int j, int part) __attribute__((always_inline)) {
+    int pid[PPW];
+    fetch(j, pid);
+    issue(j, part, pid);
   };
 
   // page ids of this split's tiles, copied once into LDS so that the DMA issue
@@ -261,55 +313,97 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     voff_hi[db] = (vr + 8) * RB + ((c ^ swz<D>(vr + 8)) << 4) + ((sl & 1) << 3);
   }
 
-  // One tile for this wavefront, as an explicit interleaved schedule. A
-  // wavefront can keep at most 15 LDS reads outstanding, so issuing all 48
-  // fragment reads of a tile in one burst stalls instruction issue; instead
-  // the reads are spread over the matrix products and the softmax VALU work
-  // that precede their use (sched_barrier fences pin the order):
-  //   K block 0 reads | S block 0 MFMAs + K block 1 reads | S block 1 MFMAs +
-  //   V^T d-block 0 reads | row max, rescale | exp work + V^T d-blocks 1, 2 |
-  //   PV d-block 0 MFMAs + V^T d-block 3 | PV d-blocks 1..3 MFMAs.
-  auto tile_step = [&](int stage, int tile) {
-    const uint8_t *Kb = &smem[stage][0][0];
-    const uint8_t *Vb = &smem[stage][1][0];
-    auto kread = [&](int kb, int t) -> bf16x8 {
-      return *reinterpret_cast<const bf16x8 *>(Kb + kb * 32 * RB + koff[t]);
-    };
-    // V^T fragment (db, kb, m2) is two transpose reads; index f = kb * 2 + m2
-    auto vread = [&](int db, int f, int half) -> bf16x4 {
-      const uint8_t *vb = Vb + ((f >> 1) * 32 + 16 * (f & 1)) * RB;
-      return lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + (half ? voff_hi[db] : voff_lo[db])));
-    };
-    bf16x8 kf[2][KS];
-    bf16x4 vh[DB][4][2];
-    f32x16 sc[2];
+  auto kread = [&](int st, int kb, int t) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(&smem[st][0][0] + kb * 32 * RB + koff[t]);
+  };
+  // V^T fragment (db, f) of a tile, f = 2 kb + m2 (32-key block kb, 16-key
+  // half m2), is two transpose reads (keys +0 and +8)
+  auto vread = [&](int st, int db, int f, int half) -> bf16x4 {
+    const uint8_t *vb = &smem[st][1][0] + ((f >> 1) * 32 + 16 * (f & 1)) * RB;
+    return lds_read_tr16(reinterpret_cast<const uint16_t *>(vb + (half ? voff_hi[db] : voff_lo[db])));
+  };
+
+  f32x16 sc[2];     // S_j^T (two 32-key blocks), from the X phase of tile j to its Y phase
+  bf16x8 pk[2][2];  // P_j in bf16, from the Y phase of tile j to the X phase of tile j + 1
+
+  // X phase of tile j (matrix cores): when j > 0, O += V_{j-1}^T P_{j-1}^T,
+  // then S_j = K_j Q^T. PV goes first so that P_{j-1} is dead before S_j is
+  // born. Fragment reads run two steps ahead of the products that use them,
+  // and the four O chains and the two S chains alternate, so no MFMA waits on
+  // the one before it. `mid` runs after the first products (the DMA issue of
+  // the wavefronts whose turn it is). For j == n the S products read a stale
+  // stage; their result is never used.
+  auto X = [&](int j, auto &&mid) __attribute__((always_inline)) {
+    const int ks = j % STAGES, vs = (j + STAGES - 1) % STAGES;
+    bf16x8 kf[3][2];
+    __builtin_amdgcn_sched_barrier(0);
+    if (j > 0) {
+      bf16x4 vh[3][DB][2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          vh[f][db][0] = vread(vs, db, f, 0);
+          vh[f][db][1] = vread(vs, db, f, 1);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (f + 2 < 4) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            vh[(f + 2) % 3][db][0] = vread(vs, db, f + 2, 0);
+            vh[(f + 2) % 3][db][1] = vread(vs, db, f + 2, 1);
+          }
+        } else {
+          kf[f - 2][0] = kread(ks, 0, f - 2);
+          kf[f - 2][1] = kread(ks, 1, f - 2);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 va = __builtin_shufflevector(vh[f % 3][db][0], vh[f % 3][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[f >> 1][f & 1], o[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (f == 0) {
+          mid();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        kf[t][0] = kread(ks, 0, t);
+        kf[t][1] = kread(ks, 1, t);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
-
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < KS; ++t) kf[0][t] = kread(0, t);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][t], qf[t], sc[0], 0, 0, 0);
-      kf[1][t] = kread(1, t);
+      if (t + 2 < KS) {
+        kf[(t + 2) % 3][0] = kread(ks, 0, t + 2);
+        kf[(t + 2) % 3][1] = kread(ks, 1, t + 2);
+      }
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % 3][0], qf[t], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % 3][1], qf[t], sc[1], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // V^T d-block 0 (8 transpose reads) under the S block 1 products
-#pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][t], qf[t], sc[1], 0, 0, 0);
-#pragma unroll
-      for (int r = (t * 8) / KS; r < ((t + 1) * 8) / KS; ++r) vh[0][r >> 1][r & 1] = vread(0, r >> 1, r & 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  };
 
+  // Y phase of tile j (vector ALU): tree/tail visibility, running max, lazy
+  // rescale, exponentials, row sums and the bf16 P_j for the next X phase.
+  // `mid` runs after the row max (the DMA issue of the wavefronts whose turn
+  // it is), so its scalar work overlaps the exponentials.
+  auto Y = [&](int j, auto &&mid) __attribute__((always_inline)) {
+    const int tile0 = (t_begin + j) * kKeys;
     // visibility (only tiles that reach the tree positions or the tail): one
     // 64-bit word per tile, bit k = key tile0 + k is visible to this row
-    const int tile0 = tile * kKeys;
     if (tile0 + kKeys > L) {
       const int off = tile0 - L;  // key k of the tile is tree node off + k; -64 < off < N
       const uint64_t tree = off >= 0 ? (mword >> off) : (mword << -off);
@@ -343,64 +437,107 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
       m_ref = m_new;
     }
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-
-    // exp work, with the V^T reads of d-blocks 1 and 2 spread through it
-    // (masked scores are -inf and c > 0, so their p is exactly 0)
-    constexpr int VMID = DB > 2 ? 2 : DB - 1;  // d-blocks read during the exps
-    bf16x8 pk[2][2];
-    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    // masked scores are -inf and c > 0, so their p is exactly 0. P_j is built
+    // in fresh vectors: element inserts into pk itself would keep P_{j-1}
+    // live through this phase.
+    bf16x8 np[2][2];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = g * 4 + u, kb = q >> 4, e = q & 15;
+      for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], a.c, -mu));
         l += p;
-        pk[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
+        np[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
       }
 #pragma unroll
-      for (int r = (g * 8 * VMID) / 8; r < ((g + 1) * 8 * VMID) / 8; ++r)
-        vh[1 + r / 8][(r & 7) >> 1][r & 1] = vread(1 + r / 8, (r & 7) >> 1, r & 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // PV: d-block 0 under the reads of the remaining d-blocks, then the rest
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const bf16x8 va = __builtin_shufflevector(vh[db][f][0], vh[db][f][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[f >> 1][f & 1], o[db], 0, 0, 0);
-        if (db == 0) {
-#pragma unroll
-          for (int r = 2 * f; r < 2 * f + 2; ++r)
-#pragma unroll
-            for (int dd = 1 + VMID; dd < DB; ++dd) vh[dd][r >> 1][r & 1] = vread(dd, r >> 1, r & 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      pk[kb][0] = np[kb][0];
+      pk[kb][1] = np[kb][1];
     }
   };
 
-  constexpr int PD = STAGES - 1;  // tiles of DMA in flight ahead of the one computed
+  // Ping-pong tile loop. Wavefront w and w + NW/2 share a SIMD; the two
+  // halves of the workgroup run the same code, a Y phase and an X phase per
+  // tile with a barrier after each, but the second half starts one barrier
+  // late. Half-step h (between barriers h-1 and h) thus holds the first
+  // half's Y(k-1) and the second half's X(k-1) when h = 2k, and the first
+  // half's X(k) and the second half's Y(k-1) when h = 2k+1: one half's
+  // matrix products always overlap the other half's exponentials.
+  //   K_j is read at half-steps 2j+1 and 2j+2, V_j (by PV) at 2j+3 and 2j+4.
+  //   With four stages per ring, K_{j+4} and V_{j+3} refill during half-step
+  //   2j+3 (group G_j, issued from inside that half-step's phase) and land
+  //   three tiles before their first use. Waits come before the odd
+  //   half-steps only.
+  const int n_t = ntiles;
+  const bool first = w < NW / 2;  // wave-uniform
+  auto parts = [&](int j) { return j >= 0 && j < n_t ? IPW : 0; };
+  // DMA instructions issued after the group that half-step 2j+1 needs
+  // (K_j and V_{j-1}) and before that half-step
+  auto wait_for = [&](int j) {
+    const int c = j == 0 ? parts(1) + parts(0) + parts(2) + parts(1) + parts(3) + parts(2)
+                         : parts(j + 1) + parts(j) + parts(j + 2) + parts(j + 1);
+    switch (c / IPW) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<IPW>(); break;
+      case 2: wait_vmcnt<2 * IPW>(); break;
+      case 3: wait_vmcnt<3 * IPW>(); break;
+      case 4: wait_vmcnt<4 * IPW>(); break;
+      case 5: wait_vmcnt<5 * IPW>(); break;
+      default: wait_vmcnt<6 * IPW>(); break;
+    }
+  };
+  // prologue groups: K_0 | K_1 V_0 | K_2 V_1 | K_3 V_2
+  if (n_t > 0) issue_now(0, 0);
 #pragma unroll
-  for (int k = 0; k < PD; ++k)
-    if (k < ntiles) issue(t_begin + k, k);
-
-  for (int it = 0; it < ntiles; ++it) {
-    // wait for this tile's DMA (younger groups may stay in flight), make every
-    // wavefront's part visible, then refill the stage that the barrier retired
-    const int younger = min(PD - 1, ntiles - 1 - it);
-    if (younger >= 2)
-      wait_vmcnt<2 * DPW>();
-    else if (younger == 1)
-      wait_vmcnt<DPW>();
-    else
-      wait_vmcnt<0>();
-    barrier_only();
-    if (it + PD < ntiles) issue(t_begin + it + PD, (it + PD) % STAGES);
-    if (wave_active) tile_step(it % STAGES, t_begin + it);
+  for (int j = 1; j < 4; ++j) {
+    if (j < n_t) issue_now(j, 0);
+    if (j - 1 < n_t) issue_now(j - 1, 1);
   }
+  if (!first) {
+    wait_for(0);
+    barrier_only();
+  }
+  for (int k = 0; k <= n_t; ++k) {
+    // group G_{k-1} (K_{k+3}, V_{k+2}) is issued during half-step 2k+1: from
+    // the second half's Y phase here, from the first half's X phase below
+    const bool dma_k = k >= 1 && k + 3 < n_t, dma_v = k >= 1 && k + 2 < n_t;
+    int pidk[PPW], pidv[PPW];
+    auto dma = [&]() __attribute__((always_inline)) {
+      if (dma_k) issue(k + 3, 0, pidk);
+      if (dma_v) issue(k + 2, 1, pidv);
+    };
+    // one instantiation of each phase: the callbacks test the half at run time
+    auto dma_in_y = [&]() __attribute__((always_inline)) {
+      if (!first) dma();
+    };
+    auto dma_in_x = [&]() __attribute__((always_inline)) {
+      if (first) dma();
+    };
+    if (!first) {
+      if (dma_k) fetch(k + 3, pidk);
+      if (dma_v) fetch(k + 2, pidv);
+    }
+    if (k >= 1) {
+      if (wave_active)
+        Y(k - 1, dma_in_y);
+      else
+        dma_in_y();
+    }
+    if (first) wait_for(k);
+    barrier_only();
+    if (first) {
+      if (dma_k) fetch(k + 3, pidk);
+      if (dma_v) fetch(k + 2, pidv);
+    }
+    if (wave_active && n_t > 0)
+      X(k, dma_in_x);
+    else
+      dma_in_x();
+    if (!first) wait_for(k + 1);
+    barrier_only();
+  }
+  if (first) barrier_only();
   if (load_bad) s_bad = 1;
   __syncthreads();
   const bool bad = bad_len || s_bad;
@@ -463,6 +600,26 @@ __global__ void __launch_bounds__(D) attn_combine_kernel(AttnArgs a) {
     static_cast<uint16_t *>(a.out)[idx] = float_to_bf16_bits(val);
   else
     static_cast<float *>(a.out)[idx] = val;
+}
+
+constexpr int kStages = 4;
+
+template <int D, bool FLAT>
+void launch_w(int qb, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
+  if (qb == 8)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 8, kStages, FLAT>), grid, block, 0, st, a);
+  else if (qb == 4)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 4, kStages, FLAT>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT>), grid, block, 0, st, a);
+}
+
+template <int D>
+void launch_dw(int qb, bool flat, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
+  if (flat)
+    launch_w<D, true>(qb, grid, block, st, a);
+  else
+    launch_w<D, false>(qb, grid, block, st, a);
 }
 
 }  // namespace
@@ -532,22 +689,13 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   a.xcd_remap = (blocks % 8) == 0;
   const dim3 grid(blocks);
   const dim3 block(64 * plan.qb);
-  constexpr int kStages = 4;
-  if (D == 128) {
-    if (plan.qb == 8)
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 8, kStages>), grid, block, 0, ctx->stream, a);
-    else if (plan.qb == 4)
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 4, kStages>), grid, block, 0, ctx->stream, a);
-    else
-      hipLaunchKernelGGL((attn_mfma_kernel<128, 2, kStages>), grid, block, 0, ctx->stream, a);
-  } else {
-    if (plan.qb == 8)
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 8, kStages>), grid, block, 0, ctx->stream, a);
-    else if (plan.qb == 4)
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 4, kStages>), grid, block, 0, ctx->stream, a);
-    else
-      hipLaunchKernelGGL((attn_mfma_kernel<64, 2, kStages>), grid, block, 0, ctx->stream, a);
-  }
+  // one buffer resource per pool when the pool is below 2 GiB (page offsets
+  // then fit the 32-bit VGPR offset with room for the out-of-range marker)
+  const bool flat = num_pages * static_cast<int64_t>(Hkv) * kPage * D * 2 <= 0x7FFF0000LL;
+  if (D == 128)
+    launch_dw<128>(plan.qb, flat, grid, block, ctx->stream, a);
+  else
+    launch_dw<64>(plan.qb, flat, grid, block, ctx->stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
     const dim3 cgrid(B * Hkv * a.rows);
