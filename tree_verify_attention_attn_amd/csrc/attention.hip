@@ -253,39 +253,63 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int p = 0; p < PPW; ++p) pid[p] = s_pid[j * (kKeys / kPage) + (w * IPW * RPI) / kPage + p];
   };
-  auto issue = [&](int j, int part, const int (&pidv)[PPW]) __attribute__((always_inline)) {
-    const int tile0 = (t_begin + j) * kKeys;
+  // A DMA item (tile j, part) is issued in three steps: fetch (LDS read of its
+  // page ids, placed before a barrier so that its latency is hidden), resolve
+  // (page ids to wave-uniform page offsets, right after the barrier, when no
+  // other LDS read is outstanding, so the wait for the read is free) and
+  // issue_range (the DMA instructions, spread over the phase; no waits).
+  struct DmaItem {
+    int j, part, poff[PPW];
+    bool on;
+  };
+  auto resolve = [&](int j, int part, bool on, const int (&pidv)[PPW]) __attribute__((always_inline)) {
+    DmaItem it;
+    it.j = j;
+    it.part = part;
+    it.on = on;
+    if (on) {
+      const int tile0 = (t_begin + j) * kKeys;
+#pragma unroll
+      for (int p = 0; p < PPW; ++p) {
+        const int pid = __builtin_amdgcn_readfirstlane(pidv[p]);
+        const bool ok = static_cast<uint32_t>(pid) < npages32;
+        if (part == 0) load_bad |= (tile0 + w * IPW * RPI + p * kPage < T) && !ok;
+        if constexpr (FLAT)
+          it.poff[p] = ok ? pid * page_bytes : static_cast<int>(0x80000000u);
+        else
+          it.poff[p] = ok ? pid : -1;
+      }
+    }
+    return it;
+  };
+  // instructions [q0, q1) of this wavefront's share of an item
+  auto issue_range = [&](const DmaItem &it, int q0, int q1) __attribute__((always_inline)) {
+    if (!it.on) return;
+    const int tile0 = (t_begin + it.j) * kKeys;
     const int row0 = w * IPW * RPI;  // first key row of this wavefront's instructions
     const bool full = tile0 + row0 + IPW * RPI <= T;
-    const uint32_t dst0 = smem_base + ((j % STAGES) * 2 + part) * TILE_BYTES + w * IPW * 1024;
+    const uint32_t dst0 = smem_base + ((it.j % STAGES) * 2 + it.part) * TILE_BYTES + w * IPW * 1024;
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-      const int pid = __builtin_amdgcn_readfirstlane(pidv[p]);
-      const bool ok = static_cast<uint32_t>(pid) < npages32;
-      if (part == 0) load_bad |= (tile0 + row0 + p * kPage < T) && !ok;
+    for (int q = 0; q < IPW; ++q) {
+      if (q < q0 || q >= q1) continue;
+      const int p = q * PPW / IPW;  // page of instruction q
       if constexpr (FLAT) {
-        const int poff = ok ? pid * page_bytes : static_cast<int>(0x80000000u);
-#pragma unroll
-        for (int q = p * IPW / PPW; q < (p + 1) * IPW / PPW; ++q) {
-          int voff = poff + dma_off[q];
-          if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = static_cast<int>(0x80000000u);
-          dma16(dst0 + q * 1024, voff, pool_rsrc[part]);
-        }
+        int voff = it.poff[p] + dma_off[q];
+        if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = static_cast<int>(0x80000000u);
+        dma16(dst0 + q * 1024, voff, pool_rsrc[it.part]);
       } else {
-        const i32x4 rs = page_rsrc(part ? a.v : a.k, ok ? pid : 0, page_elems, ok ? page_bytes : 0);
-#pragma unroll
-        for (int q = p * IPW / PPW; q < (p + 1) * IPW / PPW; ++q) {
-          int voff = dma_off[q];
-          if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = 0x7FFFFFF0;
-          dma16(dst0 + q * 1024, voff, rs);
-        }
+        const bool ok = it.poff[p] >= 0;
+        int voff = dma_off[q];
+        if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = 0x7FFFFFF0;
+        dma16(dst0 + q * 1024, voff,
+              page_rsrc(it.part ? a.v : a.k, ok ? it.poff[p] : 0, page_elems, ok ? page_bytes : 0));
       }
     }
   };
   auto issue_now = [&](int j, int part) __attribute__((always_inline)) {
     int pid[PPW];
     fetch(j, pid);
-    issue(j, part, pid);
+    issue_range(resolve(j, part, true, pid), 0, IPW);
   };
 
   // page ids of this split's tiles, copied once into LDS so that the DMA issue
@@ -330,10 +354,9 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   // then S_j = K_j Q^T. PV goes first so that P_{j-1} is dead before S_j is
   // born. Fragment reads run two steps ahead of the products that use them,
   // and the four O chains and the two S chains alternate, so no MFMA waits on
-  // the one before it. `mid` runs after the first products (the DMA issue of
-  // the wavefronts whose turn it is). For j == n the S products read a stale
+  // the one before it. For j == n the S products read a stale
   // stage; their result is never used.
-  auto X = [&](int j, auto &&mid) __attribute__((always_inline)) {
+  auto X = [&](int j) __attribute__((always_inline)) {
     const int ks = j % STAGES, vs = (j + STAGES - 1) % STAGES;
     bf16x8 kf[3][2];
     __builtin_amdgcn_sched_barrier(0);
@@ -365,10 +388,6 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[f >> 1][f & 1], o[db], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (f == 0) {
-          mid();
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
     } else {
 #pragma unroll
@@ -376,8 +395,6 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
         kf[t][0] = kread(ks, 0, t);
         kf[t][1] = kread(ks, 1, t);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mid();
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -398,8 +415,8 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 
   // Y phase of tile j (vector ALU): tree/tail visibility, running max, lazy
   // rescale, exponentials, row sums and the bf16 P_j for the next X phase.
-  // `mid` runs after the row max (the DMA issue of the wavefronts whose turn
-  // it is), so its scalar work overlaps the exponentials.
+  // `mid(0)` runs after the row max and `mid(1)` halfway through the
+  // exponentials (the DMA issue of the wavefronts whose turn it is).
   auto Y = [&](int j, auto &&mid) __attribute__((always_inline)) {
     const int tile0 = (t_begin + j) * kKeys;
     // visibility (only tiles that reach the tree positions or the tail): one
@@ -437,19 +454,21 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
       m_ref = m_new;
     }
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-    mid();
+    mid(0);
     // masked scores are -inf and c > 0, so their p is exactly 0. P_j is built
     // in fresh vectors: element inserts into pk itself would keep P_{j-1}
     // live through this phase.
     bf16x8 np[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1) mid(1);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], a.c, -mu));
         l += p;
         np[kb][e >> 3][e & 7] = static_cast<__bf16>(p);
       }
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       pk[kb][0] = np[kb][0];
@@ -464,76 +483,58 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   // half's Y(k-1) and the second half's X(k-1) when h = 2k, and the first
   // half's X(k) and the second half's Y(k-1) when h = 2k+1: one half's
   // matrix products always overlap the other half's exponentials.
-  //   K_j is read at half-steps 2j+1 and 2j+2, V_j (by PV) at 2j+3 and 2j+4.
-  //   With four stages per ring, K_{j+4} and V_{j+3} refill during half-step
-  //   2j+3 (group G_j, issued from inside that half-step's phase) and land
-  //   three tiles before their first use. Waits come before the odd
-  //   half-steps only.
+  //   K_j is read at half-steps 2j+1 and 2j+2, V_j (by PV) at 2j+3 and 2j+4,
+  //   and each ring has four stages. All DMA is issued from Y phases, where
+  //   it does not stall the matrix products: during its Y phase of iteration
+  //   k the first half (half-step 2k) refills its share of K_{k+2} and
+  //   V_{k+1}, the second half (half-step 2k+1) its share of K_{k+3} and
+  //   V_{k+2}. Both land at least five half-steps before their first use,
+  //   and each half waits for its own group of two iterations back before
+  //   the odd half-steps.
   const int n_t = ntiles;
   const bool first = w < NW / 2;  // wave-uniform
+  const int lead = first ? 0 : 1;
   auto parts = [&](int j) { return j >= 0 && j < n_t ? IPW : 0; };
-  // DMA instructions issued after the group that half-step 2j+1 needs
-  // (K_j and V_{j-1}) and before that half-step
-  auto wait_for = [&](int j) {
-    const int c = j == 0 ? parts(1) + parts(0) + parts(2) + parts(1) + parts(3) + parts(2)
-                         : parts(j + 1) + parts(j) + parts(j + 2) + parts(j + 1);
-    switch (c / IPW) {
+  // DMA instructions of this wavefront issued after its group holding K_j
+  // and V_{j-1} (what half-step 2j+1 needs) and before that half-step
+  auto wait_for = [&](int j) __attribute__((always_inline)) {
+    switch ((parts(j + 1) + parts(j) + parts(j + 2) + parts(j + 1)) / IPW) {
       case 0: wait_vmcnt<0>(); break;
       case 1: wait_vmcnt<IPW>(); break;
       case 2: wait_vmcnt<2 * IPW>(); break;
       case 3: wait_vmcnt<3 * IPW>(); break;
-      case 4: wait_vmcnt<4 * IPW>(); break;
-      case 5: wait_vmcnt<5 * IPW>(); break;
-      default: wait_vmcnt<6 * IPW>(); break;
+      default: wait_vmcnt<4 * IPW>(); break;
     }
   };
-  // prologue groups: K_0 | K_1 V_0 | K_2 V_1 | K_3 V_2
+  // prologue, in issue order: K_0 | K_1 V_0 (| K_2 V_1 for the second half)
   if (n_t > 0) issue_now(0, 0);
-#pragma unroll
-  for (int j = 1; j < 4; ++j) {
-    if (j < n_t) issue_now(j, 0);
-    if (j - 1 < n_t) issue_now(j - 1, 1);
-  }
+  if (n_t > 1) issue_now(1, 0);
+  if (n_t > 0) issue_now(0, 1);
   if (!first) {
+    if (n_t > 2) issue_now(2, 0);
+    if (n_t > 1) issue_now(1, 1);
     wait_for(0);
     barrier_only();
   }
+  int pid_k[PPW], pid_v[PPW];
+  if (2 + lead < n_t) fetch(2 + lead, pid_k);
+  if (1 + lead < n_t) fetch(1 + lead, pid_v);
   for (int k = 0; k <= n_t; ++k) {
-    // group G_{k-1} (K_{k+3}, V_{k+2}) is issued during half-step 2k+1: from
-    // the second half's Y phase here, from the first half's X phase below
-    const bool dma_k = k >= 1 && k + 3 < n_t, dma_v = k >= 1 && k + 2 < n_t;
-    int pidk[PPW], pidv[PPW];
-    auto dma = [&]() __attribute__((always_inline)) {
-      if (dma_k) issue(k + 3, 0, pidk);
-      if (dma_v) issue(k + 2, 1, pidv);
-    };
-    // one instantiation of each phase: the callbacks test the half at run time
-    auto dma_in_y = [&]() __attribute__((always_inline)) {
-      if (!first) dma();
-    };
-    auto dma_in_x = [&]() __attribute__((always_inline)) {
-      if (first) dma();
-    };
-    if (!first) {
-      if (dma_k) fetch(k + 3, pidk);
-      if (dma_v) fetch(k + 2, pidv);
-    }
-    if (k >= 1) {
-      if (wave_active)
-        Y(k - 1, dma_in_y);
-      else
-        dma_in_y();
+    const int kt = k + 2 + lead, vt = k + 1 + lead;  // tiles refilled in this Y phase
+    const DmaItem kit = resolve(kt, 0, kt < n_t, pid_k);
+    const DmaItem vit = resolve(vt, 1, vt < n_t, pid_v);
+    auto ystep = [&](int i) __attribute__((always_inline)) { issue_range(i == 0 ? kit : vit, 0, IPW); };
+    if (k >= 1 && wave_active) {
+      Y(k - 1, ystep);
+    } else {
+      ystep(0);
+      ystep(1);
     }
     if (first) wait_for(k);
     barrier_only();
-    if (first) {
-      if (dma_k) fetch(k + 3, pidk);
-      if (dma_v) fetch(k + 2, pidv);
-    }
-    if (wave_active && n_t > 0)
-      X(k, dma_in_x);
-    else
-      dma_in_x();
+    if (kt + 1 < n_t) fetch(kt + 1, pid_k);  // page ids for the next Y phase
+    if (vt + 1 < n_t) fetch(vt + 1, pid_v);
+    if (wave_active && n_t > 0) X(k);
     if (!first) wait_for(k + 1);
     barrier_only();
   }
