@@ -22,6 +22,8 @@
 //   pass 2  one workgroup per sequence: merge the chunk statistics, test
 //           u[i-1] < p_{i-1}(t_i) / q_i(t_i) node by node, then one
 //           inverse-CDF draw over max(0, p - q) (or p) with theta = u[N-1] * mass.
+//   Every exponential is fp64 (exp_fast, within a few ulp); the oracle's
+//   decisions are reproduced whenever their margins exceed ~1e-15.
 #include <math.h>
 
 #include "tv_internal.h"
@@ -163,10 +165,49 @@ __global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long lo
 
 // ---------------------------------------------------------------- stochastic
 
+// e^x in fp64 for the arguments the acceptance step forms (a scaled logit
+// minus a row maximum, so x <= 0). Cody-Waite reduction x = k ln2 + r with
+// |r| <= ln2 / 2, ln2 split into a head with 32 significant bits (so k * head
+// is exact for every k that occurs) and a tail; e^r from its Taylor series
+// to degree 13 (truncation below 2e-18 relative); scaling by 2^k. The result
+// is within a few ulp of e^x. Arguments below -745.2, -inf included, give 0.
+constexpr double kLog2eD = 1.4426950408889634;
+constexpr double kLn2Hi = 0.6931471803691238;
+constexpr double kLn2Lo = 1.9082149292705877e-10;
+
+__device__ inline double exp_fast(double x) {
+  if (!(x > -745.2)) return 0.0;
+  const double k = rint(x * kLog2eD);
+  double r = fma(-k, kLn2Hi, x);
+  r = fma(-k, kLn2Lo, r);
+  double p = 1.6059043836821613e-10;  // 1/13!
+  p = fma(p, r, 2.08767569878681e-09);
+  p = fma(p, r, 2.505210838544172e-08);
+  p = fma(p, r, 2.755731922398589e-07);
+  p = fma(p, r, 2.7557319223985893e-06);
+  p = fma(p, r, 2.48015873015873e-05);
+  p = fma(p, r, 0.0001984126984126984);
+  p = fma(p, r, 0.001388888888888889);
+  p = fma(p, r, 0.008333333333333333);
+  p = fma(p, r, 0.041666666666666664);
+  p = fma(p, r, 0.16666666666666666);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, static_cast<int>(k));
+}
+
+// x / T in fp64 from a precomputed 1/T and one FMA correction step (exact
+// when T = 1)
+__device__ inline double div_t(double x, double T, double invT) {
+  const double q = x * invT;
+  return fma(fma(-q, T, x), invT, q);
+}
+
 template <bool kVec>
 __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__restrict__ target,
                                                                  const float *__restrict__ draft, int N, int V,
-                                                                 int chunks, double T,
+                                                                 int chunks, double T, double invT,
                                                                  double *__restrict__ stats) {
   __shared__ double red[kThreads / 64];
   const int chunk = blockIdx.x;
@@ -185,42 +226,39 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
   const int x0 = chunk * kChunk;
   const int x1 = min(x0 + kChunk, V);
   constexpr int kPer = kChunk / kThreads;  // 32 values per thread, kept in registers
-  float vals[kPer];
-  int cnt = 0;
+  double z[kPer];
   if (kVec) {
 #pragma unroll
     for (int it = 0; it < kPer / 4; ++it) {
       const int x = x0 + (it * kThreads + threadIdx.x) * 4;
       float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       if (x < x1) v = *reinterpret_cast<const float4 *>(p + x);
-      vals[it * 4 + 0] = v.x;
-      vals[it * 4 + 1] = v.y;
-      vals[it * 4 + 2] = v.z;
-      vals[it * 4 + 3] = v.w;
+      z[it * 4 + 0] = div_t(v.x, T, invT);
+      z[it * 4 + 1] = div_t(v.y, T, invT);
+      z[it * 4 + 2] = div_t(v.z, T, invT);
+      z[it * 4 + 3] = div_t(v.w, T, invT);
     }
-    cnt = kPer;
   } else {
 #pragma unroll
     for (int it = 0; it < kPer; ++it) {
       const int x = x0 + it * kThreads + threadIdx.x;
-      vals[it] = x < x1 ? p[x] : -INFINITY;
+      z[it] = x < x1 ? div_t(p[x], T, invT) : -INFINITY;
     }
-    cnt = kPer;
   }
   double mx = -INFINITY;
-  for (int it = 0; it < cnt; ++it) mx = fmax(mx, static_cast<double>(vals[it]) / T);
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) mx = fmax(mx, z[it]);
   for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
   mx = red[0];
   for (int i = 1; i < kThreads / 64; ++i) mx = fmax(mx, red[i]);
   __syncthreads();
-  double z = 0.0;
-  for (int it = 0; it < cnt; ++it) {
-    if (vals[it] != -INFINITY) z += exp(static_cast<double>(vals[it]) / T - mx);
-  }
-  for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = z;
+  double zs = 0.0;
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) zs += exp_fast(z[it] - mx);  // -inf (padding) gives 0
+  for (int m = 32; m >= 1; m >>= 1) zs += __shfl_xor(zs, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = zs;
   __syncthreads();
   if (threadIdx.x == 0) {
     double tot = 0.0;
@@ -231,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
 }
 
 struct RowStat {
-  double m, Z;
+  double m, Z, invZ;
 };
 
 __device__ inline RowStat merge_stats(const double *stats, int64_t row, int which, int chunks) {
@@ -240,25 +278,31 @@ __device__ inline RowStat merge_stats(const double *stats, int64_t row, int whic
   for (int c = 0; c < chunks; ++c) M = fmax(M, s[2 * c]);
   double Z = 0.0;
   for (int c = 0; c < chunks; ++c) {
-    if (s[2 * c + 1] > 0.0) Z += s[2 * c + 1] * exp(s[2 * c] - M);
+    if (s[2 * c + 1] > 0.0) Z += s[2 * c + 1] * exp_fast(s[2 * c] - M);
   }
-  return RowStat{M, Z};
+  return RowStat{M, Z, 1.0 / Z};
 }
 
-__device__ inline double prob_at(const float *row, int x, double T, RowStat st) {
-  return exp(static_cast<double>(row[x]) / T - st.m) / st.Z;
+__device__ inline double prob_at(const float *row, int x, double T, double invT, const RowStat &st) {
+  return exp_fast(div_t(row[x], T, invT) - st.m) * st.invZ;
 }
 
-__global__ void __launch_bounds__(kThreads) stochastic_path_kernel(
+constexpr int kPathThreads = 1024;
+
+// One workgroup per sequence. Thread 0 validates the chain and runs the
+// accept tests; then the residual (or target) row is swept once by all
+// threads in contiguous token-order segments, the segment sums are scanned in
+// a fixed order, and only the segment whose running sum crosses theta is
+// swept again to find the drawn token.
+__global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
     const int32_t *__restrict__ parents, const float *__restrict__ uniforms, int B, int N, int V, int chunks,
-    double T, const double *__restrict__ stats, int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-    int32_t *__restrict__ bonus, unsigned long long *state) {
-  __shared__ int s_err, s_k, s_rej;
-  __shared__ double s_part[kThreads];
-  __shared__ int s_pick, s_lastpos;
+    double T, double invT, const double *__restrict__ stats, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ path, int32_t *__restrict__ bonus, unsigned long long *state) {
+  __shared__ int s_err, s_k, s_rej, s_pick, s_lastpos, s_cross;
+  __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t base = static_cast<int64_t>(b) * N;
   if (tid == 0) {
     int err = 0;
@@ -280,8 +324,8 @@ __global__ void __launch_bounds__(kThreads) stochastic_path_kernel(
         const int t = draft_tokens[base + i];
         const RowStat sp = merge_stats(stats, base + i - 1, 0, chunks);
         const RowStat sq = merge_stats(stats, base + i, 1, chunks);
-        const double pa = prob_at(target + (base + i - 1) * V, t, T, sp);
-        const double qa = prob_at(draft + (base + i) * V, t, T, sq);
+        const double pa = prob_at(target + (base + i - 1) * V, t, T, invT, sp);
+        const double qa = prob_at(draft + (base + i) * V, t, T, invT, sq);
         if (static_cast<double>(uniforms[base + i - 1]) < pa / qa) {
           ++k;
         } else {
@@ -294,6 +338,7 @@ __global__ void __launch_bounds__(kThreads) stochastic_path_kernel(
     }
     s_pick = 0x7FFFFFFF;
     s_lastpos = -1;
+    s_cross = 0x7FFFFFFF;
   }
   __syncthreads();
   if (s_err) {
@@ -302,7 +347,7 @@ __global__ void __launch_bounds__(kThreads) stochastic_path_kernel(
       accept_len[b] = -1;
       bonus[b] = -1;
     }
-    for (int i = tid; i < N; i += kThreads) path[base + i] = -1;
+    for (int i = tid; i < N; i += kPathThreads) path[base + i] = -1;
     return;
   }
   const int k = s_k, rej = s_rej;
@@ -310,45 +355,68 @@ __global__ void __launch_bounds__(kThreads) stochastic_path_kernel(
   const float *P = target + (base + prow) * V;
   const float *Q = rej > 0 ? draft + (base + rej) * V : nullptr;
   const RowStat sp = merge_stats(stats, base + prow, 0, chunks);
-  const RowStat sq = Q ? merge_stats(stats, base + rej, 1, chunks) : RowStat{0.0, 1.0};
+  const RowStat sq = Q ? merge_stats(stats, base + rej, 1, chunks) : RowStat{0.0, 1.0, 1.0};
   const double u = static_cast<double>(uniforms[base + N - 1]);
   // contiguous segment per thread, in token order
-  const int seg = (V + kThreads - 1) / kThreads;
+  const int seg = (V + kPathThreads - 1) / kPathThreads;
   const int x0 = min(tid * seg, V), x1 = min(x0 + seg, V);
   for (int pass = 0; pass < 2; ++pass) {
     const bool residual = Q != nullptr && pass == 0;
+    auto weight = [&](int x) {
+      double w = prob_at(P, x, T, invT, sp);
+      if (residual) w = fmax(0.0, w - prob_at(Q, x, T, invT, sq));
+      return w;
+    };
     double local = 0.0;
     int lastpos = -1;
     for (int x = x0; x < x1; ++x) {
-      double w = prob_at(P, x, T, sp);
-      if (residual) w = fmax(0.0, w - prob_at(Q, x, T, sq));
+      const double w = weight(x);
       local += w;
       if (w > 0.0) lastpos = x;
     }
-    s_part[tid] = local;
-    __syncthreads();
-    // exclusive prefix of the thread partials (sequential over threads, fixed order)
-    double prefix = 0.0, total = 0.0;
-    for (int i = 0; i < kThreads; ++i) {
-      if (i < tid) prefix += s_part[i];
-      total += s_part[i];
+    // exclusive prefix of the segment sums: a fixed-order scan within each
+    // wavefront, then over the wavefront totals in order
+    double incl = local;
+    for (int d = 1; d < 64; d <<= 1) {
+      const double t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
     }
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.0;
+    if (lane == 63) s_wave[wid] = incl;
+    __syncthreads();
+    if (tid == 0) {
+      double run = 0.0;
+      for (int i = 0; i < kPathThreads / 64; ++i) {
+        s_wpre[i] = run;
+        run += s_wave[i];
+      }
+      s_total = run;
+    }
+    __syncthreads();
+    const double prefix = s_wpre[wid] + excl;
+    const double total = s_total;
     if (residual && !(total > 0.0)) {
       __syncthreads();
       continue;  // no residual mass: draw from p instead
     }
     const double theta = u * total;
-    double run = prefix;
-    for (int x = x0; x < x1; ++x) {
-      double w = prob_at(P, x, T, sp);
-      if (residual) w = fmax(0.0, w - prob_at(Q, x, T, sq));
-      run += w;
-      if (run > theta) {
-        atomicMin(&s_pick, x);
-        break;
-      }
-    }
+    // the first segment whose running sum passes theta holds the draw
+    if (prefix + local > theta) atomicMin(&s_cross, tid);
     if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
+    __syncthreads();
+    if (tid == s_cross) {
+      double run = prefix;
+      int pick = lastpos;
+      for (int x = x0; x < x1; ++x) {
+        run += weight(x);
+        if (run > theta) {
+          pick = x;
+          break;
+        }
+      }
+      if (pick >= 0) s_pick = pick;
+    }
     __syncthreads();
     break;
   }
@@ -359,7 +427,7 @@ __global__ void __launch_bounds__(kThreads) stochastic_path_kernel(
     atomicAdd(state + 0, static_cast<unsigned long long>(k + 1));
     atomicAdd(state + 1, 1ull);
   }
-  for (int i = tid; i < N; i += kThreads) path[base + i] = i <= k ? i : -1;
+  for (int i = tid; i < N; i += kPathThreads) path[base + i] = i <= k ? i : -1;
 }
 
 }  // namespace
@@ -391,16 +459,17 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
     return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
   }
   auto *stats = static_cast<double *>(workspace);
+  const double T = static_cast<double>(temperature), invT = 1.0 / T;
   const dim3 g1(chunks, B * N, 2);
   if (vec)
     hipLaunchKernelGGL(softmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
-                       chunks, static_cast<double>(temperature), stats);
+                       chunks, T, invT, stats);
   else
     hipLaunchKernelGGL(softmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
-                       chunks, static_cast<double>(temperature), stats);
+                       chunks, T, invT, stats);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  hipLaunchKernelGGL(stochastic_path_kernel, dim3(B), blk, 0, ctx->stream, target_logits, draft_logits, draft_tokens,
-                     parents, uniforms, B, N, V, chunks, static_cast<double>(temperature), stats, accept_len, path,
+  hipLaunchKernelGGL(stochastic_path_kernel, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
+                     draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, accept_len, path,
                      bonus, ctx->d_state);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }

@@ -575,32 +575,60 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 }
 
 // Merges the S partial (m, l, o) triples of each row in a fixed split order.
+// One wavefront per row (four rows per workgroup); lane i owns D/64
+// consecutive d, so each partial row is one coalesced load.
 template <int D>
-__global__ void __launch_bounds__(D) attn_combine_kernel(AttnArgs a) {
-  const int bh = blockIdx.x / a.rows, row = blockIdx.x % a.rows, d = threadIdx.x;
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+  constexpr int E = D / 64;  // d values per lane
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= static_cast<int64_t>(a.B) * a.Hkv * a.rows) return;
+  const int bh = static_cast<int>(r / a.rows), row = static_cast<int>(r % a.rows);
   const int b = bh / a.Hkv, g = bh % a.Hkv;
+  const int64_t slot0 = static_cast<int64_t>(bh) * a.S * a.rows_pad + row;
   float M = -INFINITY;
   bool bad = false;
   for (int s = 0; s < a.S; ++s) {
-    const float ms = a.ws_ml[((static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row) * 2];
+    const float ms = a.ws_ml[(slot0 + static_cast<int64_t>(s) * a.rows_pad) * 2];
     bad |= isnan(ms);
     M = fmaxf(M, ms);
   }
-  float lsum = 0.f, acc = 0.f;
+  float lsum = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < a.S; ++s) {
-    const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
-    const float ms = a.ws_ml[slot * 2];
-    const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    lsum = fmaf(wgt, a.ws_ml[slot * 2 + 1], lsum);
-    acc = fmaf(wgt, a.ws_o[slot * D + d], acc);
+    const int64_t slot = slot0 + static_cast<int64_t>(s) * a.rows_pad;
+    const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + slot * 2);
+    const float wgt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+    lsum = fmaf(wgt, ml.y, lsum);
+    if (E == 2) {
+      const float2 o2 = *reinterpret_cast<const float2 *>(a.ws_o + slot * D + 2 * lane);
+      acc[0] = fmaf(wgt, o2.x, acc[0]);
+      acc[E - 1] = fmaf(wgt, o2.y, acc[E - 1]);
+    } else {
+      acc[0] = fmaf(wgt, a.ws_o[slot * D + lane], acc[0]);
+    }
   }
-  const float val = bad ? NAN : acc / lsum;
   const int i = row / a.G, h = g * a.G + row % a.G;
-  const int64_t idx = ((static_cast<int64_t>(b) * a.N + i) * a.Hq + h) * D + d;
-  if (a.out_bf16)
-    static_cast<uint16_t *>(a.out)[idx] = float_to_bf16_bits(val);
-  else
-    static_cast<float *>(a.out)[idx] = val;
+  const int64_t idx = ((static_cast<int64_t>(b) * a.N + i) * a.Hq + h) * D + E * lane;
+  const float inv = 1.f / lsum;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = bad ? NAN : acc[e] * inv;
+  if (a.out_bf16) {
+    uint16_t *o = static_cast<uint16_t *>(a.out) + idx;
+    if (E == 2)
+      *reinterpret_cast<uint32_t *>(o) = float_to_bf16_bits(v[0]) | (static_cast<uint32_t>(float_to_bf16_bits(v[E - 1])) << 16);
+    else
+      o[0] = float_to_bf16_bits(v[0]);
+  } else {
+    float *o = static_cast<float *>(a.out) + idx;
+    if (E == 2)
+      *reinterpret_cast<float2 *>(o) = make_float2(v[0], v[E - 1]);
+    else
+      o[0] = v[0];
+  }
 }
 
 constexpr int kStages = 4;
@@ -699,11 +727,11 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
     launch_dw<64>(plan.qb, flat, grid, block, ctx->stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
-    const dim3 cgrid(B * Hkv * a.rows);
+    const dim3 cgrid(static_cast<unsigned>((static_cast<int64_t>(B) * Hkv * a.rows + 3) / 4));
     if (D == 128)
-      hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(128), 0, ctx->stream, a);
+      hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, ctx->stream, a);
     else
-      hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(64), 0, ctx->stream, a);
+      hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, ctx->stream, a);
     if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   }
   return TV_OK;
