@@ -287,58 +287,67 @@ __device__ inline double prob_at(const float *row, int x, double T, double invT,
   return exp_fast(div_t(row[x], T, invT) - st.m) * st.invZ;
 }
 
-constexpr int kPathThreads = 1024;
+constexpr int kPathThreads = 512;
+constexpr int kBlk = 16;  // tokens per register block of the row sweep
 
-// One workgroup per sequence. Thread 0 validates the chain and runs the
-// accept tests; then the residual (or target) row is swept once by all
-// threads in contiguous token-order segments, the segment sums are scanned in
-// a fixed order, and only the segment whose running sum crosses theta is
-// swept again to find the drawn token.
+// One workgroup per sequence. Wavefront 0 validates the chain and runs the
+// accept tests with one lane per node; the first rejected node (or the end
+// of the chain) fixes the row of the final draw. That row - max(0, p - q)
+// after a rejection, p otherwise - is then swept once by all threads in
+// contiguous token-order segments (vector loads, 16 tokens per register
+// block), the segment sums are scanned in a fixed order, and only the
+// segment whose running sum passes theta is swept again, one token per lane
+// of one wavefront, to find the token.
+template <bool kVec>
 __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
     const int32_t *__restrict__ parents, const float *__restrict__ uniforms, int B, int N, int V, int chunks,
     double T, double invT, const double *__restrict__ stats, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ path, int32_t *__restrict__ bonus, unsigned long long *state) {
   __shared__ int s_err, s_k, s_rej, s_pick, s_lastpos, s_cross;
-  __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total;
+  __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total, s_cprefix;
+  __shared__ int s_cross_last;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t base = static_cast<int64_t>(b) * N;
-  if (tid == 0) {
-    int err = 0;
-    for (int i = 0; i < N && !err; ++i) {
-      const int p = parents[base + i];
-      if (p < -1 || p >= i || (i == 0 && p != -1)) err = TV_ERR_INVALID_TREE;
-    }
-    for (int i = 1; i < N && !err; ++i)
-      if (parents[base + i] != i - 1) err = TV_ERR_UNSUPPORTED;
-    for (int i = 1; i < N && !err; ++i) {
-      const int t = draft_tokens[base + i];
-      if (t < 0 || t >= V) err = TV_ERR_INVALID_ARG;
-    }
-    s_err = err;
-    if (!err) {
-      // sequential chain test: node i accepted iff u[i-1] < p_{i-1}(t_i) / q_i(t_i)
-      int k = 0, rej = -1;
-      for (int i = 1; i < N; ++i) {
-        const int t = draft_tokens[base + i];
-        const RowStat sp = merge_stats(stats, base + i - 1, 0, chunks);
-        const RowStat sq = merge_stats(stats, base + i, 1, chunks);
-        const double pa = prob_at(target + (base + i - 1) * V, t, T, invT, sp);
-        const double qa = prob_at(draft + (base + i) * V, t, T, invT, sq);
-        if (static_cast<double>(uniforms[base + i - 1]) < pa / qa) {
-          ++k;
-        } else {
-          rej = i;
-          break;
-        }
+  if (wid == 0) {
+    // validation with the same precedence as a serial check: a bad parent
+    // anywhere, then a non-chain tree, then a draft token outside [0, V)
+    bool tree_bad = false, nonchain = false, tok_bad = false;
+    if (lane < N) {
+      const int p = parents[base + lane];
+      tree_bad = p < -1 || p >= lane || (lane == 0 && p != -1);
+      nonchain = lane >= 1 && p != lane - 1;
+      if (lane >= 1) {
+        const int t = draft_tokens[base + lane];
+        tok_bad = t < 0 || t >= V;
       }
-      s_k = k;
-      s_rej = rej;
     }
-    s_pick = 0x7FFFFFFF;
-    s_lastpos = -1;
-    s_cross = 0x7FFFFFFF;
+    const int err = __builtin_amdgcn_ballot_w64(tree_bad)  ? TV_ERR_INVALID_TREE
+                    : __builtin_amdgcn_ballot_w64(nonchain) ? TV_ERR_UNSUPPORTED
+                    : __builtin_amdgcn_ballot_w64(tok_bad)  ? TV_ERR_INVALID_ARG
+                                                            : 0;
+    // chain test, one lane per node i >= 1: accepted iff
+    // u[i-1] < p_{i-1}(t_i) / q_i(t_i); the first rejection ends the chain
+    bool rejected = false;
+    if (!err && lane >= 1 && lane < N) {
+      const int t = draft_tokens[base + lane];
+      const RowStat sp = merge_stats(stats, base + lane - 1, 0, chunks);
+      const RowStat sq = merge_stats(stats, base + lane, 1, chunks);
+      const double pa = prob_at(target + (base + lane - 1) * V, t, T, invT, sp);
+      const double qa = prob_at(draft + (base + lane) * V, t, T, invT, sq);
+      rejected = !(static_cast<double>(uniforms[base + lane - 1]) < pa / qa);
+    }
+    const uint64_t rj = __builtin_amdgcn_ballot_w64(rejected);
+    if (lane == 0) {
+      s_err = err;
+      const int rej = rj ? __builtin_ctzll(rj) : -1;
+      s_rej = rej;
+      s_k = rej > 0 ? rej - 1 : N - 1;
+      s_pick = 0x7FFFFFFF;
+      s_lastpos = -1;
+      s_cross = 0x7FFFFFFF;
+    }
   }
   __syncthreads();
   if (s_err) {
@@ -357,22 +366,58 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   const RowStat sp = merge_stats(stats, base + prow, 0, chunks);
   const RowStat sq = Q ? merge_stats(stats, base + rej, 1, chunks) : RowStat{0.0, 1.0, 1.0};
   const double u = static_cast<double>(uniforms[base + N - 1]);
-  // contiguous segment per thread, in token order
-  const int seg = (V + kPathThreads - 1) / kPathThreads;
+  // contiguous segment per thread in token order, a multiple of 4 tokens
+  const int seg = ((V + 4 * kPathThreads - 1) / (4 * kPathThreads)) * 4;
   const int x0 = min(tid * seg, V), x1 = min(x0 + seg, V);
+  auto load_block = [&](const float *row, int xb, float (&v)[kBlk]) __attribute__((always_inline)) {
+    if (kVec) {  // V % 4 == 0 and xb % 4 == 0: a float4 is either all in [x0, x1) or all out
+#pragma unroll
+      for (int i = 0; i < kBlk / 4; ++i) {
+        const int x = xb + 4 * i;
+        float4 f = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (x < x1) f = *reinterpret_cast<const float4 *>(row + x);
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) v[i] = xb + i < x1 ? row[xb + i] : -INFINITY;
+    }
+  };
   for (int pass = 0; pass < 2; ++pass) {
     const bool residual = Q != nullptr && pass == 0;
-    auto weight = [&](int x) {
-      double w = prob_at(P, x, T, invT, sp);
-      if (residual) w = fmax(0.0, w - prob_at(Q, x, T, invT, sq));
+    auto weight = [&](float pl, float ql) __attribute__((always_inline)) {
+      double w = exp_fast(div_t(pl, T, invT) - sp.m) * sp.invZ;  // padding (-inf) gives 0
+      if (residual) w = fmax(0.0, w - exp_fast(div_t(ql, T, invT) - sq.m) * sq.invZ);
       return w;
     };
     double local = 0.0;
     int lastpos = -1;
-    for (int x = x0; x < x1; ++x) {
-      const double w = weight(x);
-      local += w;
-      if (w > 0.0) lastpos = x;
+    {
+      // register blocks of kBlk tokens; the next block's loads are issued
+      // before the current block's exponentials
+      float pv[kBlk], qv[kBlk], pn[kBlk], qn[kBlk];
+      load_block(P, x0, pv);
+      if (residual) load_block(Q, x0, qv);
+      for (int xb = x0; xb < x1; xb += kBlk) {
+        if (xb + kBlk < x1) {
+          load_block(P, xb + kBlk, pn);
+          if (residual) load_block(Q, xb + kBlk, qn);
+        }
+#pragma unroll
+        for (int i = 0; i < kBlk; ++i) {
+          const double w = weight(pv[i], residual ? qv[i] : 0.f);
+          local += w;
+          if (w > 0.0) lastpos = xb + i;
+        }
+#pragma unroll
+        for (int i = 0; i < kBlk; ++i) {
+          pv[i] = pn[i];
+          qv[i] = qn[i];
+        }
+      }
     }
     // exclusive prefix of the segment sums: a fixed-order scan within each
     // wavefront, then over the wavefront totals in order
@@ -406,16 +451,35 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
     __syncthreads();
     if (tid == s_cross) {
-      double run = prefix;
-      int pick = lastpos;
-      for (int x = x0; x < x1; ++x) {
-        run += weight(x);
-        if (run > theta) {
-          pick = x;
-          break;
+      s_cprefix = prefix;
+      s_cross_last = lastpos;
+    }
+    __syncthreads();
+    // wavefront 0 re-sweeps the crossing segment one token per lane: a
+    // fixed-order scan of the weights gives each token's running sum
+    const int cross = s_cross;
+    if (wid == 0 && cross != 0x7FFFFFFF) {
+      const int cx0 = min(cross * seg, V), cx1 = min(cx0 + seg, V);
+      double carry = s_cprefix;
+      int pick = -1;
+      for (int xb = cx0; xb < cx1 && pick < 0; xb += 64) {
+        const int x = xb + lane;
+        double w = 0.0;
+        if (x < cx1) {
+          w = exp_fast(div_t(P[x], T, invT) - sp.m) * sp.invZ;
+          if (residual) w = fmax(0.0, w - exp_fast(div_t(Q[x], T, invT) - sq.m) * sq.invZ);
         }
+        double run = w;
+        for (int d = 1; d < 64; d <<= 1) {
+          const double t = __shfl_up(run, d);
+          if (lane >= d) run += t;
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(x < cx1 && carry + run > theta);
+        if (hit) pick = xb + __builtin_ctzll(hit);
+        carry += __shfl(run, 63);
       }
-      if (pick >= 0) s_pick = pick;
+      const int pk = pick >= 0 ? pick : s_cross_last;  // rounding left no crossing: last positive token
+      if (lane == 0 && pk >= 0) s_pick = pk;
     }
     __syncthreads();
     break;
@@ -468,9 +532,14 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
     hipLaunchKernelGGL(softmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
                        chunks, T, invT, stats);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  hipLaunchKernelGGL(stochastic_path_kernel, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
-                     draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, accept_len, path,
-                     bonus, ctx->d_state);
+  if (vec)
+    hipLaunchKernelGGL(stochastic_path_kernel<true>, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
+                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, accept_len,
+                       path, bonus, ctx->d_state);
+  else
+    hipLaunchKernelGGL(stochastic_path_kernel<false>, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
+                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, accept_len,
+                       path, bonus, ctx->d_state);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
