@@ -142,7 +142,7 @@ __device__ inline uint32_t lds_addr_of(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
 }
 
-template <int D, int NW, int STAGES, bool FLAT>
+template <int D, int NW, int STAGES, bool FLAT, bool KSPLIT>
 __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 16;             // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;             // 32-wide d blocks of O^T
@@ -152,7 +152,9 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   constexpr int IPW = CPR / NW;          // K (and V) DMA instructions per wavefront per tile
   constexpr int DPW = 2 * IPW;           // DMA instructions per wavefront per tile
   constexpr int TILE_BYTES = kKeys * RB; // one K (or V) tile
-  constexpr int ROWS_WG = 32 * NW;
+  constexpr int ROWS_WG = KSPLIT ? 32 : 32 * NW;  // key split: every wavefront holds the same 32 rows
+  constexpr int WROW = KSPLIT ? 0 : 32;          // row offset between wavefronts
+  static_assert(!KSPLIT || NW == 2, "key split pairs two wavefronts");
   static_assert(IPW >= 1 && CPR % NW == 0, "workgroup too wide for the tile");
 
   // stage s: K tile at [s][0], V tile at [s][1]; rows are 2*D bytes with
@@ -183,8 +185,8 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   if (tid == 0) s_bad = 0;
 
   // ---- the wavefront's 32 query rows: B operands of S^T, kept in VGPRs
-  const int row = rg * ROWS_WG + w * 32 + n;
-  const bool wave_active = rg * ROWS_WG + w * 32 < a.rows;
+  const int row = rg * ROWS_WG + w * WROW + n;
+  const bool wave_active = rg * ROWS_WG + w * WROW < a.rows;
   const bool row_ok = row < a.rows;
   const int node = row_ok ? row / a.G : 0;
   const int head = g * a.G + (row_ok ? row % a.G : 0);
@@ -356,11 +358,11 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   // and the four O chains and the two S chains alternate, so no MFMA waits on
   // the one before it. For j == n the S products read a stale
   // stage; their result is never used.
-  auto X = [&](int j) __attribute__((always_inline)) {
-    const int ks = j % STAGES, vs = (j + STAGES - 1) % STAGES;
+  auto X = [&](int j, int jp) __attribute__((always_inline)) {
+    const int ks = j % STAGES, vs = (jp + STAGES) % STAGES;
     bf16x8 kf[3][2];
     __builtin_amdgcn_sched_barrier(0);
-    if (j > 0) {
+    if (jp >= 0) {
       bf16x4 vh[3][DB][2];
 #pragma unroll
       for (int f = 0; f < 2; ++f)
@@ -476,6 +478,33 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     }
   };
 
+  if constexpr (KSPLIT) {
+    // Key split (row groups of at most 32 rows): wavefront w takes tiles
+    // w, w + 2, w + 4, ... of the split with its own running max, sum and O,
+    // so both SIMDs of the workgroup compute. Iteration i holds tiles 2i and
+    // 2i+1; after its barrier it refills K for tiles 2i+2, 2i+3 (the stages
+    // of tiles 2i-2, 2i-1, read in iteration i-1) and V for tiles 2i, 2i+1
+    // (read by the PV products of iteration i+1), and each iteration waits
+    // for all of the previous one's DMA.
+    const int n_t = ntiles;
+    const int npairs = (n_t + 1) / 2;
+    auto noop = [](int) {};
+    if (n_t > 0) issue_now(0, 0);
+    if (n_t > 1) issue_now(1, 0);
+    for (int i = 0; i <= npairs; ++i) {
+      wait_vmcnt<0>();
+      barrier_only();
+      if (2 * i + 2 < n_t) issue_now(2 * i + 2, 0);
+      if (2 * i + 3 < n_t) issue_now(2 * i + 3, 0);
+      if (2 * i < n_t) issue_now(2 * i, 1);
+      if (2 * i + 1 < n_t) issue_now(2 * i + 1, 1);
+      const int j = 2 * i + w, jp = j - 2;
+      if (wave_active && (j < n_t || (jp >= 0 && jp < n_t))) {
+        X(j, jp);  // for j >= n only the PV products of tile jp matter
+        if (j < n_t) Y(j, noop);
+      }
+    }
+  } else {
   // Ping-pong tile loop. Wavefront w and w + NW/2 share a SIMD; the two
   // halves of the workgroup run the same code, a Y phase and an X phase per
   // tile with a barrier after each, but the second half starts one barrier
@@ -534,15 +563,43 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     barrier_only();
     if (kt + 1 < n_t) fetch(kt + 1, pid_k);  // page ids for the next Y phase
     if (vt + 1 < n_t) fetch(vt + 1, pid_v);
-    if (wave_active && n_t > 0) X(k);
+    if (wave_active && n_t > 0) X(k, k - 1);
     if (!first) wait_for(k + 1);
     barrier_only();
   }
   if (first) barrier_only();
+  }
   if (load_bad) s_bad = 1;
   __syncthreads();
   const bool bad = bad_len || s_bad;
   if (bad && tid == 0) raise_error(a.state, TV_ERR_INVALID_ARG);
+  if constexpr (KSPLIT) {
+    // merge wavefront 1's (m, l, O) into wavefront 0's through LDS (the tile
+    // ring is idle now: every DMA was waited for and every read is done)
+    float *xch = reinterpret_cast<float *>(&smem[0][0][0]);
+    if (w == 1 && wave_active) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xch[(db * 16 + e) * 64 + lane] = o[db][e];
+      xch[DB * 16 * 64 + lane] = m_ref;
+      xch[(DB * 16 + 1) * 64 + lane] = l;
+    }
+    __syncthreads();
+    if (w == 1) return;
+    if (wave_active) {
+      const float m1 = xch[DB * 16 * 64 + lane], l1 = xch[(DB * 16 + 1) * 64 + lane];
+      const float mm = fmaxf(m_ref, m1);
+      const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] = o[db][e] * a0 + xch[(db * 16 + e) * 64 + lane] * a1;
+      l = l * a0 + l1 * a1;
+      m_ref = mm;
+    }
+  }
   if (!wave_active) return;
 
   const float l_tot = swap_halves_sum(l);
@@ -634,21 +691,23 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
 constexpr int kStages = 4;
 
 template <int D, bool FLAT>
-void launch_w(int qb, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
-  if (qb == 8)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 8, kStages, FLAT>), grid, block, 0, st, a);
+void launch_w(int qb, bool ksplit, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
+  if (ksplit)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT, true>), grid, block, 0, st, a);
+  else if (qb == 8)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 8, kStages, FLAT, false>), grid, block, 0, st, a);
   else if (qb == 4)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 4, kStages, FLAT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 4, kStages, FLAT, false>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT, false>), grid, block, 0, st, a);
 }
 
 template <int D>
-void launch_dw(int qb, bool flat, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
+void launch_dw(int qb, bool ksplit, bool flat, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
   if (flat)
-    launch_w<D, true>(qb, grid, block, st, a);
+    launch_w<D, true>(qb, ksplit, grid, block, st, a);
   else
-    launch_w<D, false>(qb, grid, block, st, a);
+    launch_w<D, false>(qb, ksplit, grid, block, st, a);
 }
 
 }  // namespace
@@ -659,7 +718,9 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
   const int rows = G * N;
   // 32 query rows per wavefront; 8, 4 or 2 wavefronts per workgroup
   p.qb = rows > 128 ? 8 : (rows > 64 ? 4 : 2);
-  p.row_block = 32 * p.qb;
+  // up to 32 rows: two wavefronts share the rows and split the tiles
+  p.ksplit = rows <= 32 ? 1 : 0;
+  p.row_block = p.ksplit ? 32 : 32 * p.qb;
   p.row_blocks = (rows + p.row_block - 1) / p.row_block;
   const int tiles = (max_prefix_len + N + kKeys - 1) / kKeys;
   const int64_t base = static_cast<int64_t>(B) * Hkv * p.row_blocks;
@@ -722,9 +783,9 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   // then fit the 32-bit VGPR offset with room for the out-of-range marker)
   const bool flat = num_pages * static_cast<int64_t>(Hkv) * kPage * D * 2 <= 0x7FFF0000LL;
   if (D == 128)
-    launch_dw<128>(plan.qb, flat, grid, block, ctx->stream, a);
+    launch_dw<128>(plan.qb, plan.ksplit, flat, grid, block, ctx->stream, a);
   else
-    launch_dw<64>(plan.qb, flat, grid, block, ctx->stream, a);
+    launch_dw<64>(plan.qb, plan.ksplit, flat, grid, block, ctx->stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
     const dim3 cgrid(static_cast<unsigned>((static_cast<int64_t>(B) * Hkv * a.rows + 3) / 4));

@@ -61,6 +61,7 @@ struct AttnPlan {
   int S;            // key splits per (sequence, KV head, row block)
   int chunk_tiles;  // 64-key tiles per split
   int qb;           // wavefronts per workgroup (32 query rows each): 2, 4 or 8
+  int ksplit;       // 1: two wavefronts share one 32-row block and split its tiles
   int row_block;    // query rows (node, head-in-group) per workgroup
   int row_blocks;   // ceil(G*N / row_block)
   size_t ws_bytes;  // fp32 partials + (m, l)
