@@ -189,11 +189,15 @@ def main():
     if tv.tv_device_error(dev) != 0:
         raise RuntimeError("device error during warm-up")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # per-call HIP events on every EVENT_EVERY-th step only: each event record
+    # costs the stream a few microseconds, which would otherwise inflate the
+    # step time that `value` is computed from
+    EVENT_EVERY = 8
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(0, args.steps, EVENT_EVERY)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k // EVENT_EVERY] if k % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tau, cycles = tv.tv_tau(dev)
@@ -236,12 +240,31 @@ def main():
                      "traffic": measured_traffic(dom, args.config),
                      "algorithmic_bytes": dk["bytes"],
                      "note": "achieved = algorithmic bytes per call / mean call duration (HIP events on the "
-                             "launch stream over the timed steps); traffic = calibrated rocprofv3 "
+                             "launch stream around every 8th timed step); traffic = calibrated rocprofv3 "
                              "FETCH_SIZE + WRITE_SIZE bytes per call, null when not measured for this source"},
         "kernels": kernels,
         "tau": tau,
         "tau_cycles": cycles,
     }
+    # tree-mask cost: tv_attention with the tree mask against the same call
+    # with tree_mask = NULL (every tree key visible), interleaved in blocks of
+    # 20 calls so that clock drift affects both alike; medians of 5 blocks
+    def attn_block(m):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, m, float(w.sm_scale), out=out,
+                            workspace=attn_ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 20 * 1e3
+    masked, unmasked = [], []
+    for _ in range(5):
+        masked.append(attn_block(mask))
+        unmasked.append(attn_block(None))
+    t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
+    result["mask_overhead"] = {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
+                               "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -64,6 +64,14 @@ def test_greedy_odd_vocab_and_nan():
     greedy_compare(w, "odd-V-nan")
 
 
+def test_greedy_large_batch():
+    # 70000 sequences of three nodes over a tiny vocabulary: grid dimensions
+    # beyond 65536 rows and many path-pass workgroups
+    w = tvgen.make_workload(1, seed=77, with_kv=False, overrides=dict(B=70000, N=3, V=8, max_depth=2))
+    tvgen.plant_random(w, 0.7, seed=3)
+    greedy_compare(w, "B70000")
+
+
 def test_greedy_forest_nodes_never_accepted():
     w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=8, N=12, tree="forest", V=64))
     w.parents[:, 0] = -1

@@ -60,12 +60,25 @@ __global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__r
   const int x1 = min(x0 + kChunk, V);
   unsigned long long best = 0ull;
   if (kVec) {
-    for (int x = x0 + threadIdx.x * 4; x < x1; x += kThreads * 4) {
-      const float4 v = *reinterpret_cast<const float4 *>(p + x);
-      best = umax64(best, pack_key(v.x, x));
-      best = umax64(best, pack_key(v.y, x + 1));
-      best = umax64(best, pack_key(v.z, x + 2));
-      best = umax64(best, pack_key(v.w, x + 3));
+    // all of the thread's 16-byte loads are issued before any is used
+    // (streaming loads: each logit is read once)
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kIt = kChunk / (kThreads * 4);
+    f32x4 v[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int x = x0 + (it * kThreads + threadIdx.x) * 4;
+      if (x < x1) v[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + x));
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int x = x0 + (it * kThreads + threadIdx.x) * 4;
+      if (x < x1) {
+        best = umax64(best, pack_key(v[it][0], x));
+        best = umax64(best, pack_key(v[it][1], x + 1));
+        best = umax64(best, pack_key(v[it][2], x + 2));
+        best = umax64(best, pack_key(v[it][3], x + 3));
+      }
     }
   } else {
     for (int x = x0 + threadIdx.x; x < x1; x += kThreads) best = umax64(best, pack_key(p[x], x));
