@@ -22,8 +22,8 @@
 //   pass 2  one workgroup per sequence: merge the chunk statistics, test
 //           u[i-1] < p_{i-1}(t_i) / q_i(t_i) node by node, then one
 //           inverse-CDF draw over max(0, p - q) (or p) with theta = u[N-1] * mass.
-//   Every exponential is fp64 (exp_fast, within a few ulp); the oracle's
-//   decisions are reproduced whenever their margins exceed ~1e-15.
+//   Every exponential is fp64 (exp_fast, within a few ulp), so a decision
+//   agrees with exact arithmetic whenever its margin exceeds ~1e-15.
 #include <math.h>
 
 #include "tv_internal.h"
