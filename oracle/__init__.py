@@ -46,9 +46,10 @@ def _load():
                                       vp, c_int]
         lib.tvo_accept_greedy.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, c_int]
         lib.tvo_accept_stochastic.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, c_int]
+        lib.tvo_commit.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         lib.tvo_tau.argtypes = [vp, i64]
         lib.tvo_tau.restype = ctypes.c_double
-        for f in ("tvo_build_mask", "tvo_attention", "tvo_accept_greedy", "tvo_accept_stochastic"):
+        for f in ("tvo_build_mask", "tvo_attention", "tvo_accept_greedy", "tvo_accept_stochastic", "tvo_commit"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -175,3 +176,43 @@ def accept_stochastic(target_logits, draft_logits, draft_tokens, parents, unifor
 def tau(accept_lens) -> float:
     a = _c(np.asarray(accept_lens).reshape(-1), np.int32)
     return _load().tvo_tau(_p(a), a.size)
+
+
+def status_commit(k_pages, v_pages, page_table, prefix_lens, draft_tokens, path, accept_len, bonus, *, B, N, Hkv,
+                  D, num_pages=None, maxp=None, max_prefix_len=None, with_emitted=True):
+    """Accepted-path commit on copies of k_pages / v_pages.
+
+    Returns (status, k_new, v_new, dict(new_prefix_lens, emitted, next_root)).
+    """
+    k = np.array(k_pages, dtype=np.uint16, order="C", copy=True)
+    v = np.array(v_pages, dtype=np.uint16, order="C", copy=True)
+    page_table = _c(page_table, np.int32)
+    prefix_lens = _c(prefix_lens, np.int32)
+    draft_tokens = _c(draft_tokens, np.int32)
+    path = _c(path, np.int32)
+    accept_len = _c(accept_len, np.int32)
+    bonus = _c(bonus, np.int32)
+    if num_pages is None:
+        num_pages = k.shape[0]
+    if maxp is None:
+        maxp = page_table.shape[1]
+    if max_prefix_len is None:
+        max_prefix_len = int(prefix_lens.max()) if prefix_lens.size else 0
+    new_lens = np.full(max(B, 0), -2, np.int32)
+    emitted = np.full((max(B, 0), max(N, 0)), -2, np.int32) if with_emitted else None
+    next_root = np.full(max(B, 0), -2, np.int32)
+    st = _load().tvo_commit(_p(k), _p(v), num_pages, _p(page_table), maxp, _p(prefix_lens), max_prefix_len,
+                            _p(draft_tokens), _p(path), _p(accept_len), _p(bonus), B, N, Hkv, D, _p(new_lens),
+                            _p(emitted), _p(next_root))
+    return st, k, v, dict(new_prefix_lens=new_lens, emitted=emitted, next_root=next_root)
+
+
+def commit(w, path, accept_len, bonus):
+    """Commit the accepted paths of workload `w` (see tvgen.Workload) on copies
+    of its pages. Returns (k_new, v_new, dict(new_prefix_lens, emitted, next_root))."""
+    st, k, v, r = status_commit(w.k_pages, w.v_pages, w.page_table, w.prefix_lens, w.draft_tokens, path,
+                                accept_len, bonus, B=w.B, N=w.N, Hkv=w.Hkv, D=w.D, num_pages=w.num_pages,
+                                max_prefix_len=w.max_prefix_len)
+    if st != OK:
+        raise OracleError(st, "commit")
+    return k, v, r

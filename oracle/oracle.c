@@ -552,3 +552,85 @@ double tvo_tau(const int32_t *accept_len, int64_t M) {
   for (int64_t j = 0; j < M; ++j) sum += accept_len[j];
   return (double)sum / (double)M;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Accepted-path KV commit and next-input insertion.                        */
+/*                                                                          */
+/* [EAGLE-2 page], third pillar: rejected drafts must not pollute the       */
+/* target's KV cache. [Sonar page], MTP schedule: after acceptance the      */
+/* target's input is shifted and the next token is inserted on the device, */
+/* avoiding a CPU-GPU sync on the accepted length. Readings:                */
+/*  - committed position L+m (m = 0..len-1) receives the K/V that node v_m  */
+/*    of the accepted path (v_0 = 0 < v_1 < ...) holds at L+v_m, for every  */
+/*    KV head; everything is read before anything is written;              */
+/*  - the new prefix length is L + len (the root and the accepted drafts);  */
+/*  - emitted tokens: draft_tokens[v_1..v_{len-1}], then the bonus, -1 pad; */
+/*  - the next root token (the next tree's node 0) is the bonus.            */
+/* A sequence whose prefix length, path, bonus or touched pages are invalid */
+/* is left unchanged (new length L, next root -1, emitted all -1) and the   */
+/* call reports TVO_ERR_INVALID_ARG.                                        */
+/* ------------------------------------------------------------------------ */
+
+int tvo_commit(uint16_t *k_pages, uint16_t *v_pages, int64_t num_pages, const int32_t *page_table, int32_t maxp,
+               const int32_t *prefix_lens, int32_t max_prefix_len, const int32_t *draft_tokens,
+               const int32_t *path, const int32_t *accept_len, const int32_t *bonus, int32_t B, int32_t N,
+               int32_t Hkv, int32_t D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root) {
+  if (B < 0 || N < 1 || N > 64 || Hkv <= 0 || (D != 64 && D != 128) || maxp < 0 || max_prefix_len < 0 ||
+      num_pages < 0)
+    return TVO_ERR_INVALID_ARG;
+  if (B == 0) return TVO_OK;
+  if (!k_pages || !v_pages || !page_table || !prefix_lens || !draft_tokens || !path || !accept_len || !bonus ||
+      !new_prefix_lens || !next_root)
+    return TVO_ERR_INVALID_ARG;
+  int status = TVO_OK;
+  uint16_t *tmp = (uint16_t *)malloc(sizeof(uint16_t) * 2 * (size_t)N * (size_t)D);
+  if (!tmp) return TVO_ERR_RUNTIME;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t L = prefix_lens[b];
+    const int32_t len = accept_len[b];
+    const int32_t *pth = path + (int64_t)b * N;
+    int ok = L >= 0 && L <= max_prefix_len && (int64_t)L + N <= (int64_t)maxp * 16 && len >= 1 && len <= N &&
+             pth[0] == 0 && bonus[b] >= 0;
+    for (int32_t m = 1; ok && m < len; ++m) ok = pth[m] > pth[m - 1] && pth[m] < N;
+    /* every page the moves touch must exist */
+    for (int32_t m = 0; ok && m < len; ++m) {
+      const int64_t ts[2] = {(int64_t)L + pth[m], (int64_t)L + m};
+      for (int u = 0; u < 2; ++u) {
+        const int32_t pid = page_table[(int64_t)b * maxp + ts[u] / 16];
+        if (pid < 0 || pid >= num_pages) ok = 0;
+      }
+    }
+    if (!ok) {
+      status = TVO_ERR_INVALID_ARG;
+      new_prefix_lens[b] = L;
+      next_root[b] = -1;
+      if (emitted)
+        for (int32_t m = 0; m < N; ++m) emitted[(int64_t)b * N + m] = -1;
+      continue;
+    }
+    for (int32_t g = 0; g < Hkv; ++g) {
+      /* gather the accepted rows first, then write them to their new places */
+      for (int32_t m = 1; m < len; ++m) {
+        const int64_t t = (int64_t)L + pth[m];
+        const int64_t row = (((int64_t)page_table[(int64_t)b * maxp + t / 16] * Hkv + g) * 16 + t % 16) * D;
+        memcpy(tmp + (2 * (size_t)m) * D, k_pages + row, sizeof(uint16_t) * D);
+        memcpy(tmp + (2 * (size_t)m + 1) * D, v_pages + row, sizeof(uint16_t) * D);
+      }
+      for (int32_t m = 1; m < len; ++m) {
+        const int64_t t = (int64_t)L + m;
+        const int64_t row = (((int64_t)page_table[(int64_t)b * maxp + t / 16] * Hkv + g) * 16 + t % 16) * D;
+        memcpy(k_pages + row, tmp + (2 * (size_t)m) * D, sizeof(uint16_t) * D);
+        memcpy(v_pages + row, tmp + (2 * (size_t)m + 1) * D, sizeof(uint16_t) * D);
+      }
+    }
+    new_prefix_lens[b] = L + len;
+    next_root[b] = bonus[b];
+    if (emitted) {
+      for (int32_t m = 0; m < N; ++m) emitted[(int64_t)b * N + m] = -1;
+      for (int32_t m = 1; m < len; ++m) emitted[(int64_t)b * N + m - 1] = draft_tokens[(int64_t)b * N + pth[m]];
+      emitted[(int64_t)b * N + len - 1] = bonus[b];
+    }
+  }
+  free(tmp);
+  return status;
+}

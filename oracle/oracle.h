@@ -60,6 +60,18 @@ int tvo_accept_stochastic(const float *target_logits, const float *draft_logits,
                           float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus, double *margins,
                           int nthreads);
 
+/* Accepted-path KV commit (EAGLE-2 page, third pillar: no KV-cache pollution;
+ * Sonar page, MTP schedule: next token inserted on the device). Committed
+ * position L+m receives the K/V of path node v_m (all KV heads, read before
+ * written); new_prefix_lens[b] = L + len; emitted [B][N] (nullable) =
+ * draft_tokens at v_1..v_{len-1}, then the bonus, -1 padded; next_root[b] =
+ * bonus. k_pages and v_pages are updated in place. Bad sequences are left
+ * unchanged (length L, root -1, emitted -1) and make the call return 1. */
+int tvo_commit(uint16_t *k_pages, uint16_t *v_pages, int64_t num_pages, const int32_t *page_table, int32_t maxp,
+               const int32_t *prefix_lens, int32_t max_prefix_len, const int32_t *draft_tokens,
+               const int32_t *path, const int32_t *accept_len, const int32_t *bonus, int32_t B, int32_t N,
+               int32_t Hkv, int32_t D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root);
+
 /* tau = (1/M) sum_j n_accepted(j) over M verification cycles (EAGLE-3 page,
  * tree acceptance rate definition); 0 when M = 0. */
 double tvo_tau(const int32_t *accept_len, int64_t M);
