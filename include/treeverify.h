@@ -154,6 +154,39 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
                     tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus_token,
                     int32_t *target_argmax, void *workspace, size_t workspace_bytes);
 
+/* Accepted-path KV commit and next-input insertion ([EAGLE-2 page], third
+ * pillar: only the accepted path may stay in the target's KV cache;
+ * [Sonar page], MTP schedule: the next target input is inserted by a kernel
+ * after the input shift, so the host never waits for the accepted length).
+ * For sequence b with L = prefix_lens[b] and n = accept_len[b]:
+ *   - for m in [1, n) and every KV head, the K and V rows at position
+ *     L + path[b][m] are moved to position L + m (all rows are read before
+ *     any is written; rows with path[b][m] == m stay put; positions
+ *     L+n..L+N-1 keep stale data, outside the new prefix);
+ *   - new_prefix_lens[b] = L + n (root and accepted drafts are now prefix);
+ *   - emitted[b] = draft_tokens[b][path[b][1..n-1]], then bonus_token[b],
+ *     padded with -1 (the tokens this cycle produced);
+ *   - next_root[b] = bonus_token[b] (node 0 of the next tree).
+ *   k_pages, v_pages  bf16 [num_pages][Hkv][16][D], updated in place
+ *   page_table, prefix_lens, max_prefix_len, maxp: as for tv_attention
+ *   draft_tokens      int32 [B][N]
+ *   path, accept_len, bonus_token: as written by tv_accept; path[b][0] = 0
+ *                     and path[b][0..n) strictly increasing below N
+ *                     (parents are not re-checked)
+ *   new_prefix_lens, next_root  int32 [B]; emitted int32 [B][N] or NULL
+ * The outputs must not overlap any input; pages holding positions
+ * L..L+N-1 of one sequence must belong to that sequence alone (sequences are
+ * committed concurrently). A sequence with L outside [0, max_prefix_len],
+ * n outside [1, N], a bad path, a negative bonus or a page id outside
+ * [0, num_pages) at a touched position is left unchanged (new length L,
+ * next root -1, emitted -1) and sets the sticky TV_ERR_INVALID_ARG.
+ * Requires D in {64, 128}, 1 <= N <= 64 when B > 0, maxp * 16 >=
+ * max_prefix_len + N. */
+tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages, const int32_t *page_table,
+                    int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len, const int32_t *draft_tokens,
+                    const int32_t *path, const int32_t *accept_len, const int32_t *bonus_token, int32_t B, int32_t N,
+                    int32_t Hkv, int32_t D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root);
+
 /* tau = (sum of accept_len) / (number of sequences verified) since the last
  * reset ([EAGLE-3 page], tree acceptance rate); 0 when no cycle was counted.
  * tau and cycles are host pointers (cycles may be NULL). Synchronises. */

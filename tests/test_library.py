@@ -20,7 +20,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = tv.library()
     names = declared_functions()
-    assert {"tv_create", "tv_build_mask", "tv_attention", "tv_accept", "tv_tau"} <= names
+    assert {"tv_create", "tv_build_mask", "tv_attention", "tv_accept", "tv_commit", "tv_tau"} <= names
     missing = [n for n in sorted(names) if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -37,6 +37,8 @@ def test_status_strings_and_host_queries():
     # a NULL context is rejected before anything touches a device
     assert lib.tv_build_mask(None, None, 1, 1, None, None) == tv.INVALID_ARG
     assert lib.tv_tau_reset(None) == tv.INVALID_ARG
+    assert lib.tv_commit(None, None, None, 0, None, 0, None, 0, None, None, None, None, 1, 4, 1, 128, None, None,
+                         None) == tv.INVALID_ARG
 
 
 def test_product_path_never_loads_the_oracle():

@@ -57,13 +57,14 @@ def _load():
         lib.tv_accept_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
         lib.tv_accept_workspace_bytes.restype = sz
         lib.tv_accept.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, f32, vp, vp, vp, vp, vp, sz]
+        lib.tv_commit.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         lib.tv_tau.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]
         lib.tv_tau_reset.argtypes = [vp]
         lib.tv_device_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
         lib.tv_status_string.argtypes = [ctypes.c_int]
         lib.tv_status_string.restype = ctypes.c_char_p
-        for f in ("tv_create", "tv_destroy", "tv_set_stream", "tv_build_mask", "tv_attention", "tv_accept", "tv_tau",
-                  "tv_tau_reset", "tv_device_error"):
+        for f in ("tv_create", "tv_destroy", "tv_set_stream", "tv_build_mask", "tv_attention", "tv_accept",
+                  "tv_commit", "tv_tau", "tv_tau_reset", "tv_device_error"):
             getattr(lib, f).restype = st
         _lib = lib
     return _lib
@@ -174,6 +175,32 @@ def tv_accept(target_logits: torch.Tensor, draft_tokens: torch.Tensor, parents: 
                              _ptr(uniforms), B, N, V, mode, float(temperature), _ptr(outputs["accept_len"]),
                              _ptr(outputs["path"]), _ptr(outputs["bonus"]), _ptr(outputs.get("target_argmax")),
                              _ptr(workspace), ws_bytes), "tv_accept")
+    return outputs
+
+
+def tv_commit(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor, prefix_lens: torch.Tensor,
+              max_prefix_len: int, draft_tokens: torch.Tensor, path: torch.Tensor, accept_len: torch.Tensor,
+              bonus: torch.Tensor, outputs: Optional[dict] = None, want_emitted: bool = True) -> dict:
+    """Moves the accepted path's K/V rows in place (k/v_pages bf16 [P][Hkv][16][D]).
+
+    Returns dict(new_prefix_lens [B], emitted [B][N] (if wanted), next_root [B]);
+    outputs must not overlap any input."""
+    B, N = draft_tokens.shape
+    P, Hkv, page, D = k_pages.shape
+    assert page == 16 and v_pages.shape == k_pages.shape
+    assert k_pages.dtype == torch.bfloat16 and v_pages.dtype == torch.bfloat16
+    for t in (page_table, prefix_lens, draft_tokens, path, accept_len, bonus):
+        assert t.dtype == torch.int32
+    dev = k_pages.device
+    if outputs is None:
+        outputs = dict(new_prefix_lens=torch.empty(B, dtype=torch.int32, device=dev),
+                       next_root=torch.empty(B, dtype=torch.int32, device=dev))
+        if want_emitted:
+            outputs["emitted"] = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _check(_load().tv_commit(_ctx(dev), _ptr(k_pages), _ptr(v_pages), P, _ptr(page_table), page_table.shape[1],
+                             _ptr(prefix_lens), int(max_prefix_len), _ptr(draft_tokens), _ptr(path),
+                             _ptr(accept_len), _ptr(bonus), B, N, Hkv, D, _ptr(outputs["new_prefix_lens"]),
+                             _ptr(outputs.get("emitted")), _ptr(outputs["next_root"])), "tv_commit")
     return outputs
 
 

@@ -123,6 +123,24 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
                        accept_len, path, bonus_token, mode == TV_GREEDY ? target_argmax : nullptr, workspace);
 }
 
+tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages, const int32_t *page_table,
+                    int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len, const int32_t *draft_tokens,
+                    const int32_t *path, const int32_t *accept_len, const int32_t *bonus_token, int32_t B, int32_t N,
+                    int32_t Hkv, int32_t D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root) {
+  if (!ctx || B < 0 || Hkv <= 0 || num_pages < 0 || maxp < 0 || max_prefix_len < 0) return TV_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (B == 0) return TV_OK;
+  if (N < 1) return TV_ERR_INVALID_ARG;
+  if (N > 64) return TV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * Hkv > 0x7FFFFFFF) return TV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(maxp) * kPage < static_cast<int64_t>(max_prefix_len) + N) return TV_ERR_INVALID_ARG;
+  if (!k_pages || !v_pages || !page_table || !prefix_lens || !draft_tokens || !path || !accept_len || !bonus_token ||
+      !new_prefix_lens || !next_root)
+    return TV_ERR_INVALID_ARG;
+  return launch_commit(ctx, k_pages, v_pages, num_pages, page_table, maxp, prefix_lens, max_prefix_len, draft_tokens,
+                       path, accept_len, bonus_token, B, N, Hkv, D, new_prefix_lens, emitted, next_root);
+}
+
 tv_status tv_tau(tv_ctx *ctx, double *tau, uint64_t *cycles) {
   if (!ctx || !tau) return TV_ERR_INVALID_ARG;
   unsigned long long h[2] = {0, 0};

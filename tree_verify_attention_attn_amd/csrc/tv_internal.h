@@ -78,6 +78,11 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
                         int V, tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path,
                         int32_t *bonus, int32_t *target_argmax, void *workspace);
 
+tv_status launch_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages, const int32_t *page_table,
+                        int maxp, const int32_t *prefix_lens, int max_prefix_len, const int32_t *draft_tokens,
+                        const int32_t *path, const int32_t *accept_len, const int32_t *bonus, int B, int N, int Hkv,
+                        int D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root);
+
 tv_status launch_clear_state(tv_ctx *ctx, int first_word, int n_words);
 
 }  // namespace tv
