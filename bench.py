@@ -75,7 +75,8 @@ KERNEL_SOURCES = {"tv_attention": "attention.hip", "tv_accept": "accept.hip", "t
 CALL_KERNELS = {"tv_attention": "attn_mfma_kernel (+ attn_combine_kernel when the keys are split)",
                 "tv_accept": "argmax_chunk_kernel + greedy_path_kernel (greedy) or softmax_chunk_kernel + "
                              "stochastic_path_kernel (stochastic)",
-                "tv_build_mask": "build_mask_kernel"}
+                "tv_build_mask": "build_mask_kernel",
+                "tv_commit": "commit_kernel"}
 
 
 def measured_traffic(call, cfg):
@@ -126,6 +127,79 @@ def cpu_baseline(w, depth, target_s, threads):
     return dict(value=done * w.N / elapsed, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{done} of {w.B} sequences ({done * w.N} tree tokens, {done * w.N * w.Hq} attention rows "
                        f"+ acceptance), {elapsed:.1f} s wall, fp64 C oracle, {threads} threads")
+
+
+def commit_moves(w, path, lens):
+    """Rows (per KV head) a commit moves: path entries after the identity run."""
+    rows = 0
+    for b in range(w.B):
+        p = path[b, :lens[b]]
+        rows += int((p != np.arange(len(p))).sum())
+    return rows
+
+
+def commit_bytes(w, path, lens):
+    """Algorithmic bytes of one tv_commit: every moved K and V row read and
+    written once, plus per-sequence metadata (prefix length, accepted length,
+    bonus, the accepted path, two page-table entries per path node) read and
+    the outputs (new length, next root, emitted row) written."""
+    kv = commit_moves(w, path, lens) * w.Hkv * w.D * 2 * 2 * 2
+    n = int(np.sum(lens))
+    return kv + w.B * 12 + n * 4 * 3 + w.B * (w.N + 2) * 4
+
+
+def commit_timing(tv, torch, dev, w, depth, d, kp, vp, table, plens, tokens, outs):
+    """Times tv_commit (after acceptance; it rewrites the pools, so it runs
+    after every other GPU measurement) on two sets of paths: the last timed
+    step's own acceptance, and each sequence's deepest root-to-leaf path (the
+    most rows its tree can move)."""
+    deep_path = np.full((w.B, w.N), -1, np.int32)
+    deep_len = np.zeros(w.B, np.int32)
+    for b in range(w.B):
+        c, p = int(np.argmax(depth[b])), []
+        while c >= 0:
+            p.append(c)
+            c = int(w.parents[b, c])
+        deep_path[b, :len(p)] = p[::-1]
+        deep_len[b] = len(p)
+    bonus = d(np.arange(w.B, dtype=np.int32))
+    co = dict(new_prefix_lens=torch.empty(w.B, dtype=torch.int32, device=dev),
+              next_root=torch.empty(w.B, dtype=torch.int32, device=dev),
+              emitted=torch.empty((w.B, w.N), dtype=torch.int32, device=dev))
+    step_path, step_len = outs["path"].cpu().numpy(), outs["accept_len"].cpu().numpy()
+    res = {}
+    for name, pth, ln, bn in (("step_paths", outs["path"], outs["accept_len"], outs["bonus"]),
+                              ("deepest_paths", d(deep_path), d(deep_len), bonus)):
+        hp, hl = (step_path, step_len) if name == "step_paths" else (deep_path, deep_len)
+        def call():
+            tv.tv_commit(kp, vp, table, plens, w.max_prefix_len, tokens, pth, ln, bn, outputs=co)
+        for _ in range(5):
+            call()
+        # One call is shorter than its host-side launch, so the stream is held
+        # by a bounded spin kernel while the host queues all 50 calls; the
+        # events then time the calls back to back on the device. The spin must
+        # outlast the queueing, which is checked.
+        es, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        torch.cuda.synchronize()
+        es.record()
+        torch.cuda._sleep(5_000_000)
+        e0.record()
+        h0 = time.perf_counter()
+        for _ in range(50):
+            call()
+        host_ms = (time.perf_counter() - h0) * 1e3
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 50 * 1e3
+        held_ms = es.elapsed_time(e0)
+        nbytes = commit_bytes(w, hp, hl)
+        res[name] = {"avg_us": us, "queued_within_spin": bool(host_ms < held_ms),
+                     "rows_moved_per_kv_head": commit_moves(w, hp, hl),
+                     "mean_accept_len": float(np.mean(hl)), "bytes": nbytes, "gbs": nbytes / us / 1e3}
+    assert tv.tv_device_error(dev) == 0
+    res["note"] = ("tv_commit after acceptance (not part of the step); one workgroup per (sequence, KV head), "
+                   "a single dependent read-then-write round trip: latency-bound, not bandwidth-bound")
+    return res
 
 
 def main():
@@ -265,6 +339,7 @@ def main():
     t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
     result["mask_overhead"] = {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
                                "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
+    result["commit"] = commit_timing(tv, torch, dev, w, depth, d, kp, vp, table, plens, d(w.draft_tokens), outs)
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
