@@ -377,24 +377,33 @@ int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, c
 }
 
 /* ------------------------------------------------------------------------ */
-/* O4: stochastic acceptance on a chain                                     */
+/* O4: stochastic acceptance on a chain or a tree                           */
 /*                                                                          */
 /* [Sonar page], draft-target section: acceptance compares the full draft   */
 /* and target distributions, and the target always adds one token after the */
 /* accepted drafts. [EAGLE-2 page], benchmark discussion: verification is   */
 /* rejection sampling, so the output follows the target's distribution      */
-/* exactly (lossless). The pages cite Leviathan et al. and Chen et al. but  */
-/* print no formula; this is their standard rule, the plainest reading:     */
-/*  - p_j = softmax(target row j / T), q_i = softmax(draft row i / T), fp64;*/
-/*  - node i (i = 1..N-1, token t_i) is accepted iff u[i-1] < p_{i-1}(t_i) /*/
-/*    q_i(t_i); a ratio >= 1 always accepts since u < 1;                    */
-/*  - at the first rejection the next token is drawn from                   */
-/*    r = max(0, p_{i-1} - q_i) by inverse CDF in token order with          */
-/*    theta = u[N-1] * sum(r): the smallest x whose running sum exceeds     */
-/*    theta (the last x with r > 0 if rounding leaves none; p_{i-1} itself  */
-/*    if sum(r) = 0);                                                       */
-/*  - if all drafts are accepted the bonus is the same draw from p_{N-1}.   */
-/* Multi-branch trees are not covered: the pages give no tree rule.         */
+/* exactly (lossless). The pages cite Leviathan et al. and Chen et al. (and */
+/* SpecInfer for trees) but print no formula; the plainest reading is their */
+/* standard rule, applied to one candidate after another:                   */
+/*  - p_j = softmax(target row j / T), q_c = softmax(draft row c / T), fp64;*/
+/*    draft row c is the distribution node c's token was drawn from;        */
+/*  - the walk starts at the root with pi = p_0; the children c of the      */
+/*    current node are tested in increasing id order: c is accepted iff     */
+/*    u[c-1] < pi(t_c) / q_c(t_c) (a ratio >= 1 always accepts, u < 1);     */
+/*  - an accepted child becomes the current node, with pi = p_c;            */
+/*  - a rejected child replaces pi by the residual max(0, pi - q_c),        */
+/*    normalised, before the next sibling is tested (a residual of mass 0   */
+/*    leaves pi unchanged);                                                 */
+/*  - when no child of the current node is accepted (or it has none), the   */
+/*    next token is drawn from pi by inverse CDF in token order with        */
+/*    theta = u[N-1] * (sum of pi's unnormalised weights): the smallest x   */
+/*    whose running sum exceeds theta, or the last x with positive weight  */
+/*    if rounding leaves none.                                              */
+/* On a chain this is the single-candidate rule: accept node i iff          */
+/* u[i-1] < p_{i-1}(t_i) / q_i(t_i), and at the first rejection draw from   */
+/* max(0, p_{i-1} - q_i) (from p_{i-1} if that is 0), or from p_{N-1} when  */
+/* every draft is accepted.                                                 */
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
@@ -452,11 +461,7 @@ typedef struct {
   double T, mp, Zp, mq, Zq;
 } resid_ctx;
 
-static double residual_w(const void *vc, int64_t x) {
-  const resid_ctx *c = (const resid_ctx *)vc;
-  double d = prob(c->prow, x, c->T, c->mp, c->Zp) - prob(c->qrow, x, c->T, c->mq, c->Zq);
-  return d > 0.0 ? d : 0.0;
-}
+static double array_w(const void *vc, int64_t x) { return ((const double *)vc)[x]; }
 
 static double target_w(const void *vc, int64_t x) {
   const resid_ctx *c = (const resid_ctx *)vc;
@@ -476,9 +481,6 @@ int tvo_accept_stochastic(const float *target_logits, const float *draft_logits,
     return TVO_ERR_INVALID_ARG;
   int st = check_tree(parents, B, N, 1);
   if (st != TVO_OK) return st;
-  for (int64_t b = 0; b < B; ++b)
-    for (int32_t i = 1; i < N; ++i)
-      if (parents[b * N + i] != i - 1) return TVO_ERR_UNSUPPORTED;
   st = check_tokens(draft_tokens, B, N, V);
   if (st != TVO_OK) return st;
 
@@ -486,6 +488,11 @@ int tvo_accept_stochastic(const float *target_logits, const float *draft_logits,
   const int64_t R = (int64_t)B * N;
   double *mp = (double *)malloc(sizeof(double) * R), *Zp = (double *)malloc(sizeof(double) * R);
   double *mq = (double *)malloc(sizeof(double) * R), *Zq = (double *)malloc(sizeof(double) * R);
+  double *wbuf = (double *)malloc(sizeof(double) * 2 * (size_t)V);
+  if (!mp || !Zp || !mq || !Zq || !wbuf) {
+    free(mp), free(Zp), free(mq), free(Zq), free(wbuf);
+    return TVO_ERR_RUNTIME;
+  }
   softmax_ctx sp = {target_logits, V, T, mp, Zp};
   softmax_ctx sq = {draft_logits, V, T, mq, Zq};
   parallel_for(R, nthreads, softmax_stats, &sp);
@@ -493,47 +500,68 @@ int tvo_accept_stochastic(const float *target_logits, const float *draft_logits,
 
   for (int64_t b = 0; b < B; ++b) {
     const int32_t *tok = draft_tokens + b * N;
+    const int32_t *par = parents + b * N;
     const float *u = uniforms + b * N;
     double *mg = margins ? margins + b * N : NULL;
     if (mg)
       for (int32_t i = 0; i < N; ++i) mg[i] = INFINITY;
-    int32_t k = 0; /* accepted drafts */
-    int rejected_at = -1;
-    for (int32_t i = 1; i < N; ++i) {
-      const int64_t rp = b * N + (i - 1), rq = b * N + i;
-      double p = prob(target_logits + rp * V, tok[i], T, mp[rp], Zp[rp]);
-      double qv = prob(draft_logits + rq * V, tok[i], T, mq[rq], Zq[rq]);
-      double a = p / qv;
-      if (mg) mg[i - 1] = fabs((double)u[i - 1] - a);
-      if ((double)u[i - 1] < a) {
-        k += 1;
-      } else {
-        rejected_at = i;
-        break;
+    int32_t *pb = path + b * N;
+    for (int32_t i = 0; i < N; ++i) pb[i] = -1;
+    pb[0] = 0;
+    int32_t k = 0, node = 0;
+    /* the distribution the next test and the final draw use: p_node while
+     * cur is NULL, else the stored residual cur (unnormalised, mass M) */
+    double *cur = NULL, M = 1.0;
+    for (;;) {
+      const int64_t rp = b * N + node;
+      const float *prow = target_logits + rp * V;
+      int32_t accepted = -1;
+      for (int32_t c = node + 1; c < N; ++c) {
+        if (par[c] != node) continue; /* children in increasing id order */
+        const int64_t rq = b * N + c;
+        const float *qrow = draft_logits + rq * V;
+        const double qv = prob(qrow, tok[c], T, mq[rq], Zq[rq]);
+        const double pv = cur ? cur[tok[c]] / M : prob(prow, tok[c], T, mp[rp], Zp[rp]);
+        const double a = pv / qv;
+        if (mg) mg[c - 1] = fabs((double)u[c - 1] - a);
+        if ((double)u[c - 1] < a) {
+          accepted = c;
+          break;
+        }
+        /* rejected: the next sibling is tested against, and the final draw
+         * taken from, the residual max(0, pi - q_c) of the current pi */
+        double *nw = cur == wbuf ? wbuf + V : wbuf;
+        double Rsum = 0.0;
+        for (int64_t x = 0; x < V; ++x) {
+          const double d = (cur ? cur[x] / M : prob(prow, x, T, mp[rp], Zp[rp])) - prob(qrow, x, T, mq[rq], Zq[rq]);
+          nw[x] = d > 0.0 ? d : 0.0;
+          Rsum += nw[x];
+        }
+        if (Rsum > 0.0) { /* a residual of mass 0 leaves pi unchanged */
+          cur = nw;
+          M = Rsum;
+        }
       }
+      if (accepted < 0) break;
+      pb[++k] = accepted;
+      node = accepted;
+      cur = NULL;
+      M = 1.0;
     }
     double smargin = INFINITY;
     int32_t pick;
-    if (rejected_at > 0) {
-      const int64_t rp = b * N + (rejected_at - 1), rq = b * N + rejected_at;
-      resid_ctx c = {target_logits + rp * V, draft_logits + rq * V, T, mp[rp], Zp[rp], mq[rq], Zq[rq]};
-      double Rsum = 0.0;
-      for (int64_t x = 0; x < V; ++x) Rsum += residual_w(&c, x);
-      if (Rsum > 0.0)
-        pick = inverse_cdf(residual_w, &c, V, (double)u[N - 1], &smargin);
-      else
-        pick = inverse_cdf(target_w, &c, V, (double)u[N - 1], &smargin);
+    if (cur) {
+      pick = inverse_cdf(array_w, cur, V, (double)u[N - 1], &smargin);
     } else {
-      const int64_t rp = b * N + (N - 1);
+      const int64_t rp = b * N + node;
       resid_ctx c = {target_logits + rp * V, NULL, T, mp[rp], Zp[rp], 0.0, 1.0};
       pick = inverse_cdf(target_w, &c, V, (double)u[N - 1], &smargin);
     }
     if (mg) mg[N - 1] = smargin;
-    int32_t *pb = path + b * N;
-    for (int32_t i = 0; i < N; ++i) pb[i] = i <= k ? i : -1;
     accept_len[b] = k + 1;
     bonus[b] = pick;
   }
+  free(wbuf);
   free(mp);
   free(Zp);
   free(mq);

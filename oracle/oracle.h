@@ -50,10 +50,12 @@ int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, c
                       int32_t N, int32_t V, int32_t *accept_len, int32_t *path, int32_t *bonus,
                       int32_t *target_argmax, int nthreads);
 
-/* Stochastic acceptance on a chain: accept node i iff u[i-1] < p_{i-1}(t_i)/q_i(t_i),
- * then one inverse-CDF draw with u[N-1] from max(0, p - q) (or from p_{N-1}
- * when every draft is accepted). margins [B][N] (nullable): |u - a_i| for each
- * tested node at [i-1], distance of the final draw to the nearest CDF
+/* Stochastic acceptance on a chain or tree: from the root, test the current
+ * node's children in id order, child c accepted iff u[c-1] < pi(t_c)/q_c(t_c)
+ * with pi = p_node at first and, after each rejected sibling, the normalised
+ * residual max(0, pi - q_c); when no child is accepted, draw the next token
+ * from pi by inverse CDF with u[N-1]. margins [B][N] (nullable): |u - a| for
+ * each tested node c at [c-1], distance of the final draw to the nearest CDF
  * boundary relative to the total mass at [N-1], +inf where unused. */
 int tvo_accept_stochastic(const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
                           const int32_t *parents, const float *uniforms, int32_t B, int32_t N, int32_t V,

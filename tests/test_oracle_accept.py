@@ -230,10 +230,139 @@ def test_stochastic_status_codes():
     args = (w.target_logits, w.draft_logits, w.draft_tokens)
     assert oracle.status_accept_stochastic(*args, w.parents, w.uniforms, w.B, w.N, w.V, 1.0)[0] == oracle.OK
     tree = w.parents.copy()
-    tree[:, 2] = 0  # not a chain
-    assert oracle.status_accept_stochastic(*args, tree, w.uniforms, w.B, w.N, w.V, 1.0)[0] == oracle.UNSUPPORTED
+    tree[:, 2] = 0  # a tree: accepted
+    assert oracle.status_accept_stochastic(*args, tree, w.uniforms, w.B, w.N, w.V, 1.0)[0] == oracle.OK
+    tree[:, 3] = 3  # a parent not earlier than its child
+    assert oracle.status_accept_stochastic(*args, tree, w.uniforms, w.B, w.N, w.V, 1.0)[0] == oracle.INVALID_TREE
+    tree = w.parents.copy()
+    tree[:, 0] = 0  # the root must have no parent
+    assert oracle.status_accept_stochastic(*args, tree, w.uniforms, w.B, w.N, w.V, 1.0)[0] == oracle.INVALID_TREE
     assert oracle.status_accept_stochastic(*args, w.parents, w.uniforms, w.B, w.N, w.V, 0.0)[0] == \
         oracle.INVALID_ARG
+
+
+# ------------------------------------------------------------------ stochastic on trees
+
+def test_stochastic_tree_hand_worked_fixture():
+    g = json.load(open(os.path.join(GOLD, "stochastic_tree_hand.json")))
+    B = len(g["parents"])
+    tl = np.tile(np.array(g["target_rows"], np.float32)[None], (B, 1, 1))
+    dl = np.tile(np.array(g["draft_rows"], np.float32)[None], (B, 1, 1))
+    r = oracle.accept_stochastic(tl, dl, np.array(g["draft_tokens"], np.int32), np.array(g["parents"], np.int32),
+                                 np.array(g["uniforms"], np.float32), g["temperature"])
+    for k, v in g["expect"].items():
+        assert r[k].tolist() == v, k
+    assert (r["margins"][np.isfinite(r["margins"])] > 0.02).all()
+
+
+def sample_rows(seed, tid, q):
+    """One token per row of the probability matrix q by inverse CDF (seeded)."""
+    u = tvgen.uniform_f32(seed, tid, (q.shape[0],)).astype(np.float64)
+    c = np.cumsum(q, -1)
+    return np.minimum((c < (u * c[:, -1])[:, None]).sum(-1), q.shape[1] - 1).astype(np.int32)
+
+
+def star_trial(k=3, V=8, M=200000, seed=21, without_replacement=False, with_path=False):
+    """M cycles of a root with k children; child c's token drawn from its
+    draft row (with or without the earlier siblings' tokens). Target rows of
+    the children depend only on their token (table P2), as a real target's
+    would. Returns (emitted tokens [M][2], accept_len, p0, q rows, P2)."""
+    N = k + 1
+    base = tvgen.normal_f32(seed, 1, (1 + k, V), sigma=1.5)
+    P2 = tvgen.normal_f32(seed, 2, (V, V), sigma=1.0)
+    tl = np.zeros((M, N, V), np.float32)
+    dl = np.zeros((M, N, V), np.float32)
+    tl[:, 0] = base[0]
+    tokens = np.zeros((M, N), np.int32)
+    for c in range(1, N):
+        row = np.tile(base[c], (M, 1))
+        if without_replacement:
+            for e in range(1, c):
+                row[np.arange(M), tokens[:, e]] = -np.inf
+        dl[:, c] = row
+        tokens[:, c] = sample_rows(seed, 10 + c, softmax64(row))
+        tl[:, c] = P2[tokens[:, c]]
+    u = tvgen.uniform_f32(seed, 3, (M, N))
+    parents = np.tile(np.array([-1] + [0] * k, np.int32), (M, 1))
+    r = oracle.accept_stochastic(tl, dl, tokens, parents, u, 1.0)
+    first = np.where(r["accept_len"] >= 2, tokens[np.arange(M), np.maximum(r["path"][:, 1], 0)], r["bonus"])
+    second = np.where(r["accept_len"] >= 2, r["bonus"], -1)
+    out = (np.stack([first, second], 1), r["accept_len"], softmax64(base[0]), softmax64(base[1:]), P2)
+    return out + (r["path"][:, 1],) if with_path else out
+
+
+@pytest.mark.parametrize("without_replacement", [False, True])
+def test_tree_lossless_first_token(without_replacement):
+    em, alen, p, q, _ = star_trial(without_replacement=without_replacement, seed=21 + without_replacement)
+    M = alen.size
+    assert np.abs(p - q[0]).sum() > 0.3 and (alen == 1).mean() > 0.05  # rejections of every sibling happen
+    assert stats.chisquare(np.bincount(em[:, 0], minlength=p.size), p * M).pvalue > 1e-4
+
+
+def test_tree_lossless_second_token():
+    """Given the first token x came from an accepted child, the next token
+    follows the target's distribution after x (the child's row P2[x])."""
+    em, alen, _, _, P2 = star_trial(seed=31)
+    for x in range(P2.shape[0]):
+        sel = (alen == 2) & (em[:, 0] == x)
+        if sel.sum() < 2000:
+            continue
+        obs = np.bincount(em[sel, 1], minlength=P2.shape[1])
+        assert stats.chisquare(obs, softmax64(P2[x]) * sel.sum()).pvalue > 1e-4, x
+
+
+def test_tree_sibling_acceptance_closed_form():
+    # child 1 is accepted w.p. a1 = sum min(p, q1); child 2, tested after a
+    # rejection, w.p. (1 - a1) * sum min(pi1, q2) with pi1 = norm(max(0, p - q1))
+    _, alen, p, q, _, acc_child = star_trial(k=2, seed=41, with_path=True)
+    M = alen.size
+    a1 = np.minimum(p, q[0]).sum()
+    r1 = np.maximum(p - q[0], 0)
+    a2 = (1 - a1) * np.minimum(r1 / r1.sum(), q[1]).sum()
+    for child, rate in ((1, a1), (2, a2)):
+        got = (acc_child == child).mean()
+        assert abs(got - rate) < 5 * np.sqrt(rate * (1 - rate) / M), (child, got, rate)
+
+
+def test_tree_temperature_to_zero_reproduces_greedy():
+    # dynamic trees have distinct sibling tokens, so at most one child of a
+    # node matches and the greedy longest path is the first-match walk
+    V, N = 200, 24
+    w = tvgen.make_workload(2, seed=78, with_kv=False, overrides=dict(B=64, N=N, V=V))
+    w.draft_logits = tvgen.normal_f32(78, 90, (w.B, N, V))
+    w.uniforms = tvgen.uniform_f32(78, 91, (w.B, N))
+    T = 1e-6
+    y = w.target_logits.argmax(-1)
+    for b in range(w.B):
+        for pnode in range(N):
+            kids = np.nonzero(w.parents[b] == pnode)[0]
+            # plant a match under about a third of the parents, keeping the
+            # siblings' tokens distinct
+            if len(kids) and (b + pnode) % 3 == 0 and y[b, pnode] not in w.draft_tokens[b, kids]:
+                w.draft_tokens[b, kids[(b + pnode) % len(kids)]] = y[b, pnode]
+    for b in range(w.B):
+        for pnode in range(N):
+            kids = np.nonzero(w.parents[b] == pnode)[0]
+            assert len(set(w.draft_tokens[b, kids].tolist())) == len(kids)
+    for c in range(1, N):
+        w.draft_logits[np.arange(w.B), c, w.draft_tokens[:, c]] = w.draft_logits[:, c].max(-1) + 1.0
+    for arr in (w.target_logits, w.draft_logits[:, 1:]):
+        srt = np.sort(arr.reshape(-1, V), axis=-1)
+        assert (srt[:, -1] - srt[:, -2]).min() > 100 * T
+    r = oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms, T)
+    g = oracle.accept_greedy(w.target_logits, w.draft_tokens, w.parents)
+    assert (r["accept_len"] == g["accept_len"]).all()
+    assert (r["path"] == g["path"]).all()
+    assert (r["bonus"] == g["bonus"]).all()
+    assert g["accept_len"].max() >= 3
+
+
+def test_tree_star_with_p_equal_q_accepts_first_child():
+    w = tvgen.make_workload(5, seed=79, with_kv=False, overrides=dict(B=32, V=300, N=6))
+    w.parents[:] = [-1, 0, 0, 0, 0, 0]
+    w.draft_logits[:, 1:] = w.target_logits[:, :1]
+    r = oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms, 1.0)
+    assert (r["accept_len"] == 2).all() and (r["path"][:, 1] == 1).all()
 
 
 # ------------------------------------------------------------------ tau
