@@ -30,7 +30,7 @@
  *    left untouched.
  *  - Device-detected bad data (a parent not earlier than its child, a page id
  *    outside [0, num_pages), a token outside [0, V), a prefix length outside
- *    [0, max_prefix_len], a non-chain tree in stochastic mode) sets a sticky
+ *    [0, max_prefix_len]) sets a sticky
  *    per-context flag read by tv_device_error; the affected outputs are
  *    written as NaN (attention) or -1 (masks: 0 with depth -1; acceptance).
  *  - Tree numbering: node ids are topological (parent[i] < i), as in the
@@ -52,8 +52,7 @@ typedef enum tv_status {
   TV_OK = 0,
   TV_ERR_INVALID_ARG = 1,  /* bad scalar, NULL pointer, bad page id / token / prefix length */
   TV_ERR_INVALID_TREE = 2, /* parent[b][i] outside {-1} U [0, i), or accept root with a parent */
-  TV_ERR_UNSUPPORTED = 3,  /* shape outside what the kernels implement (N > 64, D not 64/128,
-                              stochastic acceptance on a non-chain tree) */
+  TV_ERR_UNSUPPORTED = 3,  /* shape outside what the kernels implement (N > 64, D not 64/128) */
   TV_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the *_workspace_bytes figure */
   TV_ERR_HIP = 5           /* HIP runtime error (launch failure, bad device) */
 } tv_status;
@@ -116,7 +115,8 @@ tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const vo
                        const uint64_t *tree_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                        float sm_scale, void *out, tv_dtype out_dtype, void *workspace, size_t workspace_bytes);
 
-/* Workspace (bytes) tv_accept needs: per-row partial vocab reductions. */
+/* Workspace (bytes) tv_accept needs: per-row partial vocab reductions, and
+ * in stochastic mode two residual rows of V doubles per sequence. */
 size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode mode);
 
 /* Acceptance and bonus token ([EAGLE-2 page], third pillar: longest
@@ -130,7 +130,7 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  *   draft_tokens   int32 [B][N]; [b][0] is the root's token (not verified)
  *   parents        int32 [B][N]; parents[b][0] must be -1
  *   uniforms       fp32 [B][N] in [0, 1) (stochastic only, else NULL):
- *                  u[i-1] tests node i, u[N-1] drives the final draw
+ *                  u[c-1] tests node c, u[N-1] drives the final draw
  *   temperature    > 0; logits are divided by it (stochastic only)
  *   accept_len     int32 [B]: root + accepted nodes = accepted drafts + 1
  *                  (counts the bonus token)
@@ -141,12 +141,22 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  *   below every number); node c matches iff draft_tokens[c] == y_parent(c);
  *   the longest root path of matching nodes wins, lexicographically smallest
  *   node sequence on ties; bonus = y at its last node.
- * STOCHASTIC (chains only, parents[i] = i-1): p_j = softmax(target row j / T),
- *   q_i = softmax(draft row i / T) in fp64; node i accepted iff
- *   u[i-1] < p_{i-1}(t_i) / q_i(t_i), stop at the first rejection; the next
- *   token is the inverse-CDF draw (token order, theta = u[N-1] * total mass,
- *   smallest token whose running sum exceeds theta) from max(0, p - q) at the
- *   rejection (from p if that mass is 0), or from p_{N-1} when all pass.
+ * STOCHASTIC (chains and trees): p_j = softmax(target row j / T), q_c =
+ *   softmax(draft row c / T) in fp64, where draft row c is the distribution
+ *   node c's token was drawn from (for siblings drawn without replacement,
+ *   the row with the earlier siblings' tokens removed). The pages give no
+ *   rule for several candidates; the single-candidate rule is applied to one
+ *   candidate after another: from the root, with pi = p_node, the children c
+ *   of the current node are tested in id order, c accepted iff
+ *   u[c-1] < pi(t_c) / q_c(t_c); an accepted child becomes the current node
+ *   (pi = p_c); a rejected one replaces pi by max(0, pi - q_c) normalised
+ *   (unchanged if its mass is 0) before the next sibling. When no child is
+ *   accepted, the next token is the inverse-CDF draw from pi (token order,
+ *   theta = u[N-1] * total mass, smallest token whose running sum exceeds
+ *   theta; the last token of positive mass if rounding finds none). On a
+ *   chain this is: accept while u[i-1] < p_{i-1}(t_i) / q_i(t_i), then draw
+ *   from max(0, p - q) at the rejection (p if its mass is 0), or from
+ *   p_{N-1} when every draft is accepted.
  * Adds sum(accept_len) and B to the context's tau counters. Requires
  * 1 <= N <= 64 when B > 0, V >= 1. */
 tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,

@@ -17,11 +17,15 @@
 //           differing mask bit). Path, length, bonus and tau counters follow.
 // Stochastic (Sonar page, draft-target section: acceptance compares the full
 // draft and target distributions; EAGLE-2 page: rejection sampling keeps the
-// target distribution) on chains:
+// target distribution), on chains and trees:
 //   pass 1  per-chunk max and sum of exp (fp64) of logits / T, target and draft
-//   pass 2  one workgroup per sequence: merge the chunk statistics, test
-//           u[i-1] < p_{i-1}(t_i) / q_i(t_i) node by node, then one
-//           inverse-CDF draw over max(0, p - q) (or p) with theta = u[N-1] * mass.
+//   pass 2  one workgroup per sequence: merge the chunk statistics and walk
+//           from the root, testing the current node's children in id order
+//           (u[c-1] < pi(t_c) / q_c(t_c)); an accepted child becomes the
+//           current node with pi = its target row, a rejected one replaces pi
+//           by the normalised residual max(0, pi - q_c) for the next sibling.
+//           The next token is one inverse-CDF draw from the final pi (or the
+//           last rejected sibling's residual) with theta = u[N-1] * mass.
 //   Every exponential is fp64 (exp_fast, within a few ulp), so a decision
 //   agrees with exact arithmetic whenever its margin exceeds ~1e-15.
 #include <math.h>
@@ -301,65 +305,80 @@ __device__ inline double prob_at(const float *row, int x, double T, double invT,
 }
 
 constexpr int kPathThreads = 512;
-constexpr int kBlk = 16;  // tokens per register block of the row sweep
+constexpr int kBlk = 16;  // tokens per register block of a row sweep
 
-// One workgroup per sequence. Wavefront 0 validates the chain and runs the
-// accept tests with one lane per node; the first rejected node (or the end
-// of the chain) fixes the row of the final draw. That row - max(0, p - q)
-// after a rejection, p otherwise - is then swept once by all threads in
-// contiguous token-order segments (vector loads, 16 tokens per register
-// block), the segment sums are scanned in a fixed order, and only the
-// segment whose running sum passes theta is swept again, one token per lane
-// of one wavefront, to find the token.
+// The target distribution pi the walk holds: the current node's target row
+// (w == nullptr, invM = 1), or a stored residual w[0..V) of mass 1 / invM.
+struct Pi {
+  const double *w;
+  double invM;
+};
+
+// One workgroup per sequence, for chains and trees alike. Wavefront 0
+// validates the tree, computes for every node c its first test's p(t_c)
+// (under its parent's target row) and q_c(t_c), and the children of every
+// node as a bit mask. Every thread then runs the same walk from the LDS
+// copies: the current node's children are tested in id order; a rejection
+// followed by another sibling stores the residual max(0, pi - q_c) of the
+// whole row in one of two per-sequence buffers (a sweep by all threads, its
+// mass summed in a fixed order), and the next sibling is tested against it.
+// The final draw - from the last rejected sibling's residual (built on the
+// fly), or from pi itself - sweeps the row once in contiguous token-order
+// segments (16-token register blocks, next block's loads issued before the
+// current block's exponentials), scans the segment sums in a fixed order,
+// and re-sweeps only the segment whose running sum passes theta, one token
+// per lane of one wavefront.
 template <bool kVec>
 __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
     const int32_t *__restrict__ parents, const float *__restrict__ uniforms, int B, int N, int V, int chunks,
-    double T, double invT, const double *__restrict__ stats, int32_t *__restrict__ accept_len,
-    int32_t *__restrict__ path, int32_t *__restrict__ bonus, unsigned long long *state) {
-  __shared__ int s_err, s_k, s_rej, s_pick, s_lastpos, s_cross;
+    double T, double invT, const double *__restrict__ stats, double *__restrict__ wbuf,
+    int32_t *__restrict__ accept_len, int32_t *__restrict__ path, int32_t *__restrict__ bonus,
+    unsigned long long *state) {
+  __shared__ int s_err, s_pick, s_lastpos, s_cross, s_cross_last;
   __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total, s_cprefix;
-  __shared__ int s_cross_last;
+  __shared__ double s_pa[64], s_qa[64], s_u[64];
+  __shared__ int s_tok[64], s_path[64];
+  __shared__ unsigned long long s_child[64];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t base = static_cast<int64_t>(b) * N;
   if (wid == 0) {
     // validation with the same precedence as a serial check: a bad parent
-    // anywhere, then a non-chain tree, then a draft token outside [0, V)
-    bool tree_bad = false, nonchain = false, tok_bad = false;
+    // anywhere, then a draft token outside [0, V)
+    bool tree_bad = false, tok_bad = false;
+    int p = -1, t = 0;
     if (lane < N) {
-      const int p = parents[base + lane];
+      p = parents[base + lane];
       tree_bad = p < -1 || p >= lane || (lane == 0 && p != -1);
-      nonchain = lane >= 1 && p != lane - 1;
       if (lane >= 1) {
-        const int t = draft_tokens[base + lane];
+        t = draft_tokens[base + lane];
         tok_bad = t < 0 || t >= V;
       }
+      s_u[lane] = static_cast<double>(uniforms[base + lane]);
     }
-    const int err = __builtin_amdgcn_ballot_w64(tree_bad)  ? TV_ERR_INVALID_TREE
-                    : __builtin_amdgcn_ballot_w64(nonchain) ? TV_ERR_UNSUPPORTED
-                    : __builtin_amdgcn_ballot_w64(tok_bad)  ? TV_ERR_INVALID_ARG
-                                                            : 0;
-    // chain test, one lane per node i >= 1: accepted iff
-    // u[i-1] < p_{i-1}(t_i) / q_i(t_i); the first rejection ends the chain
-    bool rejected = false;
+    const int err = __builtin_amdgcn_ballot_w64(tree_bad) ? TV_ERR_INVALID_TREE
+                    : __builtin_amdgcn_ballot_w64(tok_bad) ? TV_ERR_INVALID_ARG
+                                                           : 0;
     if (!err && lane >= 1 && lane < N) {
-      const int t = draft_tokens[base + lane];
-      const RowStat sp = merge_stats(stats, base + lane - 1, 0, chunks);
-      const RowStat sq = merge_stats(stats, base + lane, 1, chunks);
-      const double pa = prob_at(target + (base + lane - 1) * V, t, T, invT, sp);
-      const double qa = prob_at(draft + (base + lane) * V, t, T, invT, sq);
-      rejected = !(static_cast<double>(uniforms[base + lane - 1]) < pa / qa);
+      s_tok[lane] = t;
+      if (p >= 0) {  // a node without a parent (forest) is never tested
+        const RowStat sp = merge_stats(stats, base + p, 0, chunks);
+        const RowStat sq = merge_stats(stats, base + lane, 1, chunks);
+        s_pa[lane] = prob_at(target + (base + p) * V, t, T, invT, sp);
+        s_qa[lane] = prob_at(draft + (base + lane) * V, t, T, invT, sq);
+      }
     }
-    const uint64_t rj = __builtin_amdgcn_ballot_w64(rejected);
+    for (int n = 0; n < N; ++n) {
+      const uint64_t kids = __builtin_amdgcn_ballot_w64(!err && lane >= 1 && lane < N && p == n);
+      if (lane == 0) s_child[n] = kids;
+    }
     if (lane == 0) {
       s_err = err;
-      const int rej = rj ? __builtin_ctzll(rj) : -1;
-      s_rej = rej;
-      s_k = rej > 0 ? rej - 1 : N - 1;
       s_pick = 0x7FFFFFFF;
       s_lastpos = -1;
       s_cross = 0x7FFFFFFF;
+      s_path[0] = 0;
     }
   }
   __syncthreads();
@@ -372,16 +391,12 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     for (int i = tid; i < N; i += kPathThreads) path[base + i] = -1;
     return;
   }
-  const int k = s_k, rej = s_rej;
-  const int prow = rej > 0 ? rej - 1 : N - 1;
-  const float *P = target + (base + prow) * V;
-  const float *Q = rej > 0 ? draft + (base + rej) * V : nullptr;
-  const RowStat sp = merge_stats(stats, base + prow, 0, chunks);
-  const RowStat sq = Q ? merge_stats(stats, base + rej, 1, chunks) : RowStat{0.0, 1.0, 1.0};
-  const double u = static_cast<double>(uniforms[base + N - 1]);
   // contiguous segment per thread in token order, a multiple of 4 tokens
   const int seg = ((V + 4 * kPathThreads - 1) / (4 * kPathThreads)) * 4;
   const int x0 = min(tid * seg, V), x1 = min(x0 + seg, V);
+  double *const buf0 = wbuf + static_cast<int64_t>(b) * 2 * V;
+  double *const buf1 = buf0 + V;
+
   auto load_block = [&](const float *row, int xb, float (&v)[kBlk]) __attribute__((always_inline)) {
     if (kVec) {  // V % 4 == 0 and xb % 4 == 0: a float4 is either all in [x0, x1) or all out
 #pragma unroll
@@ -399,41 +414,57 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       for (int i = 0; i < kBlk; ++i) v[i] = xb + i < x1 ? row[xb + i] : -INFINITY;
     }
   };
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool residual = Q != nullptr && pass == 0;
-    auto weight = [&](float pl, float ql) __attribute__((always_inline)) {
-      double w = exp_fast(div_t(pl, T, invT) - sp.m) * sp.invZ;  // padding (-inf) gives 0
-      if (residual) w = fmax(0.0, w - exp_fast(div_t(ql, T, invT) - sq.m) * sq.invZ);
-      return w;
-    };
-    double local = 0.0;
-    int lastpos = -1;
-    {
-      // register blocks of kBlk tokens; the next block's loads are issued
-      // before the current block's exponentials
-      float pv[kBlk], qv[kBlk], pn[kBlk], qn[kBlk];
+  auto load_wblock = [&](const double *w, int xb, double (&v)[kBlk]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) v[i] = xb + i < x1 ? w[xb + i] : 0.0;
+  };
+  // weight of one token: pi's weight (the target row's probability, or the
+  // stored residual's entry), or, with a sibling's draft row, the residual
+  // max(0, pi - q) with pi normalised
+  auto weight = [&](const RowStat &sp, const Pi &pi, bool with_q, const RowStat &sq, float pl, double wl,
+                    float ql) __attribute__((always_inline)) {
+    const double w = pi.w ? wl : exp_fast(div_t(pl, T, invT) - sp.m) * sp.invZ;  // padding (-inf) gives 0
+    if (!with_q) return w;
+    return fmax(0.0, w * pi.invM - exp_fast(div_t(ql, T, invT) - sq.m) * sq.invZ);
+  };
+  // one sweep of this thread's segment; optionally stores every weight
+  auto sweep = [&](const float *P, const RowStat &sp, const Pi &pi, const float *Q, const RowStat &sq, double *dst,
+                   double &local, int &lastpos) __attribute__((always_inline)) {
+    local = 0.0;
+    lastpos = -1;
+    float pv[kBlk], qv[kBlk], pn[kBlk], qn[kBlk];
+    double wv[kBlk], wn[kBlk];
+    if (pi.w)
+      load_wblock(pi.w, x0, wv);
+    else
       load_block(P, x0, pv);
-      if (residual) load_block(Q, x0, qv);
-      for (int xb = x0; xb < x1; xb += kBlk) {
-        if (xb + kBlk < x1) {
+    if (Q) load_block(Q, x0, qv);
+    for (int xb = x0; xb < x1; xb += kBlk) {
+      if (xb + kBlk < x1) {
+        if (pi.w)
+          load_wblock(pi.w, xb + kBlk, wn);
+        else
           load_block(P, xb + kBlk, pn);
-          if (residual) load_block(Q, xb + kBlk, qn);
-        }
+        if (Q) load_block(Q, xb + kBlk, qn);
+      }
 #pragma unroll
-        for (int i = 0; i < kBlk; ++i) {
-          const double w = weight(pv[i], residual ? qv[i] : 0.f);
-          local += w;
-          if (w > 0.0) lastpos = xb + i;
-        }
+      for (int i = 0; i < kBlk; ++i) {
+        const double w = weight(sp, pi, Q != nullptr, sq, pv[i], wv[i], qv[i]);
+        local += w;
+        if (w > 0.0) lastpos = xb + i;
+        if (dst && xb + i < x1) dst[xb + i] = w;
+      }
 #pragma unroll
-        for (int i = 0; i < kBlk; ++i) {
-          pv[i] = pn[i];
-          qv[i] = qn[i];
-        }
+      for (int i = 0; i < kBlk; ++i) {
+        pv[i] = pn[i];
+        qv[i] = qn[i];
+        wv[i] = wn[i];
       }
     }
-    // exclusive prefix of the segment sums: a fixed-order scan within each
-    // wavefront, then over the wavefront totals in order
+  };
+  // exclusive prefix of the segment sums and their total: a fixed-order
+  // scan within each wavefront, then over the wavefront totals in order
+  auto scan = [&](double local, double &prefix, double &total) __attribute__((always_inline)) {
     double incl = local;
     for (int d = 1; d < 64; d <<= 1) {
       const double t = __shfl_up(incl, d);
@@ -452,12 +483,59 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       s_total = run;
     }
     __syncthreads();
-    const double prefix = s_wpre[wid] + excl;
-    const double total = s_total;
-    if (residual && !(total > 0.0)) {
-      __syncthreads();
-      continue;  // no residual mass: draw from p instead
+    prefix = s_wpre[wid] + excl;
+    total = s_total;
+    __syncthreads();
+  };
+
+  // the walk; every thread takes the same decisions from the same data
+  Pi pi{nullptr, 1.0};
+  int node = 0, k = 0, pend = -1;
+  for (;;) {
+    const float *P = target + (base + node) * V;
+    const RowStat sp = merge_stats(stats, base + node, 0, chunks);
+    uint64_t kids = s_child[node];
+    int acc = -1;
+    while (kids) {
+      const int c = __builtin_ctzll(kids);
+      kids &= kids - 1;
+      const double a = pi.w ? (pi.w[s_tok[c]] * pi.invM) / s_qa[c] : s_pa[c] / s_qa[c];
+      if (s_u[c - 1] < a) {
+        acc = c;
+        break;
+      }
+      if (!kids) {  // the last sibling: its residual is built on the fly by the final draw
+        pend = c;
+        break;
+      }
+      double *dst = pi.w == buf0 ? buf1 : buf0;
+      const RowStat sq = merge_stats(stats, base + c, 1, chunks);
+      double local, prefix, total;
+      int lastpos;
+      sweep(P, sp, pi, draft + (base + c) * V, sq, dst, local, lastpos);
+      scan(local, prefix, total);
+      if (total > 0.0) pi = Pi{dst, 1.0 / total};  // a residual of mass 0 leaves pi unchanged
     }
+    if (acc < 0) break;
+    node = acc;
+    ++k;
+    if (tid == 0) s_path[k] = acc;
+    pi = Pi{nullptr, 1.0};
+  }
+
+  // the final draw
+  const float *P = target + (base + node) * V;
+  const float *Q = pend >= 0 ? draft + (base + pend) * V : nullptr;
+  const RowStat sp = merge_stats(stats, base + node, 0, chunks);
+  const RowStat sq = Q ? merge_stats(stats, base + pend, 1, chunks) : RowStat{0.0, 1.0, 1.0};
+  const double u = s_u[N - 1];
+  for (int pass = 0; pass < 2; ++pass) {
+    const float *Qp = pass == 0 ? Q : nullptr;
+    double local, prefix, total;
+    int lastpos;
+    sweep(P, sp, pi, Qp, sq, nullptr, local, lastpos);
+    scan(local, prefix, total);
+    if (Qp && !(total > 0.0)) continue;  // no residual mass: draw from pi instead
     const double theta = u * total;
     // the first segment whose running sum passes theta holds the draw
     if (prefix + local > theta) atomicMin(&s_cross, tid);
@@ -478,10 +556,8 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       for (int xb = cx0; xb < cx1 && pick < 0; xb += 64) {
         const int x = xb + lane;
         double w = 0.0;
-        if (x < cx1) {
-          w = exp_fast(div_t(P[x], T, invT) - sp.m) * sp.invZ;
-          if (residual) w = fmax(0.0, w - exp_fast(div_t(Q[x], T, invT) - sq.m) * sq.invZ);
-        }
+        if (x < cx1)
+          w = weight(sp, pi, Qp != nullptr, sq, pi.w ? 0.f : P[x], pi.w ? pi.w[x] : 0.0, Qp ? Qp[x] : 0.f);
         double run = w;
         for (int d = 1; d < 64; d <<= 1) {
           const double t = __shfl_up(run, d);
@@ -504,15 +580,23 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     atomicAdd(state + 0, static_cast<unsigned long long>(k + 1));
     atomicAdd(state + 1, 1ull);
   }
-  for (int i = tid; i < N; i += kPathThreads) path[base + i] = i <= k ? i : -1;
+  for (int i = tid; i < N; i += kPathThreads) path[base + i] = i <= k ? s_path[i] : -1;
 }
 
 }  // namespace
 
+// stochastic: the chunk statistics, then (256-byte aligned) two residual
+// buffers of V doubles per sequence
+size_t stats_doubles(int B, int N, int V) {
+  const int chunks = (V + kChunk - 1) / kChunk;
+  return ((static_cast<size_t>(B) * N * 2 * chunks * 2 + 31) / 32) * 32;
+}
+
 size_t accept_ws_bytes(int B, int N, int V, tv_accept_mode mode) {
   const int chunks = (V + kChunk - 1) / kChunk;
   const size_t rows = static_cast<size_t>(B) * N;
-  return mode == TV_GREEDY ? rows * chunks * sizeof(unsigned long long) : rows * 2 * chunks * 2 * sizeof(double);
+  if (mode == TV_GREEDY) return rows * chunks * sizeof(unsigned long long);
+  return (stats_doubles(B, N, V) + static_cast<size_t>(B) * 2 * V) * sizeof(double);
 }
 
 tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits,
@@ -536,6 +620,7 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
     return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
   }
   auto *stats = static_cast<double *>(workspace);
+  double *wbuf = stats + stats_doubles(B, N, V);
   const double T = static_cast<double>(temperature), invT = 1.0 / T;
   const dim3 g1(chunks, B * N, 2);
   if (vec)
@@ -547,12 +632,12 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (vec)
     hipLaunchKernelGGL(stochastic_path_kernel<true>, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
-                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, accept_len,
-                       path, bonus, ctx->d_state);
+                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, wbuf,
+                       accept_len, path, bonus, ctx->d_state);
   else
     hipLaunchKernelGGL(stochastic_path_kernel<false>, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
-                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, accept_len,
-                       path, bonus, ctx->d_state);
+                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, wbuf,
+                       accept_len, path, bonus, ctx->d_state);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
