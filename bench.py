@@ -8,7 +8,8 @@ resident in HBM before timing starts. Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 
 --config picks the workload (1..5, default 2: the Llama-3-8B layer shape with
-an EAGLE-2 64-node tree). Only one GPU is supported.
+an EAGLE-2 64-node tree); --accept stochastic runs a greedy workload's tree
+with sampled acceptance instead. Only one GPU is supported.
 """
 from __future__ import annotations
 
@@ -33,6 +34,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--accept", default="default", choices=["default", "stochastic"],
+                    help="stochastic: run the workload's tree with sampled acceptance (T = 1, draft rows and "
+                         "uniforms from the same seeded streams, each node's token drawn from its draft row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -79,7 +83,7 @@ CALL_KERNELS = {"tv_attention": "attn_mfma_kernel (+ attn_combine_kernel when th
                 "tv_commit": "commit_kernel"}
 
 
-def measured_traffic(call, cfg):
+def measured_traffic(call, key):
     """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summaries (already scaled by the copy-kernel calibration), used only while
     the source hash recorded with them matches the current kernel source."""
@@ -97,7 +101,7 @@ def measured_traffic(call, cfg):
                 parts = line.split()
                 if len(parts) == 6 and parts[0] == "traffic" and parts[1] == call:
                     kv = dict(p.split("=", 1) for p in parts[2:])
-                    if int(kv["config"]) == cfg and kv["src"] == src:
+                    if kv["config"] == str(key) and kv["src"] == src:
                         return int(kv["read_bytes"]) + int(kv["write_bytes"])
     return None
 
@@ -217,7 +221,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     c = tvgen.CONFIGS[args.config]
-    w = tvgen.make_workload(args.config)
+    stochastic = args.accept == "stochastic" and c["mode"] != "stochastic"
+    w = tvgen.make_workload(args.config, overrides=dict(mode="stochastic") if stochastic else None)
+    key = f"{args.config}-stochastic" if stochastic else str(args.config)
     depth = np.stack([tvgen.tree_depths(p) for p in w.parents])
 
     def d(a, dtype=None):
@@ -311,7 +317,7 @@ def main():
                    "accept": w.mode, "page_size": 16, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": f"{dom}: {CALL_KERNELS[dom]}", "achieved": dk["gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["gbs"] / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(dom, args.config),
+                     "traffic": measured_traffic(dom, key),
                      "algorithmic_bytes": dk["bytes"],
                      "note": "achieved = algorithmic bytes per call / mean call duration (HIP events on the "
                              "launch stream around every 8th timed step); traffic = calibrated rocprofv3 "
