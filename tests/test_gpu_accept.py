@@ -193,6 +193,17 @@ def test_stochastic_star_every_sibling_rejected():
     assert (ref["accept_len"] == 1).any()
 
 
+@pytest.mark.parametrize("B,V", [(4, 65536), (3, 50001)])
+def test_stochastic_star_sliced_vocab(B, V):
+    # few sequences over a large vocabulary: each sequence's sweeps are split
+    # over many workgroups that exchange their slice sums; 63 siblings give
+    # long runs of stored residuals (an odd V takes the scalar loads)
+    w = tvgen.make_workload(5, seed=63, with_kv=False, overrides=dict(B=B, N=64, V=V, tree="star"))
+    w.draft_logits *= 2.5
+    w.draft_tokens[:, 1:] = tvgen.gumbel_argmax(63, 97, w.draft_logits, 1.0)[:, 1:]
+    stochastic_compare(w, f"star-sliced-B{B}-V{V}")
+
+
 def test_tau_accumulates_over_calls():
     tv.tv_tau_reset(DEV)
     lens = []

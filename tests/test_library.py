@@ -32,7 +32,8 @@ def test_status_strings_and_host_queries():
     # accept workspace: greedy = B*N*chunks 64-bit keys, stochastic = B*N*2*chunks*(m, Z) doubles
     chunks = (128256 + 8191) // 8192
     assert tv.tv_accept_workspace_bytes(8, 64, 128256, tv.GREEDY) == 8 * 64 * chunks * 8
-    assert tv.tv_accept_workspace_bytes(128, 5, 32000, tv.STOCHASTIC) == (128 * 5 * 2 * 4 * 2 + 128 * 2 * 32000) * 8
+    assert tv.tv_accept_workspace_bytes(128, 5, 32000, tv.STOCHASTIC) == \
+        (128 * 5 * 2 * 4 * 2 + 128 * 2 * 32000) * 8 + (128 * 16 + 64 * 256 * 4) * 8
     assert tv.tv_accept_workspace_bytes(0, 5, 32000, tv.GREEDY) == 0
     # a NULL context is rejected before anything touches a device
     assert lib.tv_build_mask(None, None, 1, 1, None, None) == tv.INVALID_ARG

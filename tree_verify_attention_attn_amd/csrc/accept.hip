@@ -225,13 +225,16 @@ template <bool kVec>
 __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__restrict__ target,
                                                                  const float *__restrict__ draft, int N, int V,
                                                                  int chunks, double T, double invT,
-                                                                 double *__restrict__ stats) {
+                                                                 double *__restrict__ stats,
+                                                                 unsigned long long *__restrict__ counters) {
   __shared__ double red[kThreads / 64];
   const int chunk = blockIdx.x;
   const int64_t row = blockIdx.y;  // b * N + j
   const int which = blockIdx.z;    // 0 = target, 1 = draft
   const int j = static_cast<int>(row % N);
   double *out = stats + ((row * 2 + which) * chunks + chunk) * 2;
+  // the path pass's exchange counter of this sequence starts at zero
+  if (counters && chunk == 0 && which == 0 && j == 0 && threadIdx.x == 0) counters[(row / N) * 16] = 0ull;
   if (which == 1 && j == 0) {  // draft row 0 is never used
     if (threadIdx.x == 0) {
       out[0] = 0.0;
@@ -305,7 +308,11 @@ __device__ inline double prob_at(const float *row, int x, double T, double invT,
 }
 
 constexpr int kPathThreads = 512;
-constexpr int kBlk = 16;  // tokens per register block of a row sweep
+constexpr int kBlk = 16;          // tokens per register block of a row sweep
+constexpr int kMaxGrid = 256;     // workgroups of a path pass that exchange partial sums
+constexpr int kMaxExchanges = 64; // exchanges per sequence: < N stored residuals + 2 draw passes
+constexpr int kCounterStride = 16;  // one 128-byte line per sequence counter
+constexpr int kSpinLimit = 1 << 22;
 
 // The target distribution pi the walk holds: the current node's target row
 // (w == nullptr, invM = 1), or a stored residual w[0..V) of mass 1 / invM.
@@ -314,33 +321,41 @@ struct Pi {
   double invM;
 };
 
-// One workgroup per sequence, for chains and trees alike. Wavefront 0
-// validates the tree, computes for every node c its first test's p(t_c)
-// (under its parent's target row) and q_c(t_c), and the children of every
-// node as a bit mask. Every thread then runs the same walk from the LDS
-// copies: the current node's children are tested in id order; a rejection
-// followed by another sibling stores the residual max(0, pi - q_c) of the
-// whole row in one of two per-sequence buffers (a sweep by all threads, its
-// mass summed in a fixed order), and the next sibling is tested against it.
-// The final draw - from the last rejected sibling's residual (built on the
-// fly), or from pi itself - sweeps the row once in contiguous token-order
-// segments (16-token register blocks, next block's loads issued before the
-// current block's exponentials), scans the segment sums in a fixed order,
-// and re-sweeps only the segment whose running sum passes theta, one token
-// per lane of one wavefront.
+// K workgroups per sequence (K = 1 when the batch alone fills the chip),
+// each owning a contiguous slice of the vocabulary. Wavefront 0 of every
+// workgroup validates the tree, computes for every node c its first test's
+// p(t_c) (under its parent's target row) and q_c(t_c), and the children of
+// every node as a bit mask; all threads of all K workgroups then take the
+// same walk from these copies. The current node's children are tested in
+// id order; a rejection followed by another sibling stores the residual
+// max(0, pi - q_c) of the vocabulary (each workgroup its slice, in one of
+// two per-sequence rows) and the next sibling is tested against it. The
+// final draw - from the last rejected sibling's residual (built on the fly)
+// or from pi - sweeps the slices once in contiguous token-order segments
+// (16-token register blocks, next block's loads issued before the current
+// block's exponentials). Every sweep ends in an exchange: each workgroup
+// publishes its slice's mass, pi's old and new weight at the next sibling's
+// token, and its last positive token through device-scope atomics, counts
+// itself in, and waits (bounded) until all K have; sums are then taken in a
+// fixed order, so every workgroup reaches the same decisions. For the draw,
+// the first slice (then segment) whose running sum passes theta is found,
+// and only that segment is swept again, one token per lane of a wavefront.
 template <bool kVec>
 __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
     const int32_t *__restrict__ parents, const float *__restrict__ uniforms, int B, int N, int V, int chunks,
     double T, double invT, const double *__restrict__ stats, double *__restrict__ wbuf,
-    int32_t *__restrict__ accept_len, int32_t *__restrict__ path, int32_t *__restrict__ bonus,
-    unsigned long long *state) {
-  __shared__ int s_err, s_pick, s_lastpos, s_cross, s_cross_last;
-  __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total, s_cprefix;
+    unsigned long long *__restrict__ sync, int K, int slice, int32_t *__restrict__ accept_len,
+    int32_t *__restrict__ path, int32_t *__restrict__ bonus, unsigned long long *state) {
+  __shared__ int s_err, s_ok, s_pick, s_cross, s_cross_last, s_lp;
+  __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total, s_cprefix, s_wt_new, s_wt_old;
   __shared__ double s_pa[64], s_qa[64], s_u[64];
+  __shared__ RowStat s_tst[64], s_dst[64];  // merged statistics of every target and draft row
   __shared__ int s_tok[64], s_path[64];
   __shared__ unsigned long long s_child[64];
-  const int b = blockIdx.x;
+  __shared__ double s_part[kMaxGrid], s_xnew[kMaxGrid], s_xold[kMaxGrid];
+  __shared__ int s_xlp[kMaxGrid];
+  const int b = blockIdx.x / K, kk = blockIdx.x % K;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t base = static_cast<int64_t>(b) * N;
   if (wid == 0) {
@@ -360,13 +375,21 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const int err = __builtin_amdgcn_ballot_w64(tree_bad) ? TV_ERR_INVALID_TREE
                     : __builtin_amdgcn_ballot_w64(tok_bad) ? TV_ERR_INVALID_ARG
                                                            : 0;
-    if (!err && lane >= 1 && lane < N) {
-      s_tok[lane] = t;
-      if (p >= 0) {  // a node without a parent (forest) is never tested
-        const RowStat sp = merge_stats(stats, base + p, 0, chunks);
-        const RowStat sq = merge_stats(stats, base + lane, 1, chunks);
-        s_pa[lane] = prob_at(target + (base + p) * V, t, T, invT, sp);
-        s_qa[lane] = prob_at(draft + (base + lane) * V, t, T, invT, sq);
+    const bool live = !err && lane < N;
+    const RowStat st = live ? merge_stats(stats, base + lane, 0, chunks) : RowStat{0.0, 1.0, 1.0};
+    const RowStat sd = live && lane >= 1 ? merge_stats(stats, base + lane, 1, chunks) : RowStat{0.0, 1.0, 1.0};
+    // the parent's target statistics, from its lane
+    const int src = p >= 0 ? p : lane;
+    const RowStat sp{__shfl(st.m, src), __shfl(st.Z, src), __shfl(st.invZ, src)};
+    if (live) {
+      s_tst[lane] = st;
+      s_dst[lane] = sd;
+      if (lane >= 1) {
+        s_tok[lane] = t;
+        if (p >= 0) {  // a node without a parent (forest) is never tested
+          s_pa[lane] = prob_at(target + (base + p) * V, t, T, invT, sp);
+          s_qa[lane] = prob_at(draft + (base + lane) * V, t, T, invT, sd);
+        }
       }
     }
     for (int n = 0; n < N; ++n) {
@@ -376,24 +399,30 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     if (lane == 0) {
       s_err = err;
       s_pick = 0x7FFFFFFF;
-      s_lastpos = -1;
       s_cross = 0x7FFFFFFF;
+      s_lp = -1;
+      s_wt_new = 0.0;
+      s_wt_old = 0.0;
       s_path[0] = 0;
     }
   }
   __syncthreads();
   if (s_err) {
-    if (tid == 0) {
-      raise_error(state, s_err);
-      accept_len[b] = -1;
-      bonus[b] = -1;
+    if (kk == 0) {
+      if (tid == 0) {
+        raise_error(state, s_err);
+        accept_len[b] = -1;
+        bonus[b] = -1;
+      }
+      for (int i = tid; i < N; i += kPathThreads) path[base + i] = -1;
     }
-    for (int i = tid; i < N; i += kPathThreads) path[base + i] = -1;
     return;
   }
-  // contiguous segment per thread in token order, a multiple of 4 tokens
-  const int seg = ((V + 4 * kPathThreads - 1) / (4 * kPathThreads)) * 4;
-  const int x0 = min(tid * seg, V), x1 = min(x0 + seg, V);
+  // this workgroup's slice, split into contiguous per-thread segments
+  // (multiples of 4 tokens)
+  const int v0 = min(kk * slice, V), v1 = min(v0 + slice, V);
+  const int seg = ((v1 - v0 + 4 * kPathThreads - 1) / (4 * kPathThreads)) * 4;
+  const int x0 = min(v0 + tid * seg, v1), x1 = min(x0 + seg, v1);
   double *const buf0 = wbuf + static_cast<int64_t>(b) * 2 * V;
   double *const buf1 = buf0 + V;
 
@@ -418,18 +447,20 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) v[i] = xb + i < x1 ? w[xb + i] : 0.0;
   };
-  // weight of one token: pi's weight (the target row's probability, or the
-  // stored residual's entry), or, with a sibling's draft row, the residual
-  // max(0, pi - q) with pi normalised
-  auto weight = [&](const RowStat &sp, const Pi &pi, bool with_q, const RowStat &sq, float pl, double wl,
-                    float ql) __attribute__((always_inline)) {
-    const double w = pi.w ? wl : exp_fast(div_t(pl, T, invT) - sp.m) * sp.invZ;  // padding (-inf) gives 0
-    if (!with_q) return w;
+  // pi's weight of one token (the target row's probability, or the stored
+  // residual's entry)
+  auto base_weight = [&](const RowStat &sp, const Pi &pi, float pl, double wl) __attribute__((always_inline)) {
+    return pi.w ? wl : exp_fast(div_t(pl, T, invT) - sp.m) * sp.invZ;  // padding (-inf) gives 0
+  };
+  // with a sibling's draft row: the residual max(0, pi - q) with pi normalised
+  auto resid_weight = [&](double w, const Pi &pi, const RowStat &sq, float ql) __attribute__((always_inline)) {
     return fmax(0.0, w * pi.invM - exp_fast(div_t(ql, T, invT) - sq.m) * sq.invZ);
   };
-  // one sweep of this thread's segment; optionally stores every weight
+  // one sweep of this thread's segment; stores every weight into dst if
+  // given; the thread holding token tnext records pi's old and new weight
+  // there
   auto sweep = [&](const float *P, const RowStat &sp, const Pi &pi, const float *Q, const RowStat &sq, double *dst,
-                   double &local, int &lastpos) __attribute__((always_inline)) {
+                   int tnext, double &local, int &lastpos) __attribute__((always_inline)) {
     local = 0.0;
     lastpos = -1;
     float pv[kBlk], qv[kBlk], pn[kBlk], qn[kBlk];
@@ -449,10 +480,17 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       }
 #pragma unroll
       for (int i = 0; i < kBlk; ++i) {
-        const double w = weight(sp, pi, Q != nullptr, sq, pv[i], wv[i], qv[i]);
+        const double w0 = base_weight(sp, pi, pv[i], wv[i]);
+        const double w = Q ? resid_weight(w0, pi, sq, qv[i]) : w0;
         local += w;
         if (w > 0.0) lastpos = xb + i;
-        if (dst && xb + i < x1) dst[xb + i] = w;
+        if (xb + i < x1) {
+          if (dst) dst[xb + i] = w;
+          if (xb + i == tnext) {
+            s_wt_old = w0;
+            s_wt_new = w;
+          }
+        }
       }
 #pragma unroll
       for (int i = 0; i < kBlk; ++i) {
@@ -462,9 +500,10 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       }
     }
   };
-  // exclusive prefix of the segment sums and their total: a fixed-order
-  // scan within each wavefront, then over the wavefront totals in order
-  auto scan = [&](double local, double &prefix, double &total) __attribute__((always_inline)) {
+  // exclusive prefix of the segment sums within the workgroup and the
+  // workgroup's total: a fixed-order scan within each wavefront, then over
+  // the wavefront totals in order
+  auto scan = [&](double local, int lastpos, double &prefix) __attribute__((always_inline)) {
     double incl = local;
     for (int d = 1; d < 64; d <<= 1) {
       const double t = __shfl_up(incl, d);
@@ -473,6 +512,7 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     double excl = __shfl_up(incl, 1);
     if (lane == 0) excl = 0.0;
     if (lane == 63) s_wave[wid] = incl;
+    if (lastpos >= 0) atomicMax(&s_lp, lastpos);
     __syncthreads();
     if (tid == 0) {
       double run = 0.0;
@@ -484,22 +524,79 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     }
     __syncthreads();
     prefix = s_wpre[wid] + excl;
-    total = s_total;
+  };
+  // the exchange among the K workgroups of this sequence; fills s_part,
+  // s_xnew, s_xold, s_xlp with every slice's values (thread 0 publishes this
+  // workgroup's and resets the per-sweep records); false if a peer never
+  // arrived
+  int nx = 0;
+  auto exchange = [&]() __attribute__((always_inline)) {
+    if (K == 1) {
+      if (tid == 0) {
+        s_part[0] = s_total;
+        s_xnew[0] = s_wt_new;
+        s_xold[0] = s_wt_old;
+        s_xlp[0] = s_lp;
+        s_wt_new = 0.0;
+        s_wt_old = 0.0;
+        s_lp = -1;
+        s_ok = 1;
+      }
+    } else {
+      unsigned long long *cnt = sync + static_cast<int64_t>(b) * kCounterStride;
+      unsigned long long *slots = sync + static_cast<int64_t>(B) * kCounterStride +
+                                  (static_cast<int64_t>(nx) * kMaxGrid + static_cast<int64_t>(b) * K) * 4;
+      if (tid == 0) {
+        unsigned long long *mine = slots + kk * 4;
+        atomicExch(mine + 0, static_cast<unsigned long long>(__double_as_longlong(s_total)));
+        atomicExch(mine + 1, static_cast<unsigned long long>(__double_as_longlong(s_wt_new)));
+        atomicExch(mine + 2, static_cast<unsigned long long>(__double_as_longlong(s_wt_old)));
+        atomicExch(mine + 3, static_cast<unsigned long long>(static_cast<long long>(s_lp)));
+        s_wt_new = 0.0;
+        s_wt_old = 0.0;
+        s_lp = -1;
+        // the four values are in place before this workgroup is counted in
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        atomicAdd(cnt, 1ull);
+        const unsigned long long want = static_cast<unsigned long long>(K) * (nx + 1);
+        int ok = 0;
+        for (int it = 0; it < kSpinLimit; ++it) {
+          if (atomicAdd(cnt, 0ull) >= want) {
+            ok = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        s_ok = ok;
+      }
+      __syncthreads();
+      if (s_ok && tid < K) {
+        auto *theirs = slots + tid * 4;
+        s_part[tid] = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 0, 0ull)));
+        s_xnew[tid] = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 1, 0ull)));
+        s_xold[tid] = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 2, 0ull)));
+        s_xlp[tid] = static_cast<int>(static_cast<long long>(atomicAdd(theirs + 3, 0ull)));
+      }
+    }
+    ++nx;
     __syncthreads();
+    return s_ok != 0;
   };
 
-  // the walk; every thread takes the same decisions from the same data
+  // the walk; every thread of every workgroup takes the same decisions
   Pi pi{nullptr, 1.0};
+  double wt = 0.0;  // pi's (unnormalised) weight at the next sibling's token, when pi is stored
   int node = 0, k = 0, pend = -1;
+  bool ok = true;
   for (;;) {
     const float *P = target + (base + node) * V;
-    const RowStat sp = merge_stats(stats, base + node, 0, chunks);
+    const RowStat sp = s_tst[node];
     uint64_t kids = s_child[node];
     int acc = -1;
     while (kids) {
       const int c = __builtin_ctzll(kids);
       kids &= kids - 1;
-      const double a = pi.w ? (pi.w[s_tok[c]] * pi.invM) / s_qa[c] : s_pa[c] / s_qa[c];
+      const double a = pi.w ? (wt * pi.invM) / s_qa[c] : s_pa[c] / s_qa[c];
       if (s_u[c - 1] < a) {
         acc = c;
         break;
@@ -509,14 +606,26 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
         break;
       }
       double *dst = pi.w == buf0 ? buf1 : buf0;
-      const RowStat sq = merge_stats(stats, base + c, 1, chunks);
-      double local, prefix, total;
+      const RowStat sq = s_dst[c];
+      double local, prefix;
       int lastpos;
-      sweep(P, sp, pi, draft + (base + c) * V, sq, dst, local, lastpos);
-      scan(local, prefix, total);
-      if (total > 0.0) pi = Pi{dst, 1.0 / total};  // a residual of mass 0 leaves pi unchanged
+      sweep(P, sp, pi, draft + (base + c) * V, sq, dst, s_tok[__builtin_ctzll(kids)], local, lastpos);
+      scan(local, lastpos, prefix);
+      if (!(ok = exchange())) break;
+      double total = 0.0, wnew = 0.0, wold = 0.0;
+      for (int i = 0; i < K; ++i) {
+        total += s_part[i];
+        wnew += s_xnew[i];
+        wold += s_xold[i];
+      }
+      if (total > 0.0) {
+        pi = Pi{dst, 1.0 / total};
+        wt = wnew;
+      } else if (pi.w) {
+        wt = wold;  // a residual of mass 0 leaves pi unchanged
+      }
     }
-    if (acc < 0) break;
+    if (!ok || acc < 0) break;
     node = acc;
     ++k;
     if (tid == 0) s_path[k] = acc;
@@ -524,57 +633,93 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   }
 
   // the final draw
-  const float *P = target + (base + node) * V;
-  const float *Q = pend >= 0 ? draft + (base + pend) * V : nullptr;
-  const RowStat sp = merge_stats(stats, base + node, 0, chunks);
-  const RowStat sq = Q ? merge_stats(stats, base + pend, 1, chunks) : RowStat{0.0, 1.0, 1.0};
-  const double u = s_u[N - 1];
-  for (int pass = 0; pass < 2; ++pass) {
-    const float *Qp = pass == 0 ? Q : nullptr;
-    double local, prefix, total;
-    int lastpos;
-    sweep(P, sp, pi, Qp, sq, nullptr, local, lastpos);
-    scan(local, prefix, total);
-    if (Qp && !(total > 0.0)) continue;  // no residual mass: draw from pi instead
-    const double theta = u * total;
-    // the first segment whose running sum passes theta holds the draw
-    if (prefix + local > theta) atomicMin(&s_cross, tid);
-    if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
-    __syncthreads();
-    if (tid == s_cross) {
-      s_cprefix = prefix;
-      s_cross_last = lastpos;
-    }
-    __syncthreads();
-    // wavefront 0 re-sweeps the crossing segment one token per lane: a
-    // fixed-order scan of the weights gives each token's running sum
-    const int cross = s_cross;
-    if (wid == 0 && cross != 0x7FFFFFFF) {
-      const int cx0 = min(cross * seg, V), cx1 = min(cx0 + seg, V);
-      double carry = s_cprefix;
-      int pick = -1;
-      for (int xb = cx0; xb < cx1 && pick < 0; xb += 64) {
-        const int x = xb + lane;
-        double w = 0.0;
-        if (x < cx1)
-          w = weight(sp, pi, Qp != nullptr, sq, pi.w ? 0.f : P[x], pi.w ? pi.w[x] : 0.0, Qp ? Qp[x] : 0.f);
-        double run = w;
-        for (int d = 1; d < 64; d <<= 1) {
-          const double t = __shfl_up(run, d);
-          if (lane >= d) run += t;
-        }
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(x < cx1 && carry + run > theta);
-        if (hit) pick = xb + __builtin_ctzll(hit);
-        carry += __shfl(run, 63);
+  int writer = 0, pick = -1;
+  if (ok) {
+    const float *P = target + (base + node) * V;
+    const float *Q = pend >= 0 ? draft + (base + pend) * V : nullptr;
+    const RowStat sp = s_tst[node];
+    const RowStat sq = Q ? s_dst[pend] : RowStat{0.0, 1.0, 1.0};
+    const double u = s_u[N - 1];
+    for (int pass = 0; pass < 2; ++pass) {
+      const float *Qp = pass == 0 ? Q : nullptr;
+      double local, prefix;
+      int lastpos;
+      sweep(P, sp, pi, Qp, sq, nullptr, -1, local, lastpos);
+      scan(local, lastpos, prefix);
+      if (!(ok = exchange())) break;
+      double total = 0.0;
+      int glast = -1;
+      for (int i = 0; i < K; ++i) {
+        total += s_part[i];
+        glast = max(glast, s_xlp[i]);
       }
-      const int pk = pick >= 0 ? pick : s_cross_last;  // rounding left no crossing: last positive token
-      if (lane == 0 && pk >= 0) s_pick = pk;
+      if (Qp && !(total > 0.0)) continue;  // no residual mass: draw from pi instead
+      const double theta = u * total;
+      // the first slice whose running sum passes theta holds the draw
+      int cross_wg = -1;
+      double wg_prefix = 0.0, run = 0.0;
+      for (int i = 0; i < K; ++i) {
+        if (cross_wg < 0 && run + s_part[i] > theta) {
+          cross_wg = i;
+          wg_prefix = run;
+        }
+        run += s_part[i];
+      }
+      writer = cross_wg >= 0 ? cross_wg : 0;
+      pick = glast;  // rounding left no crossing: the last token of positive weight
+      if (cross_wg == kk) {
+        // the first segment of this slice whose running sum passes theta
+        const double pre = wg_prefix + prefix;
+        if (pre + local > theta) atomicMin(&s_cross, tid);
+        __syncthreads();
+        if (tid == s_cross) {
+          s_cprefix = pre;
+          s_cross_last = lastpos;
+        }
+        __syncthreads();
+        // wavefront 0 re-sweeps the crossing segment one token per lane: a
+        // fixed-order scan of the weights gives each token's running sum
+        const int cross = s_cross;
+        if (wid == 0 && cross != 0x7FFFFFFF) {
+          const int cx0 = min(v0 + cross * seg, v1), cx1 = min(cx0 + seg, v1);
+          double carry = s_cprefix;
+          int found = -1;
+          for (int xb = cx0; xb < cx1 && found < 0; xb += 64) {
+            const int x = xb + lane;
+            double w = 0.0;
+            if (x < cx1) {
+              w = base_weight(sp, pi, pi.w ? 0.f : P[x], pi.w ? pi.w[x] : 0.0);
+              if (Qp) w = resid_weight(w, pi, sq, Qp[x]);
+            }
+            double rs = w;
+            for (int d = 1; d < 64; d <<= 1) {
+              const double t = __shfl_up(rs, d);
+              if (lane >= d) rs += t;
+            }
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(x < cx1 && carry + rs > theta);
+            if (hit) found = xb + __builtin_ctzll(hit);
+            carry += __shfl(rs, 63);
+          }
+          const int pk = found >= 0 ? found : s_cross_last;  // no crossing after rounding: segment's last positive
+          if (lane == 0 && pk >= 0) s_pick = pk;
+        }
+        __syncthreads();
+        if (s_pick != 0x7FFFFFFF) pick = s_pick;
+      }
+      break;
     }
-    __syncthreads();
-    break;
+  }
+  if (kk != writer) return;
+  if (!ok) {  // a peer workgroup never arrived (not co-resident): report and give up
+    if (tid == 0) {
+      raise_error(state, TV_ERR_HIP);
+      accept_len[b] = -1;
+      bonus[b] = -1;
+    }
+    for (int i = tid; i < N; i += kPathThreads) path[base + i] = -1;
+    return;
   }
   if (tid == 0) {
-    const int pick = s_pick != 0x7FFFFFFF ? s_pick : s_lastpos;
     accept_len[b] = k + 1;
     bonus[b] = pick;
     atomicAdd(state + 0, static_cast<unsigned long long>(k + 1));
@@ -586,7 +731,9 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
 }  // namespace
 
 // stochastic: the chunk statistics, then (256-byte aligned) two residual
-// buffers of V doubles per sequence
+// rows of V doubles per sequence, then the path pass's exchange area (one
+// counter line per sequence, slots for every exchange of up to kMaxGrid
+// workgroups)
 size_t stats_doubles(int B, int N, int V) {
   const int chunks = (V + kChunk - 1) / kChunk;
   return ((static_cast<size_t>(B) * N * 2 * chunks * 2 + 31) / 32) * 32;
@@ -596,7 +743,9 @@ size_t accept_ws_bytes(int B, int N, int V, tv_accept_mode mode) {
   const int chunks = (V + kChunk - 1) / kChunk;
   const size_t rows = static_cast<size_t>(B) * N;
   if (mode == TV_GREEDY) return rows * chunks * sizeof(unsigned long long);
-  return (stats_doubles(B, N, V) + static_cast<size_t>(B) * 2 * V) * sizeof(double);
+  const size_t sync = static_cast<size_t>(B) * kCounterStride + static_cast<size_t>(kMaxExchanges) * kMaxGrid * 4;
+  return (stats_doubles(B, N, V) + static_cast<size_t>(B) * 2 * V) * sizeof(double) +
+         sync * sizeof(unsigned long long);
 }
 
 tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits,
@@ -621,24 +770,46 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
   }
   auto *stats = static_cast<double *>(workspace);
   double *wbuf = stats + stats_doubles(B, N, V);
+  auto *sync = reinterpret_cast<unsigned long long *>(wbuf + static_cast<size_t>(B) * 2 * V);
   const double T = static_cast<double>(temperature), invT = 1.0 / T;
+  // workgroups per sequence for the path pass: enough to fill the chip when
+  // the batch is small, all co-resident (cooperative launch), each with a
+  // slice of at most about 4096 tokens (8 per thread)
+  const void *path_fn = vec ? reinterpret_cast<const void *>(stochastic_path_kernel<true>)
+                            : reinterpret_cast<const void *>(stochastic_path_kernel<false>);
+  int K = 1;
+  if (B <= kMaxGrid && V >= 2 * 4096) {
+    if (ctx->path_blocks_per_cu == 0) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, path_fn, kPathThreads, 0) != hipSuccess || nb < 1) nb = -1;
+      ctx->path_blocks_per_cu = nb;
+    }
+    if (ctx->path_blocks_per_cu > 0) {
+      // splitting pays only when it gives each sequence several workgroups
+      const int cap = min(kMaxGrid, ctx->path_blocks_per_cu * ctx->cu_count);
+      if (cap / B >= 4) K = max(1, min(min(cap / B, (V + 4095) / 4096), 64));
+    }
+  }
+  const int slice = (((V + K - 1) / K) + 3) / 4 * 4;
   const dim3 g1(chunks, B * N, 2);
+  unsigned long long *counters = K > 1 ? sync : nullptr;
   if (vec)
     hipLaunchKernelGGL(softmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
-                       chunks, T, invT, stats);
+                       chunks, T, invT, stats, counters);
   else
     hipLaunchKernelGGL(softmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
-                       chunks, T, invT, stats);
+                       chunks, T, invT, stats, counters);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  if (vec)
-    hipLaunchKernelGGL(stochastic_path_kernel<true>, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
-                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, wbuf,
-                       accept_len, path, bonus, ctx->d_state);
-  else
-    hipLaunchKernelGGL(stochastic_path_kernel<false>, dim3(B), dim3(kPathThreads), 0, ctx->stream, target_logits,
-                       draft_logits, draft_tokens, parents, uniforms, B, N, V, chunks, T, invT, stats, wbuf,
-                       accept_len, path, bonus, ctx->d_state);
-  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+  unsigned long long *st = ctx->d_state;
+  void *args[] = {const_cast<float **>(&target_logits), const_cast<float **>(&draft_logits),
+                  const_cast<int32_t **>(&draft_tokens), const_cast<int32_t **>(&parents),
+                  const_cast<float **>(&uniforms), &B, &N, &V, const_cast<int *>(&chunks),
+                  const_cast<double *>(&T), const_cast<double *>(&invT), &stats, &wbuf, &sync, &K,
+                  const_cast<int *>(&slice), &accept_len, &path, &bonus, &st};
+  const hipError_t e = K > 1 ? hipLaunchCooperativeKernel(path_fn, dim3(B * K), dim3(kPathThreads), args, 0,
+                                                          ctx->stream)
+                             : hipLaunchKernel(path_fn, dim3(B), dim3(kPathThreads), args, 0, ctx->stream);
+  return e == hipSuccess && hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
 }  // namespace tv

@@ -12,6 +12,9 @@ struct tv_ctx {
   int cu_count;
   // d_state[0] = tau sum, d_state[1] = tau cycles, d_state[2] low 32 bits = sticky error code
   unsigned long long *d_state;
+  // resident workgroups per CU of the stochastic path pass (0 = not yet
+  // queried, -1 = query failed)
+  int path_blocks_per_cu;
 };
 
 namespace tv {
