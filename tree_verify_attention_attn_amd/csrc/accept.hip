@@ -26,7 +26,7 @@
 //           by the normalised residual max(0, pi - q_c) for the next sibling.
 //           The next token is one inverse-CDF draw from the final pi (or the
 //           last rejected sibling's residual) with theta = u[N-1] * mass.
-//   Every exponential is fp64 (exp_fast, within a few ulp), so a decision
+//   Every exponential is fp64 (exp_tab, within a few ulp), so a decision
 //   agrees with exact arithmetic whenever its margin exceeds ~1e-15.
 #include <math.h>
 
@@ -214,6 +214,31 @@ __device__ inline double exp_fast(double x) {
   return ldexp(p, static_cast<int>(k));
 }
 
+// e^x with a finer reduction, for the per-token work: x = (64 n + j) ln2/64
+// + r with |r| <= ln2/128, e^x = 2^n * 2^(j/64) * e^r, the 64 values
+// 2^(j/64) from a table the workgroup fills once (exp_table_init, exp_fast of
+// j ln2/64), e^r from its Taylor series to degree 5 (truncation below 4e-17
+// relative). Within a few ulp of e^x (2 ulp worst over 2e7 sampled
+// arguments in [-700, 0]); arguments below -745.2 give 0.
+__device__ inline void exp_table_init(double *tab, int tid) {
+  if (tid < 64) tab[tid] = exp_fast(tid * (kLn2Hi / 64.0) + tid * (kLn2Lo / 64.0));
+}
+
+__device__ inline double exp_tab(double x, const double *tab) {
+  if (!(x > -745.2)) return 0.0;
+  const double k = rint(x * (kLog2eD * 64.0));
+  double r = fma(-k, kLn2Hi / 64.0, x);  // exact: k has at most 17 bits, the head 32
+  r = fma(-k, kLn2Lo / 64.0, r);
+  const int ki = static_cast<int>(k);
+  double p = 1.0 / 120.0;
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(tab[ki & 63] * p, ki >> 6);
+}
+
 // x / T in fp64 from a precomputed 1/T and one FMA correction step (exact
 // when T = 1)
 __device__ inline double div_t(double x, double T, double invT) {
@@ -245,38 +270,43 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
   const float *p = (which ? draft : target) + row * V;
   const int x0 = chunk * kChunk;
   const int x1 = min(x0 + kChunk, V);
-  constexpr int kPer = kChunk / kThreads;  // 32 values per thread, kept in registers
-  double z[kPer];
+  constexpr int kPer = kChunk / kThreads;  // 32 logits per thread, kept in registers as fp32
+  float v[kPer];
   if (kVec) {
 #pragma unroll
     for (int it = 0; it < kPer / 4; ++it) {
       const int x = x0 + (it * kThreads + threadIdx.x) * 4;
-      float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (x < x1) v = *reinterpret_cast<const float4 *>(p + x);
-      z[it * 4 + 0] = div_t(v.x, T, invT);
-      z[it * 4 + 1] = div_t(v.y, T, invT);
-      z[it * 4 + 2] = div_t(v.z, T, invT);
-      z[it * 4 + 3] = div_t(v.w, T, invT);
+      float4 f = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (x < x1) f = *reinterpret_cast<const float4 *>(p + x);
+      v[it * 4 + 0] = f.x;
+      v[it * 4 + 1] = f.y;
+      v[it * 4 + 2] = f.z;
+      v[it * 4 + 3] = f.w;
     }
   } else {
 #pragma unroll
     for (int it = 0; it < kPer; ++it) {
       const int x = x0 + it * kThreads + threadIdx.x;
-      z[it] = x < x1 ? div_t(p[x], T, invT) : -INFINITY;
+      v[it] = x < x1 ? p[x] : -INFINITY;
     }
   }
-  double mx = -INFINITY;
+  // x -> x / T is monotonic, so the maximum of the scaled logits is the
+  // scaled maximum logit (found in fp32)
+  float mf = -INFINITY;
 #pragma unroll
-  for (int it = 0; it < kPer; ++it) mx = fmax(mx, z[it]);
-  for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  for (int it = 0; it < kPer; ++it) mf = fmaxf(mf, v[it]);
+  for (int m = 32; m >= 1; m >>= 1) mf = fmaxf(mf, __shfl_xor(mf, m));
+  __shared__ float redf[kThreads / 64];
+  __shared__ double s_tab[64];
+  exp_table_init(s_tab, threadIdx.x);
+  if ((threadIdx.x & 63) == 0) redf[threadIdx.x >> 6] = mf;
   __syncthreads();
-  mx = red[0];
-  for (int i = 1; i < kThreads / 64; ++i) mx = fmax(mx, red[i]);
-  __syncthreads();
+  mf = redf[0];
+  for (int i = 1; i < kThreads / 64; ++i) mf = fmaxf(mf, redf[i]);
+  const double mx = div_t(mf, T, invT);
   double zs = 0.0;
-#pragma unroll
-  for (int it = 0; it < kPer; ++it) zs += exp_fast(z[it] - mx);  // -inf (padding) gives 0
+#pragma unroll 8
+  for (int it = 0; it < kPer; ++it) zs += exp_tab(div_t(v[it], T, invT) - mx, s_tab);  // -inf (padding) gives 0
   for (int m = 32; m >= 1; m >>= 1) zs += __shfl_xor(zs, m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = zs;
   __syncthreads();
@@ -292,19 +322,20 @@ struct RowStat {
   double m, Z, invZ;
 };
 
-__device__ inline RowStat merge_stats(const double *stats, int64_t row, int which, int chunks) {
+__device__ inline RowStat merge_stats(const double *stats, int64_t row, int which, int chunks, const double *tab) {
   const double *s = stats + (row * 2 + which) * chunks * 2;
   double M = -INFINITY;
   for (int c = 0; c < chunks; ++c) M = fmax(M, s[2 * c]);
   double Z = 0.0;
   for (int c = 0; c < chunks; ++c) {
-    if (s[2 * c + 1] > 0.0) Z += s[2 * c + 1] * exp_fast(s[2 * c] - M);
+    if (s[2 * c + 1] > 0.0) Z += s[2 * c + 1] * exp_tab(s[2 * c] - M, tab);
   }
   return RowStat{M, Z, 1.0 / Z};
 }
 
-__device__ inline double prob_at(const float *row, int x, double T, double invT, const RowStat &st) {
-  return exp_fast(div_t(row[x], T, invT) - st.m) * st.invZ;
+__device__ inline double prob_at(const float *row, int x, double T, double invT, const RowStat &st,
+                                const double *tab) {
+  return exp_tab(div_t(row[x], T, invT) - st.m, tab) * st.invZ;
 }
 
 constexpr int kPathThreads = 512;
@@ -355,10 +386,12 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   __shared__ unsigned long long s_child[64];
   __shared__ double s_part[kMaxGrid], s_xnew[kMaxGrid], s_xold[kMaxGrid];
   __shared__ int s_xlp[kMaxGrid];
+  __shared__ double s_tab[64];
   const int b = blockIdx.x / K, kk = blockIdx.x % K;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t base = static_cast<int64_t>(b) * N;
   if (wid == 0) {
+    exp_table_init(s_tab, lane);  // wavefront 0 fills it and uses it first
     // validation with the same precedence as a serial check: a bad parent
     // anywhere, then a draft token outside [0, V)
     bool tree_bad = false, tok_bad = false;
@@ -376,8 +409,9 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
                     : __builtin_amdgcn_ballot_w64(tok_bad) ? TV_ERR_INVALID_ARG
                                                            : 0;
     const bool live = !err && lane < N;
-    const RowStat st = live ? merge_stats(stats, base + lane, 0, chunks) : RowStat{0.0, 1.0, 1.0};
-    const RowStat sd = live && lane >= 1 ? merge_stats(stats, base + lane, 1, chunks) : RowStat{0.0, 1.0, 1.0};
+    const RowStat st = live ? merge_stats(stats, base + lane, 0, chunks, s_tab) : RowStat{0.0, 1.0, 1.0};
+    const RowStat sd =
+        live && lane >= 1 ? merge_stats(stats, base + lane, 1, chunks, s_tab) : RowStat{0.0, 1.0, 1.0};
     // the parent's target statistics, from its lane
     const int src = p >= 0 ? p : lane;
     const RowStat sp{__shfl(st.m, src), __shfl(st.Z, src), __shfl(st.invZ, src)};
@@ -387,8 +421,8 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       if (lane >= 1) {
         s_tok[lane] = t;
         if (p >= 0) {  // a node without a parent (forest) is never tested
-          s_pa[lane] = prob_at(target + (base + p) * V, t, T, invT, sp);
-          s_qa[lane] = prob_at(draft + (base + lane) * V, t, T, invT, sd);
+          s_pa[lane] = prob_at(target + (base + p) * V, t, T, invT, sp, s_tab);
+          s_qa[lane] = prob_at(draft + (base + lane) * V, t, T, invT, sd, s_tab);
         }
       }
     }
@@ -450,11 +484,11 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   // pi's weight of one token (the target row's probability, or the stored
   // residual's entry)
   auto base_weight = [&](const RowStat &sp, const Pi &pi, float pl, double wl) __attribute__((always_inline)) {
-    return pi.w ? wl : exp_fast(div_t(pl, T, invT) - sp.m) * sp.invZ;  // padding (-inf) gives 0
+    return pi.w ? wl : exp_tab(div_t(pl, T, invT) - sp.m, s_tab) * sp.invZ;  // padding (-inf) gives 0
   };
   // with a sibling's draft row: the residual max(0, pi - q) with pi normalised
   auto resid_weight = [&](double w, const Pi &pi, const RowStat &sq, float ql) __attribute__((always_inline)) {
-    return fmax(0.0, w * pi.invM - exp_fast(div_t(ql, T, invT) - sq.m) * sq.invZ);
+    return fmax(0.0, w * pi.invM - exp_tab(div_t(ql, T, invT) - sq.m, s_tab) * sq.invZ);
   };
   // one sweep of this thread's segment; stores every weight into dst if
   // given; the thread holding token tnext records pi's old and new weight
