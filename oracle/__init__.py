@@ -47,9 +47,11 @@ def _load():
         lib.tvo_accept_greedy.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, c_int]
         lib.tvo_accept_stochastic.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, c_int]
         lib.tvo_commit.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+        lib.tvo_build_tree.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
         lib.tvo_tau.argtypes = [vp, i64]
         lib.tvo_tau.restype = ctypes.c_double
-        for f in ("tvo_build_mask", "tvo_attention", "tvo_accept_greedy", "tvo_accept_stochastic", "tvo_commit"):
+        for f in ("tvo_build_mask", "tvo_attention", "tvo_accept_greedy", "tvo_accept_stochastic", "tvo_commit",
+                  "tvo_build_tree"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -216,3 +218,28 @@ def commit(w, path, accept_len, bonus):
     if st != OK:
         raise OracleError(st, "commit")
     return k, v, r
+
+
+def status_build_tree(root_tokens, cand_tokens, cand_probs, *, k_root, threshold, max_depth, B=None, N=None, k=None):
+    """Returns (status, dict(parents, tokens, depth, mask, scores, n_nodes))."""
+    cand_tokens = _c(cand_tokens, np.int32)
+    cand_probs = _c(cand_probs, np.float32)
+    root_tokens = _c(root_tokens, np.int32)
+    B = cand_tokens.shape[0] if B is None else B
+    N = cand_tokens.shape[1] if N is None else N
+    k = cand_tokens.shape[2] if k is None else k
+    shp = (max(B, 0), max(N, 0))
+    out = dict(parents=np.full(shp, -2, np.int32), tokens=np.full(shp, -2, np.int32), depth=np.full(shp, -2, np.int32),
+               mask=np.zeros(shp, np.uint64), scores=np.full(shp, np.nan), n_nodes=np.full(shp[0], -2, np.int32))
+    st = _load().tvo_build_tree(_p(root_tokens), _p(cand_tokens), _p(cand_probs), B, N, k, k_root,
+                                np.float32(threshold), max_depth, _p(out["parents"]), _p(out["tokens"]),
+                                _p(out["depth"]), _p(out["mask"]), _p(out["scores"]), _p(out["n_nodes"]))
+    return st, out
+
+
+def build_tree(root_tokens, cand_tokens, cand_probs, *, k_root, threshold, max_depth):
+    st, out = status_build_tree(root_tokens, cand_tokens, cand_probs, k_root=k_root, threshold=threshold,
+                                max_depth=max_depth)
+    if st != OK:
+        raise OracleError(st, "build_tree")
+    return out

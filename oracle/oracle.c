@@ -662,3 +662,89 @@ int tvo_commit(uint16_t *k_pages, uint16_t *v_pages, int64_t num_pages, const in
   free(tmp);
   return status;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic draft-tree construction ([EAGLE-2 page], the dynamic-tree        */
+/* algorithm section and its reference code's tree builder).                */
+/*                                                                          */
+/* A node's cumulative score is the product of the draft probabilities on   */
+/* its root path (root = 1). The candidate queue starts with the root's     */
+/* top-k_root proposals; repeatedly the candidate with the highest score is */
+/* made the next node (ids in creation order; ties go to the candidate      */
+/* queued first); a node shallower than max_depth then proposes its top-k   */
+/* children, and a child is queued only if its cumulative score is above    */
+/* the threshold (the reference code's strict test; the prose says "at or  */
+/* above"). Construction stops at N nodes (root included) or when the      */
+/* queue is empty. Proposal row i of a sequence is what the draft head      */
+/* proposes for the node created i-th (row 0: the root); scores are fp64    */
+/* products of the fp32 probabilities. Unused slots of a short tree are     */
+/* padding: parent -1, the root's token, depth 0, mask = the slot itself,   */
+/* score 0. A probability that is NaN or negative makes that sequence all   */
+/* padding with n_nodes = 0 and the call return TVO_ERR_INVALID_ARG.        */
+/* ------------------------------------------------------------------------ */
+
+int tvo_build_tree(const int32_t *root_tokens, const int32_t *cand_tokens, const float *cand_probs, int32_t B,
+                   int32_t N, int32_t k, int32_t k_root, float threshold, int32_t max_depth, int32_t *parents,
+                   int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores, int32_t *n_nodes) {
+  if (B < 0 || N < 1 || N > 64 || k < 1 || k > 32 || k_root < 1 || k_root > k || max_depth < 1 ||
+      !(threshold == threshold))
+    return TVO_ERR_INVALID_ARG;
+  if (B == 0) return TVO_OK;
+  if (!root_tokens || !cand_tokens || !cand_probs || !parents || !tokens) return TVO_ERR_INVALID_ARG;
+  const int64_t cap = (int64_t)k_root + (int64_t)(N - 1) * k;
+  double *qs = (double *)malloc(sizeof(double) * cap);
+  int32_t *qp = (int32_t *)malloc(sizeof(int32_t) * cap), *qt = (int32_t *)malloc(sizeof(int32_t) * cap);
+  char *alive = (char *)malloc(cap);
+  if (!qs || !qp || !qt || !alive) {
+    free(qs), free(qp), free(qt), free(alive);
+    return TVO_ERR_RUNTIME;
+  }
+  int status = TVO_OK;
+  for (int64_t b = 0; b < B; ++b) {
+    const int32_t *ct = cand_tokens + b * N * k;
+    const float *cp = cand_probs + b * N * k;
+    int32_t *pa = parents + b * N, *tk = tokens + b * N;
+    double sc[64];
+    int32_t dp[64];
+    int bad = 0;
+    for (int64_t j = 0; j < (int64_t)N * k; ++j)
+      if (!(cp[j] >= 0.0f)) bad = 1; /* NaN or negative */
+    int32_t n = 0;
+    if (!bad) {
+      int64_t q = 0;
+      pa[0] = -1, tk[0] = root_tokens[b], dp[0] = 0, sc[0] = 1.0, n = 1;
+      for (int32_t s = 0; s < k_root; ++s) { /* the root's proposals are queued unconditionally */
+        qs[q] = sc[0] * (double)cp[s], qp[q] = 0, qt[q] = ct[s], alive[q] = 1, ++q;
+      }
+      while (n < N) {
+        int64_t best = -1;
+        for (int64_t j = 0; j < q; ++j) /* strict '>' keeps the earliest queued among equal scores */
+          if (alive[j] && (best < 0 || qs[j] > qs[best])) best = j;
+        if (best < 0) break;
+        alive[best] = 0;
+        const int32_t id = n++;
+        pa[id] = qp[best], tk[id] = qt[best], dp[id] = dp[qp[best]] + 1, sc[id] = qs[best];
+        if (dp[id] < max_depth)
+          for (int32_t s = 0; s < k; ++s) {
+            const double c = sc[id] * (double)cp[(int64_t)id * k + s];
+            if (c > (double)threshold) qs[q] = c, qp[q] = id, qt[q] = ct[(int64_t)id * k + s], alive[q] = 1, ++q;
+          }
+      }
+    } else {
+      status = TVO_ERR_INVALID_ARG;
+    }
+    for (int32_t i = n; i < N; ++i) pa[i] = -1, tk[i] = root_tokens[b], dp[i] = 0, sc[i] = 0.0;
+    for (int32_t i = 0; i < N; ++i) {
+      if (depth) depth[b * N + i] = dp[i];
+      if (scores) scores[b * N + i] = sc[i];
+      if (mask) { /* the node and every ancestor */
+        uint64_t m = 0;
+        for (int32_t c = i; c >= 0; c = pa[c]) m |= 1ull << c;
+        mask[b * N + i] = m;
+      }
+    }
+    if (n_nodes) n_nodes[b] = n;
+  }
+  free(qs), free(qp), free(qt), free(alive);
+  return status;
+}

@@ -74,6 +74,17 @@ int tvo_commit(uint16_t *k_pages, uint16_t *v_pages, int64_t num_pages, const in
                const int32_t *path, const int32_t *accept_len, const int32_t *bonus, int32_t B, int32_t N,
                int32_t Hkv, int32_t D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root);
 
+/* Dynamic draft-tree construction (EAGLE-2 page, dynamic-tree algorithm and
+ * its reference code): best-first by cumulative score from the root's
+ * top-k_root proposals; a created node shallower than max_depth queues its
+ * top-k children whose cumulative score is > threshold; N nodes at most.
+ * cand_tokens / cand_probs [B][N][k]: row i = proposals of the node created
+ * i-th. Outputs [B][N] (depth, mask, scores, n_nodes nullable); unused slots
+ * are padding (parent -1, root token, depth 0, self mask, score 0). */
+int tvo_build_tree(const int32_t *root_tokens, const int32_t *cand_tokens, const float *cand_probs, int32_t B,
+                   int32_t N, int32_t k, int32_t k_root, float threshold, int32_t max_depth, int32_t *parents,
+                   int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores, int32_t *n_nodes);
+
 /* tau = (1/M) sum_j n_accepted(j) over M verification cycles (EAGLE-3 page,
  * tree acceptance rate definition); 0 when M = 0. */
 double tvo_tau(const int32_t *accept_len, int64_t M);

@@ -204,12 +204,13 @@ def random_tree(seed: int, tid: int, N: int, max_depth: int) -> np.ndarray:
     return parents
 
 
-def dynamic_tree(seed: int, tid: int, N: int, max_depth: int, topk: int, V: int):
+def dynamic_tree(seed: int, tid: int, N: int, max_depth: int, topk: int, V: int, record: Optional[dict] = None):
     """Best-first expansion by cumulative score, as in the EAGLE-2 page's
     dynamic-tree algorithm (no pruning threshold, budget N including the root).
 
     Returns (parents int32[N], tokens int32[N]); tokens[0] is the root token.
-    Sibling tokens are distinct (drawn without replacement).
+    Sibling tokens are distinct (drawn without replacement). If `record` is a
+    dict, record[node] = (tokens, probabilities) of every node's proposals.
     """
     s = Stream(seed, tid)
     zs = NormalStream(seed, tid + (1 << 20), sigma=math.sqrt(2.0))
@@ -232,6 +233,8 @@ def dynamic_tree(seed: int, tid: int, N: int, max_depth: int, topk: int, V: int)
             t = s.randint(V)
             if t not in toks:
                 toks.append(t)
+        if record is not None:
+            record[node] = (list(toks), sc.copy())
         for k in range(topk):
             heapq.heappush(heap, (-(cum[node] * sc[k]), seq, node, toks[k]))
             seq += 1
