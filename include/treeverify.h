@@ -85,6 +85,38 @@ tv_status tv_set_stream(tv_ctx *ctx, void *hip_stream);
 tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, int32_t B, int32_t N, uint64_t *mask,
                         int32_t *depth);
 
+/* Dynamic draft-tree construction ([EAGLE-2 page], dynamic-tree algorithm
+ * section and its reference code's builder). A node's cumulative score is the
+ * product of the draft probabilities on its root path (root = 1). The queue
+ * starts with the root's first k_root proposals (queued whatever their
+ * score); repeatedly the queued candidate with the highest score becomes the
+ * next node (ids in creation order, so parents come first; on equal scores
+ * the candidate queued first); a node whose depth is below max_depth then
+ * queues those of its k proposals whose cumulative score is > threshold (the
+ * reference code's strict test), in slot order. Construction stops at N
+ * nodes (root included) or when the queue is empty.
+ *   root_tokens  int32 [B]: node 0's token (the last verified token)
+ *   cand_tokens  int32 [B][N][k], cand_probs fp32 [B][N][k]: row i holds the
+ *                draft head's top-k proposals (token, probability) for the
+ *                node created i-th (row 0: the root); rows of nodes that are
+ *                never created or never expanded are not read for scores
+ *   threshold    fp32, compared in fp64 with the fp64 product of fp32 scores
+ *   parents, tokens  int32 [B][N]: the tree, in the layout tv_build_mask,
+ *                tv_attention and tv_accept take
+ *   depth int32 [B][N], mask uint64 [B][N][1] (ancestor-or-self bits as
+ *                tv_build_mask writes them), scores fp64 [B][N] (cumulative),
+ *                n_nodes int32 [B]: all nullable
+ * Slots past n_nodes of a short tree are padding: parent -1, the root's
+ * token, depth 0, mask = the slot's own bit, score 0 (never accepted).
+ * Requires 1 <= N <= 64, 1 <= k_root <= k <= 32, max_depth >= 1, threshold
+ * not NaN. A sequence with a NaN or negative probability anywhere in its
+ * table is written as padding with n_nodes 0 and sets the sticky
+ * TV_ERR_INVALID_ARG. */
+tv_status tv_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *cand_tokens, const float *cand_probs,
+                        int32_t B, int32_t N, int32_t k, int32_t k_root, float threshold, int32_t max_depth,
+                        int32_t *parents, int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores,
+                        int32_t *n_nodes);
+
 /* Workspace (bytes) tv_attention needs for these host scalars: fp32 partial
  * results when one sequence's keys are split over several workgroups. The
  * split plan depends only on these arguments and the device's CU count, so

@@ -20,7 +20,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = tv.library()
     names = declared_functions()
-    assert {"tv_create", "tv_build_mask", "tv_attention", "tv_accept", "tv_commit", "tv_tau"} <= names
+    assert {"tv_create", "tv_build_mask", "tv_attention", "tv_accept", "tv_commit", "tv_build_tree", "tv_tau"} <= names
     missing = [n for n in sorted(names) if not hasattr(lib, n)]
     assert not missing, missing
 

@@ -57,6 +57,7 @@ def _load():
         lib.tv_accept_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
         lib.tv_accept_workspace_bytes.restype = sz
         lib.tv_accept.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, f32, vp, vp, vp, vp, vp, sz]
+        lib.tv_build_tree.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
         lib.tv_commit.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         lib.tv_tau.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]
         lib.tv_tau_reset.argtypes = [vp]
@@ -64,7 +65,7 @@ def _load():
         lib.tv_status_string.argtypes = [ctypes.c_int]
         lib.tv_status_string.restype = ctypes.c_char_p
         for f in ("tv_create", "tv_destroy", "tv_set_stream", "tv_build_mask", "tv_attention", "tv_accept",
-                  "tv_commit", "tv_tau", "tv_tau_reset", "tv_device_error"):
+                  "tv_commit", "tv_build_tree", "tv_tau", "tv_tau_reset", "tv_device_error"):
             getattr(lib, f).restype = st
         _lib = lib
     return _lib
@@ -117,6 +118,29 @@ def tv_build_mask(parents: torch.Tensor, mask: Optional[torch.Tensor] = None, de
     assert parents.dtype == torch.int32
     _check(_load().tv_build_mask(_ctx(dev), _ptr(parents), B, N, _ptr(mask), _ptr(depth)), "tv_build_mask")
     return mask, depth
+
+
+def tv_build_tree(root_tokens: torch.Tensor, cand_tokens: torch.Tensor, cand_probs: torch.Tensor, k_root: int,
+                  threshold: float, max_depth: int, outputs: Optional[dict] = None) -> dict:
+    """root_tokens int32 [B]; cand_tokens int32 / cand_probs fp32 [B][N][k] ->
+    dict(parents, tokens, depth [B][N] int32, mask int64 [B][N][1], scores fp64 [B][N], n_nodes [B])."""
+    B, N, k = cand_tokens.shape
+    assert cand_probs.shape == cand_tokens.shape and cand_probs.dtype == torch.float32
+    assert cand_tokens.dtype == torch.int32 and root_tokens.dtype == torch.int32
+    dev = cand_tokens.device
+    if outputs is None:
+        outputs = dict(parents=torch.empty((B, N), dtype=torch.int32, device=dev),
+                       tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+                       depth=torch.empty((B, N), dtype=torch.int32, device=dev),
+                       mask=torch.empty((B, N, 1), dtype=torch.int64, device=dev),
+                       scores=torch.empty((B, N), dtype=torch.float64, device=dev),
+                       n_nodes=torch.empty(B, dtype=torch.int32, device=dev))
+    o = outputs
+    _check(_load().tv_build_tree(_ctx(dev), _ptr(root_tokens), _ptr(cand_tokens), _ptr(cand_probs), B, N, k, k_root,
+                                 float(threshold), max_depth, _ptr(o["parents"]), _ptr(o["tokens"]),
+                                 _ptr(o.get("depth")), _ptr(o.get("mask")), _ptr(o.get("scores")),
+                                 _ptr(o.get("n_nodes"))), "tv_build_tree")
+    return outputs
 
 
 def tv_attention_workspace_bytes(device, B, N, Hq, Hkv, D, max_prefix_len) -> int:

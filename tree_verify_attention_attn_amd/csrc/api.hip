@@ -141,6 +141,21 @@ tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages
                        path, accept_len, bonus_token, B, N, Hkv, D, new_prefix_lens, emitted, next_root);
 }
 
+tv_status tv_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *cand_tokens, const float *cand_probs,
+                        int32_t B, int32_t N, int32_t k, int32_t k_root, float threshold, int32_t max_depth,
+                        int32_t *parents, int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores,
+                        int32_t *n_nodes) {
+  if (!ctx || B < 0 || k < 1 || k_root < 1 || k_root > k || max_depth < 1 || isnan(threshold))
+    return TV_ERR_INVALID_ARG;
+  if (k > 32) return TV_ERR_UNSUPPORTED;
+  if (B == 0) return TV_OK;
+  if (N < 1) return TV_ERR_INVALID_ARG;
+  if (N > 64) return TV_ERR_UNSUPPORTED;
+  if (!root_tokens || !cand_tokens || !cand_probs || !parents || !tokens) return TV_ERR_INVALID_ARG;
+  return launch_build_tree(ctx, root_tokens, cand_tokens, cand_probs, B, N, k, k_root, threshold, max_depth, parents,
+                           tokens, depth, mask, scores, n_nodes);
+}
+
 tv_status tv_tau(tv_ctx *ctx, double *tau, uint64_t *cycles) {
   if (!ctx || !tau) return TV_ERR_INVALID_ARG;
   unsigned long long h[2] = {0, 0};

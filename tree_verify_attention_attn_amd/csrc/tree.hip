@@ -1,0 +1,152 @@
+// tree.hip - dynamic draft-tree construction on the device.
+//
+// EAGLE-2 deep-dive page, dynamic-tree algorithm and its reference code's
+// builder: a node's cumulative score is the product of the draft
+// probabilities on its root path; the queue starts with the root's top-k
+// proposals; the highest-scoring candidate becomes the next node (equal
+// scores: the one queued first); a node shallower than the depth limit
+// queues its top-k children whose cumulative score is above the threshold
+// (the reference code's strict test); construction stops at the node budget,
+// root included, or when the queue is empty. The tree is emitted with its
+// ancestor masks, ready for the attention call.
+//
+// One wavefront per sequence. The sequence's proposal table (row i: what the
+// draft head proposes for the node created i-th, at most 64 x 32 entries) is
+// copied into LDS first, so every pop is LDS and register work: a
+// lane-strided scan of the candidate pool for the best (score, queue
+// position), a wavefront reduction, and the new node's fields kept in lane
+// `node` (parent, token, depth, score, ancestor mask). Accepted children are
+// appended in slot order through a ballot prefix, which keeps the queue
+// order of the definition.
+#include "tv_internal.h"
+
+namespace tv {
+
+namespace {
+
+constexpr int kMaxK = 32;
+constexpr int kMaxPool = kMaxK + 63 * kMaxK;  // root proposals + k per other node
+
+__global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restrict__ root_tokens,
+                                                        const int32_t *__restrict__ cand_tokens,
+                                                        const float *__restrict__ cand_probs, int N, int k, int k_root,
+                                                        double threshold, int max_depth, int32_t *__restrict__ parents,
+                                                        int32_t *__restrict__ tokens, int32_t *__restrict__ depth,
+                                                        uint64_t *__restrict__ mask, double *__restrict__ scores,
+                                                        int32_t *__restrict__ n_nodes,
+                                                        unsigned long long *state) {
+  __shared__ float s_prob[64 * kMaxK];
+  __shared__ int32_t s_tok[64 * kMaxK];
+  __shared__ double s_score[kMaxPool];  // queued candidates; -1 once made a node
+  __shared__ int16_t s_src[kMaxPool];   // proposer row * 32 + slot
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t rows = static_cast<int64_t>(N) * k;
+  const int32_t *ct = cand_tokens + b * rows;
+  const float *cp = cand_probs + b * rows;
+  bool bad = false;
+  for (int j = lane; j < rows; j += 64) {
+    const float p = cp[j];
+    bad |= !(p >= 0.0f);  // NaN or negative
+    s_prob[(j / k) * kMaxK + j % k] = p;
+    s_tok[(j / k) * kMaxK + j % k] = ct[j];
+  }
+  bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  const int root_tok = root_tokens[b];
+  __syncthreads();
+
+  // lane i holds node i
+  int my_parent = -1, my_token = root_tok, my_depth = 0;
+  double my_score = lane == 0 ? 1.0 : 0.0;
+  uint64_t my_mask = 1ull << lane;
+  int n = 0;
+  if (!bad) {
+    n = 1;
+    int q = 0;  // pool size
+    for (int s = lane; s < k_root; s += 64) {  // the root's proposals are queued unconditionally
+      s_score[s] = static_cast<double>(s_prob[s]);
+      s_src[s] = static_cast<int16_t>(s);
+    }
+    q = k_root;
+    __syncthreads();
+    while (n < N) {
+      // best alive candidate: highest score, earliest queued on ties
+      double bs = -1.0;
+      int bj = 0x7FFFFFFF;
+      for (int j = lane; j < q; j += 64) {
+        const double sc = s_score[j];
+        if (sc > bs) {  // lane-strided j increases, so '>' keeps the earliest
+          bs = sc;
+          bj = j;
+        }
+      }
+      for (int m = 32; m >= 1; m >>= 1) {
+        const double os = __shfl_xor(bs, m);
+        const int oj = __shfl_xor(bj, m);
+        if (os > bs || (os == bs && oj < bj)) {
+          bs = os;
+          bj = oj;
+        }
+      }
+      if (bs < 0.0) break;  // queue empty
+      const int src = s_src[bj];
+      const int row = src >> 5, slot = src & 31;
+      const int id = n++;
+      const int pdepth = __shfl(my_depth, row);
+      const uint64_t pmask = shfl_u64(my_mask, row);
+      __syncthreads();  // every lane has read s_score[bj] before it is retired
+      if (lane == 0) s_score[bj] = -1.0;
+      if (lane == id) {
+        my_parent = row;
+        my_token = s_tok[row * kMaxK + slot];
+        my_depth = pdepth + 1;
+        my_score = bs;
+        my_mask = pmask | (1ull << id);
+      }
+      if (pdepth + 1 < max_depth) {
+        // the new node's proposals above the threshold, in slot order
+        double c = 0.0;
+        bool take = false;
+        if (lane < k) {
+          c = bs * static_cast<double>(s_prob[id * kMaxK + lane]);
+          take = c > threshold;
+        }
+        const uint64_t tk = __builtin_amdgcn_ballot_w64(take);
+        if (take) {
+          const int at = q + __popcll(tk & ((1ull << lane) - 1ull));
+          s_score[at] = c;
+          s_src[at] = static_cast<int16_t>(id * 32 + lane);
+        }
+        q += __popcll(tk);
+      }
+      __syncthreads();
+    }
+  }
+  if (lane < N) {
+    const int64_t o = static_cast<int64_t>(b) * N + lane;
+    const bool live = lane < n;
+    parents[o] = live ? my_parent : -1;
+    tokens[o] = live ? my_token : root_tok;
+    if (depth) depth[o] = live ? my_depth : 0;
+    if (mask) mask[o] = live ? my_mask : (1ull << lane);
+    if (scores) scores[o] = live ? my_score : 0.0;
+  }
+  if (lane == 0) {
+    if (n_nodes) n_nodes[b] = n;
+    if (bad) raise_error(state, TV_ERR_INVALID_ARG);
+  }
+}
+
+}  // namespace
+
+tv_status launch_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *cand_tokens,
+                            const float *cand_probs, int B, int N, int k, int k_root, float threshold, int max_depth,
+                            int32_t *parents, int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores,
+                            int32_t *n_nodes) {
+  hipLaunchKernelGGL(build_tree_kernel, dim3(B), dim3(64), 0, ctx->stream, root_tokens, cand_tokens, cand_probs, N, k,
+                     k_root, static_cast<double>(threshold), max_depth, parents, tokens, depth, mask, scores, n_nodes,
+                     ctx->d_state);
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+}  // namespace tv

@@ -86,6 +86,11 @@ tv_status launch_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_p
                         const int32_t *path, const int32_t *accept_len, const int32_t *bonus, int B, int N, int Hkv,
                         int D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root);
 
+tv_status launch_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *cand_tokens,
+                            const float *cand_probs, int B, int N, int k, int k_root, float threshold, int max_depth,
+                            int32_t *parents, int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores,
+                            int32_t *n_nodes);
+
 tv_status launch_clear_state(tv_ctx *ctx, int first_word, int n_words);
 
 }  // namespace tv
