@@ -152,6 +152,56 @@ def commit_bytes(w, path, lens):
     return kv + w.B * 12 + n * 4 * 3 + w.B * (w.N + 2) * 4
 
 
+def device_time(torch, call, n=50):
+    """Mean device time (us) of `call` over n back-to-back calls. A call can be
+    shorter than its host-side launch, so the stream is held by a bounded spin
+    kernel while the host queues all n; the events then time the calls back
+    to back on the device. Returns (us, whether the spin outlasted the
+    queueing)."""
+    for _ in range(5):
+        call()
+    es, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    torch.cuda.synchronize()
+    es.record()
+    torch.cuda._sleep(5_000_000)
+    e0.record()
+    h0 = time.perf_counter()
+    for _ in range(n):
+        call()
+    host_ms = (time.perf_counter() - h0) * 1e3
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3, bool(host_ms < es.elapsed_time(e0))
+
+
+def build_tree_timing(tv, torch, d, w, c):
+    """Times tv_build_tree on this workload's tree shape, fed the proposal
+    rows the input generator draws for its trees (threshold 0, as there)."""
+    import tvgen
+
+    B, N, k = w.B, w.N, c["topk"]
+    toks, probs = np.zeros((B, N, k), np.int32), np.zeros((B, N, k), np.float32)
+    roots = np.zeros(B, np.int32)
+    for b in range(B):
+        rec = {}
+        _, t = tvgen.dynamic_tree(w.seed, (tvgen.TID_TREE << 16) + b, N, c["max_depth"], k, w.V, record=rec)
+        roots[b] = t[0]
+        for node, (tk, sc) in rec.items():
+            if node < N:
+                toks[b, node], probs[b, node] = tk, sc
+    dr, dt, dp = d(roots), d(toks), d(probs)
+    out = tv.tv_build_tree(dr, dt, dp, k, 0.0, c["max_depth"])
+    # the generator multiplies fp64 probabilities, the builder their fp32
+    # roundings: a near tie can order two nodes differently
+    same = float((out["parents"].cpu().numpy() == w.parents).all(1).mean())
+    us, ok = device_time(torch, lambda: tv.tv_build_tree(dr, dt, dp, k, 0.0, c["max_depth"], outputs=out))
+    return {"avg_us": us, "queued_within_spin": ok, "trees": B, "nodes_per_tree": N, "proposals_per_node": k,
+            "same_trees_as_workload": same,
+            "nodes_per_s": B * N / us * 1e6,
+            "note": "tv_build_tree (not part of the step) rebuilding this workload's trees from the proposal rows "
+                    "the input generator drew; one wavefront per tree, sequential best-first pops: latency-bound"}
+
+
 def commit_timing(tv, torch, dev, w, depth, d, kp, vp, table, plens, tokens, outs):
     """Times tv_commit (after acceptance; it rewrites the pools, so it runs
     after every other GPU measurement) on two sets of paths: the last timed
@@ -177,27 +227,9 @@ def commit_timing(tv, torch, dev, w, depth, d, kp, vp, table, plens, tokens, out
         hp, hl = (step_path, step_len) if name == "step_paths" else (deep_path, deep_len)
         def call():
             tv.tv_commit(kp, vp, table, plens, w.max_prefix_len, tokens, pth, ln, bn, outputs=co)
-        for _ in range(5):
-            call()
-        # One call is shorter than its host-side launch, so the stream is held
-        # by a bounded spin kernel while the host queues all 50 calls; the
-        # events then time the calls back to back on the device. The spin must
-        # outlast the queueing, which is checked.
-        es, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        torch.cuda.synchronize()
-        es.record()
-        torch.cuda._sleep(5_000_000)
-        e0.record()
-        h0 = time.perf_counter()
-        for _ in range(50):
-            call()
-        host_ms = (time.perf_counter() - h0) * 1e3
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / 50 * 1e3
-        held_ms = es.elapsed_time(e0)
+        us, queued = device_time(torch, call)
         nbytes = commit_bytes(w, hp, hl)
-        res[name] = {"avg_us": us, "queued_within_spin": bool(host_ms < held_ms),
+        res[name] = {"avg_us": us, "queued_within_spin": queued,
                      "rows_moved_per_kv_head": commit_moves(w, hp, hl),
                      "mean_accept_len": float(np.mean(hl)), "bytes": nbytes, "gbs": nbytes / us / 1e3}
     assert tv.tv_device_error(dev) == 0
@@ -345,6 +377,8 @@ def main():
     t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
     result["mask_overhead"] = {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
                                "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
+    if c["tree"] == "dynamic":
+        result["build_tree"] = build_tree_timing(tv, torch, d, w, c)
     result["commit"] = commit_timing(tv, torch, dev, w, depth, d, kp, vp, table, plens, d(w.draft_tokens), outs)
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)

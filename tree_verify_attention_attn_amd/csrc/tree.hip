@@ -13,11 +13,11 @@
 // One wavefront per sequence. The sequence's proposal table (row i: what the
 // draft head proposes for the node created i-th, at most 64 x 32 entries) is
 // copied into LDS first, so every pop is LDS and register work: a
-// lane-strided scan of the candidate pool for the best (score, queue
-// position), a wavefront reduction, and the new node's fields kept in lane
-// `node` (parent, token, depth, score, ancestor mask). Accepted children are
-// appended in slot order through a ballot prefix, which keeps the queue
-// order of the definition.
+// lane-strided scan of the candidate pool for each lane's best (score, queue
+// position), a wavefront maximum of those pairs moved with DPP row shifts and
+// broadcasts, and the new node's fields kept in lane `node` (parent, token,
+// depth, score, ancestor mask). Accepted children are appended in slot order
+// through a ballot prefix, which keeps the queue order of the definition.
 #include "tv_internal.h"
 
 namespace tv {
@@ -26,6 +26,40 @@ namespace {
 
 constexpr int kMaxK = 32;
 constexpr int kMaxPool = kMaxK + 63 * kMaxK;  // root proposals + k per other node
+
+// (score, position) of the better candidate: higher score, then the one
+// queued first
+__device__ inline bool better(double os, int oj, double s, int j) { return os > s || (os == s && oj < j); }
+
+// one step of the wavefront maximum over (score, position), moving values
+// with DPP; lanes without a source in this pattern keep their own pair
+template <int kCtrl, int kRowMask>
+__device__ inline void best_step(double &s, int &j) {
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(s), __double2hiint(s), kCtrl, kRowMask, 0xF, false);
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(s), __double2loint(s), kCtrl, kRowMask, 0xF, false);
+  const int oj = __builtin_amdgcn_update_dpp(j, j, kCtrl, kRowMask, 0xF, false);
+  const double os = __hiloint2double(hi, lo);
+  if (better(os, oj, s, j)) {
+    s = os;
+    j = oj;
+  }
+}
+
+// the best (score, position) of the wavefront, returned to every lane:
+// prefix maxima within each row of 16 lanes (row_shr 1, 2, 4, 8), then
+// across rows (row_bcast 15 and 31) into lane 63, then read back
+__device__ inline void wave_best(double &s, int &j) {
+  best_step<0x111, 0xF>(s, j);
+  best_step<0x112, 0xF>(s, j);
+  best_step<0x114, 0xF>(s, j);
+  best_step<0x118, 0xF>(s, j);
+  best_step<0x142, 0xA>(s, j);
+  best_step<0x143, 0xC>(s, j);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(s), 63);
+  const int lo = __builtin_amdgcn_readlane(__double2loint(s), 63);
+  j = __builtin_amdgcn_readlane(j, 63);
+  s = __hiloint2double(hi, lo);
+}
 
 __global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restrict__ root_tokens,
                                                         const int32_t *__restrict__ cand_tokens,
@@ -80,14 +114,7 @@ __global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restric
           bj = j;
         }
       }
-      for (int m = 32; m >= 1; m >>= 1) {
-        const double os = __shfl_xor(bs, m);
-        const int oj = __shfl_xor(bj, m);
-        if (os > bs || (os == bs && oj < bj)) {
-          bs = os;
-          bj = oj;
-        }
-      }
+      wave_best(bs, bj);
       if (bs < 0.0) break;  // queue empty
       const int src = s_src[bj];
       const int row = src >> 5, slot = src & 31;
