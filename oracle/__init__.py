@@ -41,11 +41,11 @@ def _load():
             build(force=False)
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i32, i64, f32, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int
-        lib.tvo_build_mask.argtypes = [vp, i32, i32, vp, vp]
-        lib.tvo_attention.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, i64,
-                                      vp, c_int]
-        lib.tvo_accept_greedy.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, c_int]
-        lib.tvo_accept_stochastic.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, c_int]
+        lib.tvo_build_mask.argtypes = [vp, vp, i32, i32, vp, vp]
+        lib.tvo_attention.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp,
+                                      i64, vp, c_int]
+        lib.tvo_accept_greedy.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, c_int]
+        lib.tvo_accept_stochastic.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, c_int]
         lib.tvo_commit.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         lib.tvo_build_tree.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
         lib.tvo_tau.argtypes = [vp, i64]
@@ -68,33 +68,35 @@ def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
 
 
-def status_build_mask(parents, B=None, N=None):
+def status_build_mask(parents, B=None, N=None, tree_sizes=None):
     parents = _c(parents, np.int32)
+    tree_sizes = _c(tree_sizes, np.int32)
     B = parents.shape[0] if B is None else B
     N = parents.shape[1] if N is None else N
     W = max((N + 63) // 64, 1)
     mask = np.zeros((max(B, 0), max(N, 0), W), np.uint64)
     depth = np.zeros((max(B, 0), max(N, 0)), np.int32)
-    st = _load().tvo_build_mask(_p(parents), B, N, _p(mask), _p(depth))
+    st = _load().tvo_build_mask(_p(parents), _p(tree_sizes), B, N, _p(mask), _p(depth))
     return st, mask, depth
 
 
-def build_mask(parents):
+def build_mask(parents, tree_sizes=None):
     """parents int32 [B][N] -> (mask uint64 [B][N][ceil(N/64)], depth int32 [B][N])."""
-    st, mask, depth = status_build_mask(parents)
+    st, mask, depth = status_build_mask(parents, tree_sizes=tree_sizes)
     if st != OK:
         raise OracleError(st, "build_mask")
     return mask, depth
 
 
 def status_attention(q, k_pages, v_pages, page_table, prefix_lens, tree_mask, *, B, N, Hq, Hkv, D, sm_scale,
-                     num_pages=None, maxp=None, max_prefix_len=None, rows=None, nthreads=0):
+                     num_pages=None, maxp=None, max_prefix_len=None, rows=None, nthreads=0, tree_sizes=None):
     q = _c(q, np.uint16)
     k_pages = _c(k_pages, np.uint16)
     v_pages = _c(v_pages, np.uint16)
     page_table = _c(page_table, np.int32)
     prefix_lens = _c(prefix_lens, np.int32)
     tree_mask = _c(tree_mask, np.uint64)
+    tree_sizes = _c(tree_sizes, np.int32)
     if num_pages is None:
         num_pages = k_pages.shape[0]
     if maxp is None:
@@ -105,12 +107,13 @@ def status_attention(q, k_pages, v_pages, page_table, prefix_lens, tree_mask, *,
     n_rows = rows.shape[0] if rows is not None else max(B, 0) * max(N, 0) * max(Hq, 0)
     out = np.zeros((n_rows, max(D, 1)), np.float64)
     st = _load().tvo_attention(_p(q), _p(k_pages), _p(v_pages), num_pages, _p(page_table), maxp, _p(prefix_lens),
-                               max_prefix_len, _p(tree_mask), B, N, Hq, Hkv, D, np.float32(sm_scale), _p(rows),
+                               max_prefix_len, _p(tree_mask), _p(tree_sizes), B, N, Hq, Hkv, D, np.float32(sm_scale),
+                               _p(rows),
                                n_rows, _p(out), nthreads)
     return st, out
 
 
-def attention(w, tree_mask, rows=None, nthreads=0):
+def attention(w, tree_mask, rows=None, nthreads=0, tree_sizes=None):
     """fp64 attention for workload `w` (see tvgen.Workload).
 
     rows: optional int32 [n][3] (b, i, h) list; default every row. Returns
@@ -118,7 +121,7 @@ def attention(w, tree_mask, rows=None, nthreads=0):
     """
     st, out = status_attention(w.q, w.k_pages, w.v_pages, w.page_table, w.prefix_lens, tree_mask, B=w.B, N=w.N,
                                Hq=w.Hq, Hkv=w.Hkv, D=w.D, sm_scale=w.sm_scale, num_pages=w.num_pages,
-                               max_prefix_len=w.max_prefix_len, rows=rows, nthreads=nthreads)
+                               max_prefix_len=w.max_prefix_len, rows=rows, nthreads=nthreads, tree_sizes=tree_sizes)
     if st != OK:
         raise OracleError(st, "attention")
     if rows is None:
@@ -126,7 +129,7 @@ def attention(w, tree_mask, rows=None, nthreads=0):
     return out
 
 
-def status_accept_greedy(target_logits, draft_tokens, parents, B, N, V, nthreads=0):
+def status_accept_greedy(target_logits, draft_tokens, parents, B, N, V, nthreads=0, tree_sizes=None):
     target_logits = _c(target_logits, np.float32)
     draft_tokens = _c(draft_tokens, np.int32)
     parents = _c(parents, np.int32)
@@ -135,21 +138,22 @@ def status_accept_greedy(target_logits, draft_tokens, parents, B, N, V, nthreads
     path = np.zeros((Bn, Nn), np.int32)
     bonus = np.zeros(Bn, np.int32)
     y = np.zeros((Bn, Nn), np.int32)
-    st = _load().tvo_accept_greedy(_p(target_logits), _p(draft_tokens), _p(parents), B, N, V, _p(accept_len),
-                                   _p(path), _p(bonus), _p(y), nthreads)
+    tree_sizes = _c(tree_sizes, np.int32)
+    st = _load().tvo_accept_greedy(_p(target_logits), _p(draft_tokens), _p(parents), _p(tree_sizes), B, N, V,
+                                   _p(accept_len), _p(path), _p(bonus), _p(y), nthreads)
     return st, dict(accept_len=accept_len, path=path, bonus=bonus, target_argmax=y)
 
 
-def accept_greedy(target_logits, draft_tokens, parents, nthreads=0):
+def accept_greedy(target_logits, draft_tokens, parents, nthreads=0, tree_sizes=None):
     B, N, V = target_logits.shape
-    st, r = status_accept_greedy(target_logits, draft_tokens, parents, B, N, V, nthreads)
+    st, r = status_accept_greedy(target_logits, draft_tokens, parents, B, N, V, nthreads, tree_sizes=tree_sizes)
     if st != OK:
         raise OracleError(st, "accept_greedy")
     return r
 
 
 def status_accept_stochastic(target_logits, draft_logits, draft_tokens, parents, uniforms, B, N, V, temperature,
-                             nthreads=0):
+                             nthreads=0, tree_sizes=None):
     target_logits = _c(target_logits, np.float32)
     draft_logits = _c(draft_logits, np.float32)
     draft_tokens = _c(draft_tokens, np.int32)
@@ -160,16 +164,18 @@ def status_accept_stochastic(target_logits, draft_logits, draft_tokens, parents,
     path = np.zeros((Bn, Nn), np.int32)
     bonus = np.zeros(Bn, np.int32)
     margins = np.zeros((Bn, Nn), np.float64)
+    tree_sizes = _c(tree_sizes, np.int32)
     st = _load().tvo_accept_stochastic(_p(target_logits), _p(draft_logits), _p(draft_tokens), _p(parents),
-                                       _p(uniforms), B, N, V, np.float32(temperature), _p(accept_len), _p(path),
+                                       _p(tree_sizes), _p(uniforms), B, N, V, np.float32(temperature), _p(accept_len), _p(path),
                                        _p(bonus), _p(margins), nthreads)
     return st, dict(accept_len=accept_len, path=path, bonus=bonus, margins=margins)
 
 
-def accept_stochastic(target_logits, draft_logits, draft_tokens, parents, uniforms, temperature, nthreads=0):
+def accept_stochastic(target_logits, draft_logits, draft_tokens, parents, uniforms, temperature, nthreads=0,
+                      tree_sizes=None):
     B, N, V = target_logits.shape
     st, r = status_accept_stochastic(target_logits, draft_logits, draft_tokens, parents, uniforms, B, N, V,
-                                     temperature, nthreads)
+                                     temperature, nthreads, tree_sizes=tree_sizes)
     if st != OK:
         raise OracleError(st, "accept_stochastic")
     return r
@@ -229,8 +235,10 @@ def status_build_tree(root_tokens, cand_tokens, cand_probs, *, k_root, threshold
     N = cand_tokens.shape[1] if N is None else N
     k = cand_tokens.shape[2] if k is None else k
     shp = (max(B, 0), max(N, 0))
+    W = max((N + 63) // 64, 1)
     out = dict(parents=np.full(shp, -2, np.int32), tokens=np.full(shp, -2, np.int32), depth=np.full(shp, -2, np.int32),
-               mask=np.zeros(shp, np.uint64), scores=np.full(shp, np.nan), n_nodes=np.full(shp[0], -2, np.int32))
+               mask=np.zeros(shp + (W,), np.uint64), scores=np.full(shp, np.nan),
+               n_nodes=np.full(shp[0], -2, np.int32))
     st = _load().tvo_build_tree(_p(root_tokens), _p(cand_tokens), _p(cand_probs), B, N, k, k_root,
                                 np.float32(threshold), max_depth, _p(out["parents"]), _p(out["tokens"]),
                                 _p(out["depth"]), _p(out["mask"]), _p(out["scores"]), _p(out["n_nodes"]))

@@ -83,6 +83,28 @@ static void parallel_for(int64_t n, int nthreads, range_fn fn, void *ctx) {
 /* Tree rule shared by every call: parent[b][i] in {-1} U [0, i) (node ids are
  * assigned in creation order on the EAGLE-2 page, so a parent always precedes
  * its child); with need_root, parent[b][0] must be -1. */
+/* Node count of sequence b: tree_sizes[b] when given, else N. */
+static int32_t nodes_of(const int32_t *tree_sizes, int64_t b, int32_t N) { return tree_sizes ? tree_sizes[b] : N; }
+
+static int check_sizes(const int32_t *tree_sizes, int32_t B, int32_t N) {
+  for (int64_t b = 0; tree_sizes && b < B; ++b)
+    if (tree_sizes[b] < 1 || tree_sizes[b] > N) return TVO_ERR_INVALID_ARG;
+  return TVO_OK;
+}
+
+/* parents of the present nodes: -1 or an earlier node (need_root: node 0 has
+ * no parent) */
+static int check_tree_sized(const int32_t *parents, const int32_t *tree_sizes, int32_t B, int32_t N,
+                            int need_root) {
+  for (int64_t b = 0; b < B; ++b)
+    for (int32_t i = 0; i < nodes_of(tree_sizes, b, N); ++i) {
+      int32_t p = parents[b * N + i];
+      if (p < -1 || p >= i) return TVO_ERR_INVALID_TREE;
+      if (need_root && i == 0 && p != -1) return TVO_ERR_INVALID_TREE;
+    }
+  return TVO_OK;
+}
+
 static int check_tree(const int32_t *parents, int32_t B, int32_t N, int need_root) {
   for (int64_t b = 0; b < B; ++b)
     for (int32_t i = 0; i < N; ++i) {
@@ -98,20 +120,24 @@ static int check_tree(const int32_t *parents, int32_t B, int32_t N, int need_roo
  * start at the node itself, mark it, move to its parent, stop past the root) */
 /* ------------------------------------------------------------------------ */
 
-int tvo_build_mask(const int32_t *parents, int32_t B, int32_t N, uint64_t *mask, int32_t *depth) {
+int tvo_build_mask(const int32_t *parents, const int32_t *tree_sizes, int32_t B, int32_t N, uint64_t *mask,
+                   int32_t *depth) {
   if (B < 0 || N < 0) return TVO_ERR_INVALID_ARG;
-  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if (N > 128) return TVO_ERR_UNSUPPORTED;
   if ((int64_t)B * N == 0) return TVO_OK;
   if (!parents || !mask) return TVO_ERR_INVALID_ARG;
-  int st = check_tree(parents, B, N, 0);
+  int st = check_sizes(tree_sizes, B, N);
+  if (st != TVO_OK) return st;
+  st = check_tree_sized(parents, tree_sizes, B, N, 0);
   if (st != TVO_OK) return st;
   const int32_t W = (N + 63) / 64;
   for (int64_t b = 0; b < B; ++b) {
+    const int32_t n = nodes_of(tree_sizes, b, N);
     for (int32_t i = 0; i < N; ++i) {
       uint64_t *row = mask + ((int64_t)b * N + i) * W;
       for (int32_t w = 0; w < W; ++w) row[w] = 0;
       int32_t d = -1;
-      int32_t c = i;
+      int32_t c = i < n ? i : -1; /* an absent node: empty row, depth -1 */
       while (c != -1) {
         row[c / 64] |= (uint64_t)1 << (c % 64);
         d += 1;
@@ -148,6 +174,7 @@ typedef struct {
   int32_t maxp;
   const int32_t *prefix_lens;
   const uint64_t *mask;
+  const int32_t *tree_sizes;
   int32_t B, N, Hq, Hkv, D;
   double scale;
   const int32_t *rows;
@@ -184,10 +211,16 @@ static void attn_rows(void *vctx, int64_t lo, int64_t hi) {
     const uint16_t *qr = a->q + ((b * a->N + i) * a->Hq + h) * a->D;
     for (int32_t d = 0; d < a->D; ++d) qd[d] = bf16_to_double(qr[d]);
 
-    /* visible key positions: the whole prefix, then the tree nodes on the mask */
+    const int32_t n = nodes_of(a->tree_sizes, b, a->N);
+    double *o = a->out + r * a->D;
+    if (i >= n) { /* an absent node has no output */
+      for (int32_t d = 0; d < a->D; ++d) o[d] = NAN;
+      continue;
+    }
+    /* visible key positions: the whole prefix, then the present tree nodes on the mask */
     int64_t nk = 0;
     for (int64_t t = 0; t < L; ++t) keys[nk++] = t;
-    for (int32_t j = 0; j < a->N; ++j) {
+    for (int32_t j = 0; j < n; ++j) {
       int visible = 1;
       if (a->mask) visible = (int)((a->mask[(b * a->N + i) * W + j / 64] >> (j % 64)) & 1u);
       if (visible) keys[nk++] = L + j;
@@ -206,7 +239,6 @@ static void attn_rows(void *vctx, int64_t lo, int64_t hi) {
       s[n] = exp(s[n] - m);
       Z += s[n];
     }
-    double *o = a->out + r * a->D;
     for (int32_t d = 0; d < a->D; ++d) o[d] = 0.0;
     for (int64_t n = 0; n < nk; ++n) {
       const uint16_t *vr = kv_row(a, a->vp, b, g, keys[n]);
@@ -223,24 +255,26 @@ static void attn_rows(void *vctx, int64_t lo, int64_t hi) {
 
 int tvo_attention(const uint16_t *q, const uint16_t *k_pages, const uint16_t *v_pages, int64_t num_pages,
                   const int32_t *page_table, int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len,
-                  const uint64_t *tree_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                  float sm_scale, const int32_t *rows, int64_t n_rows, double *out, int nthreads) {
+                  const uint64_t *tree_mask, const int32_t *tree_sizes, int32_t B, int32_t N, int32_t Hq,
+                  int32_t Hkv, int32_t D, float sm_scale, const int32_t *rows, int64_t n_rows, double *out,
+                  int nthreads) {
   /* argument rules (same as the library's) */
   if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_pages < 0 || maxp < 0 || max_prefix_len < 0)
     return TVO_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return TVO_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return TVO_ERR_UNSUPPORTED;
-  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if (N > 128) return TVO_ERR_UNSUPPORTED;
   if (!isfinite(sm_scale)) return TVO_ERR_INVALID_ARG;
   if ((int64_t)B * N == 0) return TVO_OK;
   if ((int64_t)maxp * 16 < (int64_t)max_prefix_len + N) return TVO_ERR_INVALID_ARG;
   if (!q || !k_pages || !v_pages || !page_table || !prefix_lens || !out) return TVO_ERR_INVALID_ARG;
-  /* data rules: prefix lengths within [0, max_prefix_len], every page the
-   * sequence touches inside [0, num_pages) */
+  /* data rules: node counts within [1, N], prefix lengths within
+   * [0, max_prefix_len], every page the sequence touches inside [0, num_pages) */
+  if (check_sizes(tree_sizes, B, N) != TVO_OK) return TVO_ERR_INVALID_ARG;
   for (int64_t b = 0; b < B; ++b) {
     int32_t L = prefix_lens[b];
     if (L < 0 || L > max_prefix_len) return TVO_ERR_INVALID_ARG;
-    int64_t np = ((int64_t)L + N + 15) / 16;
+    int64_t np = ((int64_t)L + nodes_of(tree_sizes, b, N) + 15) / 16;
     for (int64_t p = 0; p < np; ++p) {
       int32_t id = page_table[b * maxp + p];
       if (id < 0 || id >= num_pages) return TVO_ERR_INVALID_ARG;
@@ -261,6 +295,7 @@ int tvo_attention(const uint16_t *q, const uint16_t *k_pages, const uint16_t *v_
   a.maxp = maxp;
   a.prefix_lens = prefix_lens;
   a.mask = tree_mask;
+  a.tree_sizes = tree_sizes;
   a.B = B;
   a.N = N;
   a.Hq = Hq;
@@ -316,41 +351,45 @@ static void argmax_rows(void *vctx, int64_t lo, int64_t hi) {
   }
 }
 
-static int check_tokens(const int32_t *tok, int32_t B, int32_t N, int32_t V) {
+static int check_tokens(const int32_t *tok, const int32_t *tree_sizes, int32_t B, int32_t N, int32_t V) {
   for (int64_t b = 0; b < B; ++b)
-    for (int32_t i = 1; i < N; ++i)
+    for (int32_t i = 1; i < nodes_of(tree_sizes, b, N); ++i)
       if (tok[b * N + i] < 0 || tok[b * N + i] >= V) return TVO_ERR_INVALID_ARG;
   return TVO_OK;
 }
 
-int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, const int32_t *parents, int32_t B,
-                      int32_t N, int32_t V, int32_t *accept_len, int32_t *path, int32_t *bonus,
-                      int32_t *target_argmax, int nthreads) {
+int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, const int32_t *parents,
+                      const int32_t *tree_sizes, int32_t B, int32_t N, int32_t V, int32_t *accept_len, int32_t *path,
+                      int32_t *bonus, int32_t *target_argmax, int nthreads) {
   if (B < 0 || V <= 0) return TVO_ERR_INVALID_ARG;
   if (B == 0) return TVO_OK;
   if (N < 1) return TVO_ERR_INVALID_ARG;
-  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if (N > 128) return TVO_ERR_UNSUPPORTED;
   if (!target_logits || !draft_tokens || !parents || !accept_len || !path || !bonus) return TVO_ERR_INVALID_ARG;
-  int st = check_tree(parents, B, N, 1);
+  int st = check_sizes(tree_sizes, B, N);
   if (st != TVO_OK) return st;
-  st = check_tokens(draft_tokens, B, N, V);
+  st = check_tree_sized(parents, tree_sizes, B, N, 1);
+  if (st != TVO_OK) return st;
+  st = check_tokens(draft_tokens, tree_sizes, B, N, V);
   if (st != TVO_OK) return st;
 
   int32_t *y = (int32_t *)malloc(sizeof(int32_t) * (size_t)B * N);
   argmax_ctx ac = {target_logits, V, y};
   parallel_for((int64_t)B * N, nthreads, argmax_rows, &ac);
 
-  int32_t best[64], next[64];
+  int32_t best[128], next[128];
   for (int64_t b = 0; b < B; ++b) {
+    const int32_t n = nodes_of(tree_sizes, b, N);
     const int32_t *par = parents + b * N;
     const int32_t *tok = draft_tokens + b * N;
-    const int32_t *yb = y + b * N;
+    int32_t *yb = y + b * N;
+    for (int32_t i = n; i < N; ++i) yb[i] = -1; /* absent nodes have no row */
     /* bottom-up: best[i] = most matching nodes on a path below i,
      * next[i] = the lowest child reaching it */
-    for (int32_t i = N - 1; i >= 0; --i) {
+    for (int32_t i = n - 1; i >= 0; --i) {
       best[i] = 0;
       next[i] = -1;
-      for (int32_t c = i + 1; c < N; ++c) {
+      for (int32_t c = i + 1; c < n; ++c) {
         if (par[c] != i) continue;
         if (tok[c] != yb[i]) continue;
         if (1 + best[c] > best[i]) {
@@ -469,19 +508,22 @@ static double target_w(const void *vc, int64_t x) {
 }
 
 int tvo_accept_stochastic(const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
-                          const int32_t *parents, const float *uniforms, int32_t B, int32_t N, int32_t V,
+                          const int32_t *parents, const int32_t *tree_sizes, const float *uniforms, int32_t B,
+                          int32_t N, int32_t V,
                           float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus, double *margins,
                           int nthreads) {
   if (B < 0 || V <= 0) return TVO_ERR_INVALID_ARG;
   if (!(temperature > 0.0f) || !isfinite(temperature)) return TVO_ERR_INVALID_ARG;
   if (B == 0) return TVO_OK;
   if (N < 1) return TVO_ERR_INVALID_ARG;
-  if (N > 64) return TVO_ERR_UNSUPPORTED;
+  if (N > 128) return TVO_ERR_UNSUPPORTED;
   if (!target_logits || !draft_logits || !draft_tokens || !parents || !uniforms || !accept_len || !path || !bonus)
     return TVO_ERR_INVALID_ARG;
-  int st = check_tree(parents, B, N, 1);
+  int st = check_sizes(tree_sizes, B, N);
   if (st != TVO_OK) return st;
-  st = check_tokens(draft_tokens, B, N, V);
+  st = check_tree_sized(parents, tree_sizes, B, N, 1);
+  if (st != TVO_OK) return st;
+  st = check_tokens(draft_tokens, tree_sizes, B, N, V);
   if (st != TVO_OK) return st;
 
   const double T = (double)temperature;
@@ -499,6 +541,7 @@ int tvo_accept_stochastic(const float *target_logits, const float *draft_logits,
   parallel_for(R, nthreads, softmax_stats, &sq);
 
   for (int64_t b = 0; b < B; ++b) {
+    const int32_t n = nodes_of(tree_sizes, b, N);
     const int32_t *tok = draft_tokens + b * N;
     const int32_t *par = parents + b * N;
     const float *u = uniforms + b * N;
@@ -516,7 +559,7 @@ int tvo_accept_stochastic(const float *target_logits, const float *draft_logits,
       const int64_t rp = b * N + node;
       const float *prow = target_logits + rp * V;
       int32_t accepted = -1;
-      for (int32_t c = node + 1; c < N; ++c) {
+      for (int32_t c = node + 1; c < n; ++c) {
         if (par[c] != node) continue; /* children in increasing id order */
         const int64_t rq = b * N + c;
         const float *qrow = draft_logits + rq * V;
@@ -603,7 +646,7 @@ int tvo_commit(uint16_t *k_pages, uint16_t *v_pages, int64_t num_pages, const in
                const int32_t *prefix_lens, int32_t max_prefix_len, const int32_t *draft_tokens,
                const int32_t *path, const int32_t *accept_len, const int32_t *bonus, int32_t B, int32_t N,
                int32_t Hkv, int32_t D, int32_t *new_prefix_lens, int32_t *emitted, int32_t *next_root) {
-  if (B < 0 || N < 1 || N > 64 || Hkv <= 0 || (D != 64 && D != 128) || maxp < 0 || max_prefix_len < 0 ||
+  if (B < 0 || N < 1 || N > 128 || Hkv <= 0 || (D != 64 && D != 128) || maxp < 0 || max_prefix_len < 0 ||
       num_pages < 0)
     return TVO_ERR_INVALID_ARG;
   if (B == 0) return TVO_OK;
@@ -686,7 +729,7 @@ int tvo_commit(uint16_t *k_pages, uint16_t *v_pages, int64_t num_pages, const in
 int tvo_build_tree(const int32_t *root_tokens, const int32_t *cand_tokens, const float *cand_probs, int32_t B,
                    int32_t N, int32_t k, int32_t k_root, float threshold, int32_t max_depth, int32_t *parents,
                    int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores, int32_t *n_nodes) {
-  if (B < 0 || N < 1 || N > 64 || k < 1 || k > 32 || k_root < 1 || k_root > k || max_depth < 1 ||
+  if (B < 0 || N < 1 || N > 128 || k < 1 || k > 32 || k_root < 1 || k_root > k || max_depth < 1 ||
       !(threshold == threshold))
     return TVO_ERR_INVALID_ARG;
   if (B == 0) return TVO_OK;
@@ -704,8 +747,8 @@ int tvo_build_tree(const int32_t *root_tokens, const int32_t *cand_tokens, const
     const int32_t *ct = cand_tokens + b * N * k;
     const float *cp = cand_probs + b * N * k;
     int32_t *pa = parents + b * N, *tk = tokens + b * N;
-    double sc[64];
-    int32_t dp[64];
+    double sc[128];
+    int32_t dp[128];
     int bad = 0;
     for (int64_t j = 0; j < (int64_t)N * k; ++j)
       if (!(cp[j] >= 0.0f)) bad = 1; /* NaN or negative */
@@ -737,10 +780,11 @@ int tvo_build_tree(const int32_t *root_tokens, const int32_t *cand_tokens, const
     for (int32_t i = 0; i < N; ++i) {
       if (depth) depth[b * N + i] = dp[i];
       if (scores) scores[b * N + i] = sc[i];
-      if (mask) { /* the node and every ancestor */
-        uint64_t m = 0;
-        for (int32_t c = i; c >= 0; c = pa[c]) m |= 1ull << c;
-        mask[b * N + i] = m;
+      if (mask) { /* the node and every ancestor, W = ceil(N / 64) words per row */
+        const int32_t W = (N + 63) / 64;
+        uint64_t *row = mask + (b * N + i) * W;
+        for (int32_t w = 0; w < W; ++w) row[w] = 0;
+        for (int32_t c = i; c >= 0; c = pa[c]) row[c / 64] |= 1ull << (c % 64);
       }
     }
     if (n_nodes) n_nodes[b] = n;

@@ -30,25 +30,32 @@ enum {
   TVO_ERR_RUNTIME = 5
 };
 
+/* Node counts: tree_sizes [B] (nullable, NULL = every sequence has N nodes)
+ * gives sequence b n_b nodes, 1 <= n_b <= N <= 128; nodes n_b..N-1 are
+ * absent: their parents, tokens, logits rows and K/V are never read, mask
+ * rows are 0 with depth -1, attention rows are NaN, argmax rows -1. */
+
 /* Ancestor-or-self mask and depth of every node (EAGLE-2 deep-dive page,
  * tree-mask assembly in its reference code): bit j of mask[b][i][j/64]
  * (bit position j%64, least significant bit = node 0) is set iff j is met on
  * the walk i, parent[i], parent[parent[i]], ... ; depth[i] = (#set bits) - 1. */
-int tvo_build_mask(const int32_t *parents, int32_t B, int32_t N, uint64_t *mask, int32_t *depth);
+int tvo_build_mask(const int32_t *parents, const int32_t *tree_sizes, int32_t B, int32_t N, uint64_t *mask,
+                   int32_t *depth);
 
 /* Tree-masked paged GQA attention in fp64 for the listed rows.
  * rows: [n_rows][3] triples (b, i, h), or NULL for every row in [B][N][Hq]
  * order. out: [n_rows][D] doubles. tree_mask NULL = every tree node visible. */
 int tvo_attention(const uint16_t *q, const uint16_t *k_pages, const uint16_t *v_pages, int64_t num_pages,
                   const int32_t *page_table, int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len,
-                  const uint64_t *tree_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                  float sm_scale, const int32_t *rows, int64_t n_rows, double *out, int nthreads);
+                  const uint64_t *tree_mask, const int32_t *tree_sizes, int32_t B, int32_t N, int32_t Hq,
+                  int32_t Hkv, int32_t D, float sm_scale, const int32_t *rows, int64_t n_rows, double *out,
+                  int nthreads);
 
 /* Greedy acceptance: longest root path of matching nodes, lexicographically
  * smallest on ties; accept_len counts the bonus token. */
-int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, const int32_t *parents, int32_t B,
-                      int32_t N, int32_t V, int32_t *accept_len, int32_t *path, int32_t *bonus,
-                      int32_t *target_argmax, int nthreads);
+int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, const int32_t *parents,
+                      const int32_t *tree_sizes, int32_t B, int32_t N, int32_t V, int32_t *accept_len, int32_t *path,
+                      int32_t *bonus, int32_t *target_argmax, int nthreads);
 
 /* Stochastic acceptance on a chain or tree: from the root, test the current
  * node's children in id order, child c accepted iff u[c-1] < pi(t_c)/q_c(t_c)
@@ -58,7 +65,8 @@ int tvo_accept_greedy(const float *target_logits, const int32_t *draft_tokens, c
  * each tested node c at [c-1], distance of the final draw to the nearest CDF
  * boundary relative to the total mass at [N-1], +inf where unused. */
 int tvo_accept_stochastic(const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
-                          const int32_t *parents, const float *uniforms, int32_t B, int32_t N, int32_t V,
+                          const int32_t *parents, const int32_t *tree_sizes, const float *uniforms, int32_t B,
+                          int32_t N, int32_t V,
                           float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus, double *margins,
                           int nthreads);
 

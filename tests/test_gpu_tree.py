@@ -22,7 +22,7 @@ KEYS = ("parents", "tokens", "depth", "mask", "scores", "n_nodes")
 def gpu_tree(roots, toks, probs, k_root, threshold, max_depth):
     out = tv.tv_build_tree(dev(roots), dev(toks), dev(probs), k_root, threshold, max_depth)
     r = {key: host(v) for key, v in out.items()}
-    r["mask"] = r["mask"].view(np.uint64)[..., 0]
+    r["mask"] = r["mask"].view(np.uint64)
     return r
 
 

@@ -202,7 +202,7 @@ def test_status_codes():
     assert oracle.status_attention(*args, **kw)[0] == oracle.OK
     assert oracle.status_attention(*args, **{**kw, "Hkv": 3})[0] == oracle.INVALID_ARG
     assert oracle.status_attention(*args, **{**kw, "D": 96})[0] == oracle.UNSUPPORTED
-    assert oracle.status_attention(*args, **{**kw, "N": 65})[0] == oracle.UNSUPPORTED
+    assert oracle.status_attention(*args, **{**kw, "N": 129})[0] == oracle.UNSUPPORTED
     assert oracle.status_attention(*args, **kw, maxp=1)[0] == oracle.INVALID_ARG
     bad = w.page_table.copy()
     bad[0, 0] = w.num_pages

@@ -176,7 +176,7 @@ def test_commit_argument_errors():
     lens = np.full(w.B, w.N, np.int32)
     bonus = np.zeros(w.B, np.int32)
     args = (w.k_pages, w.v_pages, w.page_table, w.prefix_lens, w.draft_tokens, path, lens, bonus)
-    for kw in (dict(D=96), dict(N=0), dict(N=65), dict(Hkv=0), dict(B=-1)):
+    for kw in (dict(D=96), dict(N=0), dict(N=129), dict(Hkv=0), dict(B=-1)):
         base = dict(B=w.B, N=w.N, Hkv=w.Hkv, D=w.D)
         base.update(kw)
         st, *_ = oracle.status_commit(*args, **base, num_pages=w.num_pages)

@@ -91,7 +91,7 @@ def test_status_codes():
     assert st == oracle.INVALID_TREE
     st, _, _ = oracle.status_build_mask(np.array([[0, 0]], np.int32))  # root with a parent
     assert st == oracle.INVALID_TREE
-    st, _, _ = oracle.status_build_mask(np.full((1, 65), -1, np.int32))
+    st, _, _ = oracle.status_build_mask(np.full((1, 129), -1, np.int32))
     assert st == oracle.UNSUPPORTED
     st, _, _ = oracle.status_build_mask(np.zeros((0, 5), np.int32))
     assert st == oracle.OK

@@ -28,7 +28,7 @@ def test_tree_build_hand_worked_fixture():
     for key, v in g["expect"].items():
         assert r[key].tolist() == v, key
     mask, _ = oracle.build_mask(r["parents"])
-    assert np.array_equal(r["mask"], mask[:, :, 0])
+    assert np.array_equal(r["mask"], mask)
 
 
 def generator_tables(seed, B, N, max_depth, topk, V):
@@ -131,7 +131,7 @@ def test_tree_build_invariants():
     for thr, md in ((0.0, 8), (1e-3, 6), (0.05, 3)):
         r = oracle.build_tree(roots, toks.astype(np.int32), probs, k_root=4, threshold=thr, max_depth=md)
         mask, depth = oracle.build_mask(r["parents"])
-        assert np.array_equal(r["mask"], mask[:, :, 0])
+        assert np.array_equal(r["mask"], mask)
         for b in range(B):
             n = r["n_nodes"][b]
             s, p, d = r["scores"][b], r["parents"][b], r["depth"][b]
@@ -163,5 +163,5 @@ def test_tree_build_status():
     assert oracle.status_build_tree(roots, toks, probs, k_root=4, threshold=0.0, max_depth=3)[0] == oracle.INVALID_ARG
     assert oracle.status_build_tree(roots, toks, probs, k_root=2, threshold=0.0, max_depth=0)[0] == oracle.INVALID_ARG
     assert oracle.status_build_tree(roots, toks, probs, B=0, **kw)[0] == oracle.OK
-    big = np.zeros((1, 65, 3), np.int32)
-    assert oracle.status_build_tree(roots[:1], big, np.zeros((1, 65, 3), np.float32), **kw)[0] == oracle.INVALID_ARG
+    big = np.zeros((1, 129, 3), np.int32)
+    assert oracle.status_build_tree(roots[:1], big, np.zeros((1, 129, 3), np.float32), **kw)[0] == oracle.INVALID_ARG
