@@ -36,6 +36,13 @@
  *  - Tree numbering: node ids are topological (parent[i] < i), as in the
  *    EAGLE-2 page's reference code which numbers nodes in creation order.
  *    Node 0 is the root: the last verified token, counted in the tree.
+ *  - Tree sizes: N <= 128 node slots per sequence; masks have W =
+ *    ceil(N / 64) words per row. tree_sizes int32 [B] (nullable; NULL =
+ *    every sequence has N nodes) gives sequence b n_b nodes, 1 <= n_b <= N;
+ *    slots n_b..N-1 are absent: their parents, tokens, logits rows and K/V
+ *    are never read; mask rows are written 0 with depth -1, attention rows
+ *    are not written, argmax rows are -1. A count outside [1, N] sets the
+ *    sticky TV_ERR_INVALID_ARG (that sequence's outputs as for bad data).
  *  - A context is not thread-safe; use one per stream/thread.
  */
 #ifndef TREEVERIFY_H
@@ -52,7 +59,7 @@ typedef enum tv_status {
   TV_OK = 0,
   TV_ERR_INVALID_ARG = 1,  /* bad scalar, NULL pointer, bad page id / token / prefix length */
   TV_ERR_INVALID_TREE = 2, /* parent[b][i] outside {-1} U [0, i), or accept root with a parent */
-  TV_ERR_UNSUPPORTED = 3,  /* shape outside what the kernels implement (N > 64, D not 64/128) */
+  TV_ERR_UNSUPPORTED = 3,  /* shape outside what the kernels implement (N > 128, D not 64/128) */
   TV_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than the *_workspace_bytes figure */
   TV_ERR_HIP = 5           /* HIP runtime error (launch failure, bad device) */
 } tv_status;
@@ -74,16 +81,18 @@ tv_status tv_set_stream(tv_ctx *ctx, void *hip_stream);
 /* Ancestor-or-self bitmask of every tree node ([EAGLE-2 page], reference
  * code, tree-mask assembly: a node's row marks the node, then each parent up
  * to the root).
- *   parents  int32 [B][N]: parent id, or -1 for a root (forests allowed).
- *   mask     uint64 [B][N][W], W = ceil(N/64) (= 1, since N <= 64): bit j
- *            (position j % 64 of word j / 64, least significant bit = node 0)
- *            of row (b, i) is set iff j is i or an ancestor of i.
- *   depth    int32 [B][N] or NULL: number of ancestors (root = 0); a node's
- *            position id would be prefix_len + depth.
- * Requires 0 <= N <= 64, B >= 0. Bad parents: sticky TV_ERR_INVALID_TREE and
- * that sequence's rows are written as mask 0, depth -1. */
-tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, int32_t B, int32_t N, uint64_t *mask,
-                        int32_t *depth);
+ *   parents     int32 [B][N]: parent id, or -1 for a root (forests allowed).
+ *   tree_sizes  int32 [B] or NULL: node counts (see the conventions above).
+ *   mask        uint64 [B][N][W], W = ceil(N/64): bit j (position j % 64 of
+ *               word j / 64, least significant bit = node 0) of row (b, i)
+ *               is set iff j is i or an ancestor of i.
+ *   depth       int32 [B][N] or NULL: number of ancestors (root = 0); a
+ *               node's position id would be prefix_len + depth.
+ * Requires 0 <= N <= 128, B >= 0. Bad parents among the present nodes:
+ * sticky TV_ERR_INVALID_TREE and that sequence's rows are written as mask 0,
+ * depth -1. */
+tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, const int32_t *tree_sizes, int32_t B, int32_t N,
+                        uint64_t *mask, int32_t *depth);
 
 /* Dynamic draft-tree construction ([EAGLE-2 page], dynamic-tree algorithm
  * section and its reference code's builder). A node's cumulative score is the
@@ -103,12 +112,12 @@ tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, int32_t B, int32_t 
  *   threshold    fp32, compared in fp64 with the fp64 product of fp32 scores
  *   parents, tokens  int32 [B][N]: the tree, in the layout tv_build_mask,
  *                tv_attention and tv_accept take
- *   depth int32 [B][N], mask uint64 [B][N][1] (ancestor-or-self bits as
+ *   depth int32 [B][N], mask uint64 [B][N][W] (ancestor-or-self bits as
  *                tv_build_mask writes them), scores fp64 [B][N] (cumulative),
  *                n_nodes int32 [B]: all nullable
  * Slots past n_nodes of a short tree are padding: parent -1, the root's
  * token, depth 0, mask = the slot's own bit, score 0 (never accepted).
- * Requires 1 <= N <= 64, 1 <= k_root <= k <= 32, max_depth >= 1, threshold
+ * Requires 1 <= N <= 128, 1 <= k_root <= k <= 32, max_depth >= 1, threshold
  * not NaN. A sequence with a NaN or negative probability anywhere in its
  * table is written as padding with n_nodes 0 and sets the sticky
  * TV_ERR_INVALID_ARG. */
@@ -126,10 +135,10 @@ size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t H
 
 /* Tree-masked attention over a paged GQA KV cache ([EAGLE-2 page], third
  * pillar and the production note on paged tree masks).
- * For sequence b, node i, query head h (KV head g = h / (Hq/Hkv)):
+ * For sequence b, present node i < n_b, query head h (KV head g = h / (Hq/Hkv)):
  *   keys  = prefix tokens t in [0, L_b) and tree tokens t = L_b + j for every
- *           j whose bit is set in tree_mask[b][i] (all j when tree_mask is
- *           NULL: the unmasked baseline);
+ *           present j whose bit is set in tree_mask[b][i] (all present j when
+ *           tree_mask is NULL: the unmasked baseline);
  *   s_t   = sm_scale * <q, k_t>,  out = sum_t softmax(s)_t v_t.
  * Token t of sequence b lives in page page_table[b][t / 16], slot t % 16.
  *   q            bf16 [B][N][Hq][D]
@@ -139,13 +148,16 @@ size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t H
  *   prefix_lens  int32 [B], L_b in [0, max_prefix_len] (root excluded)
  *   max_prefix_len (host) bound used for planning; maxp * 16 >= max_prefix_len + N
  *   tree_mask    uint64 [B][N][W] as written by tv_build_mask, or NULL
+ *   tree_sizes   int32 [B] or NULL: node counts; rows of absent nodes are not
+ *                written and their keys are never read
  *   out          [B][N][Hq][D] in out_dtype (TV_F32 or TV_BF16)
  *   workspace    >= tv_attention_workspace_bytes(...) bytes (may be NULL if 0)
- * Requires D in {64, 128}, Hq % Hkv == 0, 0 <= N <= 64. Accumulates in fp32. */
+ * Requires D in {64, 128}, Hq % Hkv == 0, 0 <= N <= 128. Accumulates in fp32. */
 tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const void *v_pages, int64_t num_pages,
                        const int32_t *page_table, int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len,
-                       const uint64_t *tree_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                       float sm_scale, void *out, tv_dtype out_dtype, void *workspace, size_t workspace_bytes);
+                       const uint64_t *tree_mask, const int32_t *tree_sizes, int32_t B, int32_t N, int32_t Hq,
+                       int32_t Hkv, int32_t D, float sm_scale, void *out, tv_dtype out_dtype, void *workspace,
+                       size_t workspace_bytes);
 
 /* Workspace (bytes) tv_accept needs: per-row partial vocab reductions, and
  * in stochastic mode two residual rows of V doubles per sequence. */
@@ -161,6 +173,8 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  *                  the draft distribution that produced node i's token
  *   draft_tokens   int32 [B][N]; [b][0] is the root's token (not verified)
  *   parents        int32 [B][N]; parents[b][0] must be -1
+ *   tree_sizes     int32 [B] or NULL: node counts; absent nodes are never
+ *                  read or accepted, their argmax rows are -1
  *   uniforms       fp32 [B][N] in [0, 1) (stochastic only, else NULL):
  *                  u[c-1] tests node c, u[N-1] drives the final draw
  *   temperature    > 0; logits are divided by it (stochastic only)
@@ -190,9 +204,10 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  *   from max(0, p - q) at the rejection (p if its mass is 0), or from
  *   p_{N-1} when every draft is accepted.
  * Adds sum(accept_len) and B to the context's tau counters. Requires
- * 1 <= N <= 64 when B > 0, V >= 1. */
+ * 1 <= N <= 128 when B > 0, V >= 1. */
 tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
-                    const int32_t *parents, const float *uniforms, int32_t B, int32_t N, int32_t V,
+                    const int32_t *parents, const int32_t *tree_sizes, const float *uniforms, int32_t B, int32_t N,
+                    int32_t V,
                     tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus_token,
                     int32_t *target_argmax, void *workspace, size_t workspace_bytes);
 
@@ -222,7 +237,7 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
  * n outside [1, N], a bad path, a negative bonus or a page id outside
  * [0, num_pages) at a touched position is left unchanged (new length L,
  * next root -1, emitted -1) and sets the sticky TV_ERR_INVALID_ARG.
- * Requires D in {64, 128}, 1 <= N <= 64 when B > 0, maxp * 16 >=
+ * Requires D in {64, 128}, 1 <= N <= 128 when B > 0, maxp * 16 >=
  * max_prefix_len + N. */
 tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages, const int32_t *page_table,
                     int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len, const int32_t *draft_tokens,

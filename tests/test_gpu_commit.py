@@ -207,7 +207,7 @@ def test_commit_host_errors():
                              p(args[3]), p(args[4]), p(args[5]), B, N, Hkv, D, p(outs[0]), p(outs[1]), p(outs[2]))
 
     assert call(D=96) == tv.UNSUPPORTED
-    assert call(N=65) == tv.UNSUPPORTED
+    assert call(N=129) == tv.UNSUPPORTED
     assert call(N=0) == tv.INVALID_ARG
     assert call(Hkv=0) == tv.INVALID_ARG
     assert call(maxp=0) == tv.INVALID_ARG

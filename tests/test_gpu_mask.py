@@ -54,5 +54,5 @@ def test_bad_parent_sets_device_error():
 
 def test_host_detected_errors():
     with pytest.raises(tv.TVError) as e:
-        tv.tv_build_mask(dev(np.full((1, 65), -1, np.int32)))
+        tv.tv_build_mask(dev(np.full((1, 129), -1, np.int32)))
     assert e.value.status == tv.UNSUPPORTED

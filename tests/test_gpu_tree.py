@@ -121,7 +121,7 @@ def test_build_tree_host_errors_and_mask_consistency():
         return lib.tv_build_tree(tv._ctx(DEV), p(d_r), p(d_t), p(d_p), B, N, k, k_root, thr, md, p(outs[0]),
                                  p(outs[1]), None, None, None, None)
 
-    assert call(N=65) == tv.UNSUPPORTED
+    assert call(N=129) == tv.UNSUPPORTED
     assert call(k=33, k_root=3) == tv.UNSUPPORTED
     assert call(k_root=11) == tv.INVALID_ARG
     assert call(md=0) == tv.INVALID_ARG

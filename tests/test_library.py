@@ -33,10 +33,10 @@ def test_status_strings_and_host_queries():
     chunks = (128256 + 8191) // 8192
     assert tv.tv_accept_workspace_bytes(8, 64, 128256, tv.GREEDY) == 8 * 64 * chunks * 8
     assert tv.tv_accept_workspace_bytes(128, 5, 32000, tv.STOCHASTIC) == \
-        (128 * 5 * 2 * 4 * 2 + 128 * 2 * 32000) * 8 + (128 * 16 + 64 * 256 * 4) * 8
+        (128 * 5 * 2 * 4 * 2 + 128 * 2 * 32000) * 8 + (128 * 16 + 128 * 256 * 4) * 8
     assert tv.tv_accept_workspace_bytes(0, 5, 32000, tv.GREEDY) == 0
     # a NULL context is rejected before anything touches a device
-    assert lib.tv_build_mask(None, None, 1, 1, None, None) == tv.INVALID_ARG
+    assert lib.tv_build_mask(None, None, None, 1, 1, None, None) == tv.INVALID_ARG
     assert lib.tv_tau_reset(None) == tv.INVALID_ARG
     assert lib.tv_commit(None, None, None, 0, None, 0, None, 0, None, None, None, None, 1, 4, 1, 128, None, None,
                          None) == tv.INVALID_ARG

@@ -49,14 +49,15 @@ def _load():
         lib.tv_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp]
         lib.tv_destroy.argtypes = [vp]
         lib.tv_set_stream.argtypes = [vp, vp]
-        lib.tv_build_mask.argtypes = [vp, vp, i32, i32, vp, vp]
+        lib.tv_build_mask.argtypes = [vp, vp, vp, i32, i32, vp, vp]
         lib.tv_attention_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32]
         lib.tv_attention_workspace_bytes.restype = sz
-        lib.tv_attention.argtypes = [vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, f32, vp,
-                                     ctypes.c_int, vp, sz]
+        lib.tv_attention.argtypes = [vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, f32,
+                                     vp, ctypes.c_int, vp, sz]
         lib.tv_accept_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
         lib.tv_accept_workspace_bytes.restype = sz
-        lib.tv_accept.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, f32, vp, vp, vp, vp, vp, sz]
+        lib.tv_accept.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, f32, vp, vp, vp, vp, vp,
+                                  sz]
         lib.tv_build_tree.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
         lib.tv_commit.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         lib.tv_tau.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]
@@ -106,8 +107,10 @@ def _check(s: int, what: str):
         raise TVError(s, what)
 
 
-def tv_build_mask(parents: torch.Tensor, mask: Optional[torch.Tensor] = None, depth: Optional[torch.Tensor] = None):
-    """parents int32 [B][N] -> (mask uint64-as-int64 [B][N][1], depth int32 [B][N])."""
+def tv_build_mask(parents: torch.Tensor, mask: Optional[torch.Tensor] = None, depth: Optional[torch.Tensor] = None,
+                  tree_sizes: Optional[torch.Tensor] = None):
+    """parents int32 [B][N] (N <= 128), tree_sizes int32 [B] or None ->
+    (mask uint64-as-int64 [B][N][ceil(N/64)], depth int32 [B][N])."""
     B, N = parents.shape
     dev = parents.device
     W = max((N + 63) // 64, 1)
@@ -116,14 +119,15 @@ def tv_build_mask(parents: torch.Tensor, mask: Optional[torch.Tensor] = None, de
     if depth is None:
         depth = torch.empty((B, N), dtype=torch.int32, device=dev)
     assert parents.dtype == torch.int32
-    _check(_load().tv_build_mask(_ctx(dev), _ptr(parents), B, N, _ptr(mask), _ptr(depth)), "tv_build_mask")
+    _check(_load().tv_build_mask(_ctx(dev), _ptr(parents), _ptr(tree_sizes), B, N, _ptr(mask), _ptr(depth)),
+           "tv_build_mask")
     return mask, depth
 
 
 def tv_build_tree(root_tokens: torch.Tensor, cand_tokens: torch.Tensor, cand_probs: torch.Tensor, k_root: int,
                   threshold: float, max_depth: int, outputs: Optional[dict] = None) -> dict:
     """root_tokens int32 [B]; cand_tokens int32 / cand_probs fp32 [B][N][k] ->
-    dict(parents, tokens, depth [B][N] int32, mask int64 [B][N][1], scores fp64 [B][N], n_nodes [B])."""
+    dict(parents, tokens, depth [B][N] int32, mask int64 [B][N][W], scores fp64 [B][N], n_nodes [B])."""
     B, N, k = cand_tokens.shape
     assert cand_probs.shape == cand_tokens.shape and cand_probs.dtype == torch.float32
     assert cand_tokens.dtype == torch.int32 and root_tokens.dtype == torch.int32
@@ -132,7 +136,7 @@ def tv_build_tree(root_tokens: torch.Tensor, cand_tokens: torch.Tensor, cand_pro
         outputs = dict(parents=torch.empty((B, N), dtype=torch.int32, device=dev),
                        tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
                        depth=torch.empty((B, N), dtype=torch.int32, device=dev),
-                       mask=torch.empty((B, N, 1), dtype=torch.int64, device=dev),
+                       mask=torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=dev),
                        scores=torch.empty((B, N), dtype=torch.float64, device=dev),
                        n_nodes=torch.empty(B, dtype=torch.int32, device=dev))
     o = outputs
@@ -150,9 +154,10 @@ def tv_attention_workspace_bytes(device, B, N, Hq, Hkv, D, max_prefix_len) -> in
 def tv_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
                  prefix_lens: torch.Tensor, max_prefix_len: int, tree_mask: Optional[torch.Tensor], sm_scale: float,
                  out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
-                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 workspace: Optional[torch.Tensor] = None, tree_sizes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """q bf16 [B][N][Hq][D]; k/v_pages bf16 [P][Hkv][16][D]; page_table int32 [B][maxp];
-    prefix_lens int32 [B]; tree_mask int64 [B][N][1] or None -> out [B][N][Hq][D]."""
+    prefix_lens int32 [B]; tree_mask int64 [B][N][W] or None; tree_sizes int32 [B] or None
+    -> out [B][N][Hq][D] (rows of absent nodes are not written)."""
     B, N, Hq, D = q.shape
     P, Hkv, page, D2 = k_pages.shape
     assert page == 16 and D2 == D and q.dtype == torch.bfloat16 and k_pages.dtype == torch.bfloat16
@@ -168,7 +173,8 @@ def tv_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_load().tv_attention(h, _ptr(q), _ptr(k_pages), _ptr(v_pages), P, _ptr(page_table), page_table.shape[1],
-                                _ptr(prefix_lens), int(max_prefix_len), _ptr(tree_mask), B, N, Hq, Hkv, D,
+                                _ptr(prefix_lens), int(max_prefix_len), _ptr(tree_mask), _ptr(tree_sizes), B, N,
+                                Hq, Hkv, D,
                                 float(sm_scale), _ptr(out), odt, _ptr(workspace), ws_bytes), "tv_attention")
     return out
 
@@ -180,7 +186,7 @@ def tv_accept_workspace_bytes(B, N, V, mode=GREEDY) -> int:
 def tv_accept(target_logits: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor, mode: int = GREEDY,
               draft_logits: Optional[torch.Tensor] = None, uniforms: Optional[torch.Tensor] = None,
               temperature: float = 1.0, outputs: Optional[dict] = None, want_argmax: bool = True,
-              workspace: Optional[torch.Tensor] = None) -> dict:
+              workspace: Optional[torch.Tensor] = None, tree_sizes: Optional[torch.Tensor] = None) -> dict:
     """Returns dict(accept_len [B], path [B][N], bonus [B], target_argmax [B][N] (greedy))."""
     B, N, V = target_logits.shape
     dev = target_logits.device
@@ -196,7 +202,7 @@ def tv_accept(target_logits: torch.Tensor, draft_tokens: torch.Tensor, parents: 
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_load().tv_accept(_ctx(dev), _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(parents),
-                             _ptr(uniforms), B, N, V, mode, float(temperature), _ptr(outputs["accept_len"]),
+                             _ptr(tree_sizes), _ptr(uniforms), B, N, V, mode, float(temperature), _ptr(outputs["accept_len"]),
                              _ptr(outputs["path"]), _ptr(outputs["bonus"]), _ptr(outputs.get("target_argmax")),
                              _ptr(workspace), ws_bytes), "tv_accept")
     return outputs

@@ -53,12 +53,16 @@ __device__ inline unsigned long long pack_key(float v, int x) {
 
 __device__ inline unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
 
+__device__ inline int size_of(const int32_t *sizes, int64_t b, int N) { return sizes ? sizes[b] : N; }
+
 template <bool kVec>
-__global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__restrict__ logits, int V, int chunks,
-                                                                unsigned long long *__restrict__ keys) {
+__global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__restrict__ logits,
+                                                                const int32_t *__restrict__ sizes, int N, int V,
+                                                                int chunks, unsigned long long *__restrict__ keys) {
   __shared__ unsigned long long red[kThreads / 64];
   const int chunk = blockIdx.x;
   const int64_t row = blockIdx.y;
+  if (sizes && row % N >= sizes[row / N]) return;  // an absent node: its row is never read
   const float *p = logits + row * V;
   const int x0 = chunk * kChunk;
   const int x1 = min(x0 + kChunk, V);
@@ -96,10 +100,13 @@ __global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__r
   }
 }
 
-// One wavefront per sequence; lane = node.
+// One wavefront per sequence; lane i holds node i (and node i + 64 when
+// H = 2). Ancestor sets are 128-bit (nodes 0..63 in word 0, 64..127 in word 1).
+template <int H>
 __global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long long *__restrict__ keys, int chunks,
                                                           const int32_t *__restrict__ draft_tokens,
-                                                          const int32_t *__restrict__ parents, int B, int N, int V,
+                                                          const int32_t *__restrict__ parents,
+                                                          const int32_t *__restrict__ sizes, int B, int N, int V,
                                                           int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
                                                           int32_t *__restrict__ bonus,
                                                           int32_t *__restrict__ target_argmax,
@@ -107,25 +114,39 @@ __global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long lo
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (b >= B) return;
-  const bool live = lane < N;
-  const int64_t idx = static_cast<int64_t>(b) * N + lane;
-  int y = 0;
-  if (live) {
-    unsigned long long best = 0ull;
-    for (int c = 0; c < chunks; ++c) best = umax64(best, keys[idx * chunks + c]);
-    y = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
+  const int nb = size_of(sizes, b, N);
+  const bool bad_size = nb < 1 || nb > N;
+  bool live[H], bad_tree = false, bad_tok = false;
+  int y[H], par[H], tok[H];
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const int i = lane + 64 * k;
+    const int64_t idx = static_cast<int64_t>(b) * N + i;
+    live[k] = !bad_size && i < nb;
+    y[k] = -1;
+    if (live[k]) {
+      unsigned long long best = 0ull;
+      for (int c = 0; c < chunks; ++c) best = umax64(best, keys[idx * chunks + c]);
+      y[k] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
+    }
+    par[k] = live[k] ? parents[idx] : -1;
+    tok[k] = live[k] ? draft_tokens[idx] : 0;
+    bad_tree |= live[k] && (par[k] < -1 || par[k] >= i || (i == 0 && par[k] != -1));
+    bad_tok |= live[k] && i > 0 && (tok[k] < 0 || tok[k] >= V);
   }
-  const int par = live ? parents[idx] : -1;
-  const int tok = live ? draft_tokens[idx] : 0;
-  const bool bad_tree = live && (par < -1 || par >= lane || (lane == 0 && par != -1));
-  const bool bad_tok = live && lane > 0 && (tok < 0 || tok >= V);
   const bool tree_err = __ballot(bad_tree) != 0;
   const bool tok_err = __ballot(bad_tok) != 0;
-  if (tree_err || tok_err) {
-    if (lane == 0) raise_error(state, tree_err ? TV_ERR_INVALID_TREE : TV_ERR_INVALID_ARG);
-    if (live) {
-      path[idx] = -1;
-      if (target_argmax) target_argmax[idx] = y;
+  if (bad_size || tree_err || tok_err) {
+    if (lane == 0)
+      raise_error(state, bad_size ? TV_ERR_INVALID_ARG : tree_err ? TV_ERR_INVALID_TREE : TV_ERR_INVALID_ARG);
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const int i = lane + 64 * k;
+      if (i < N) {
+        const int64_t idx = static_cast<int64_t>(b) * N + i;
+        path[idx] = -1;
+        if (target_argmax) target_argmax[idx] = y[k];
+      }
     }
     if (lane == 0) {
       accept_len[b] = -1;
@@ -133,44 +154,117 @@ __global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long lo
     }
     return;
   }
-  // ancestor-or-self masks by pointer doubling (parents precede children)
-  unsigned long long anc = live ? (1ull << lane) : 0ull;
-  int jump = live ? par : -1;
+  // ancestor-or-self sets by pointer doubling (parents precede children):
+  // node j's values are in lane j % 64, half j / 64
+  unsigned long long a0[H], a1[H];
+  int jump[H];
 #pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    const int src = jump >= 0 ? jump : lane;
-    const unsigned long long a_src = shfl_u64(anc, src);
-    const int j_src = __shfl(jump, src);
-    if (jump >= 0) {
-      anc |= a_src;
-      jump = j_src;
+  for (int k = 0; k < H; ++k) {
+    a0[k] = live[k] && k == 0 ? (1ull << lane) : 0ull;
+    a1[k] = live[k] && k == 1 ? (1ull << lane) : 0ull;
+    jump[k] = live[k] ? par[k] : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < (H == 1 ? 6 : 7); ++r) {
+    unsigned long long n0[H], n1[H];
+    int nj[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const int j = jump[k] >= 0 ? jump[k] : lane + 64 * k;
+      const int src = j & 63;
+      unsigned long long s0 = shfl_u64(a0[0], src), s1 = shfl_u64(a1[0], src);
+      int sj = __shfl(jump[0], src);
+      if (H == 2) {
+        const unsigned long long t0 = shfl_u64(a0[H - 1], src), t1 = shfl_u64(a1[H - 1], src);
+        const int tj = __shfl(jump[H - 1], src);
+        if (j >= 64) {
+          s0 = t0;
+          s1 = t1;
+          sj = tj;
+        }
+      }
+      n0[k] = a0[k];
+      n1[k] = a1[k];
+      nj[k] = jump[k];
+      if (jump[k] >= 0) {
+        n0[k] |= s0;
+        n1[k] |= s1;
+        nj[k] = sj;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      a0[k] = n0[k];
+      a1[k] = n1[k];
+      jump[k] = nj[k];
     }
   }
   // node c >= 1 matches iff its token is the target's argmax at its parent
-  const int y_par = __shfl(y, par >= 0 ? par : 0);
-  const bool match = live && (lane == 0 || (par >= 0 && tok == y_par));
-  const unsigned long long match_bits = __ballot(match);
-  const bool ok = live && (anc & 1ull) && ((anc & ~match_bits) == 0ull);
-  // deepest ok node; ties -> lexicographically smallest root path
-  int depth = ok ? __popcll(anc) : 0;
-  int dmax = depth;
-  for (int m = 32; m >= 1; m >>= 1) dmax = max(dmax, __shfl_xor(dmax, m));
-  unsigned long long key = (ok && depth == dmax) ? __brevll(anc) : 0ull;
-  for (int m = 32; m >= 1; m >>= 1) key = umax64(key, shfl_xor_u64(key, m));
-  const unsigned long long chosen = __brevll(key);  // the chosen path's node set; always holds node 0
-  const int len = __popcll(chosen);
-  const int last = 63 - __clzll(static_cast<long long>(chosen));
-  const int y_last = __shfl(y, last);
-  if (live) {
-    // lane p writes the p-th node of the path (the p-th set bit of `chosen`)
-    int node = -1;
-    if (lane < len) {
-      unsigned long long rest = chosen;
-      for (int q = 0; q < lane; ++q) rest &= rest - 1ull;
-      node = __ffsll(static_cast<long long>(rest)) - 1;
+  bool match[H];
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const int pp = par[k] >= 0 ? par[k] : 0;
+    int y_par = __shfl(y[0], pp & 63);
+    if (H == 2) {
+      const int y_hi = __shfl(y[H - 1], pp & 63);
+      if (pp >= 64) y_par = y_hi;
     }
-    path[idx] = node;
-    if (target_argmax) target_argmax[idx] = y;
+    match[k] = live[k] && (lane + 64 * k == 0 || (par[k] >= 0 && tok[k] == y_par));
+  }
+  const unsigned long long m0 = __ballot(match[0]);
+  const unsigned long long m1 = H == 2 ? __ballot(match[H - 1]) : 0ull;
+  // deepest ok node (every node on its root path matches); ties -> the
+  // lexicographically smallest root path, i.e. the largest bit-reversed set
+  // (node ids increase along a path, so the first differing path element is
+  // the lowest differing set bit)
+  int dmax = 0;
+  bool ok[H];
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    ok[k] = live[k] && (a0[k] & 1ull) && ((a0[k] & ~m0) == 0ull) && ((a1[k] & ~m1) == 0ull);
+    if (ok[k]) dmax = max(dmax, __popcll(a0[k]) + __popcll(a1[k]));
+  }
+  for (int m = 32; m >= 1; m >>= 1) dmax = max(dmax, __shfl_xor(dmax, m));
+  unsigned long long khi = 0ull, klo = 0ull;  // key = (brev(word 0), brev(word 1))
+#pragma unroll
+  for (int k = 0; k < H; ++k)
+    if (ok[k] && __popcll(a0[k]) + __popcll(a1[k]) == dmax) {
+      const unsigned long long h = __brevll(a0[k]), l = __brevll(a1[k]);
+      if (h > khi || (h == khi && l > klo)) {
+        khi = h;
+        klo = l;
+      }
+    }
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned long long oh = shfl_xor_u64(khi, m), ol = shfl_xor_u64(klo, m);
+    if (oh > khi || (oh == khi && ol > klo)) {
+      khi = oh;
+      klo = ol;
+    }
+  }
+  const unsigned long long c0 = __brevll(khi), c1 = __brevll(klo);  // the chosen path's set; holds node 0
+  const int len = __popcll(c0) + __popcll(c1);
+  const int last = c1 ? 64 + 63 - __clzll(static_cast<long long>(c1)) : 63 - __clzll(static_cast<long long>(c0));
+  int y_last = __shfl(y[0], last & 63);
+  if (H == 2) {
+    const int y_hi = __shfl(y[H - 1], last & 63);
+    if (last >= 64) y_last = y_hi;
+  }
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const int pos = lane + 64 * k;  // writes the pos-th node of the path (the pos-th set bit)
+    if (pos < N) {
+      int node = -1;
+      if (pos < len) {
+        const int n0 = __popcll(c0);
+        unsigned long long rest = pos < n0 ? c0 : c1;
+        for (int q = pos < n0 ? pos : pos - n0; q > 0; --q) rest &= rest - 1ull;
+        node = (pos < n0 ? 0 : 64) + __ffsll(static_cast<long long>(rest)) - 1;
+      }
+      const int64_t idx = static_cast<int64_t>(b) * N + pos;
+      path[idx] = node;
+      if (target_argmax) target_argmax[idx] = y[k];
+    }
   }
   if (lane == 0) {
     accept_len[b] = len;
@@ -248,7 +342,8 @@ __device__ inline double div_t(double x, double T, double invT) {
 
 template <bool kVec>
 __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__restrict__ target,
-                                                                 const float *__restrict__ draft, int N, int V,
+                                                                 const float *__restrict__ draft,
+                                                                 const int32_t *__restrict__ sizes, int N, int V,
                                                                  int chunks, double T, double invT,
                                                                  double *__restrict__ stats,
                                                                  unsigned long long *__restrict__ counters) {
@@ -257,6 +352,7 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
   const int64_t row = blockIdx.y;  // b * N + j
   const int which = blockIdx.z;    // 0 = target, 1 = draft
   const int j = static_cast<int>(row % N);
+  if (sizes && j > 0 && j >= sizes[row / N]) return;  // an absent node: its rows are never read
   double *out = stats + ((row * 2 + which) * chunks + chunk) * 2;
   // the path pass's exchange counter of this sequence starts at zero
   if (counters && chunk == 0 && which == 0 && j == 0 && threadIdx.x == 0) counters[(row / N) * 16] = 0ull;
@@ -341,7 +437,7 @@ __device__ inline double prob_at(const float *row, int x, double T, double invT,
 constexpr int kPathThreads = 512;
 constexpr int kBlk = 16;          // tokens per register block of a row sweep
 constexpr int kMaxGrid = 256;     // workgroups of a path pass that exchange partial sums
-constexpr int kMaxExchanges = 64; // exchanges per sequence: < N stored residuals + 2 draw passes
+constexpr int kMaxExchanges = 128;  // exchanges per sequence: < N stored residuals + 2 draw passes
 constexpr int kCounterStride = 16;  // one 128-byte line per sequence counter
 constexpr int kSpinLimit = 1 << 22;
 
@@ -374,16 +470,17 @@ struct Pi {
 template <bool kVec>
 __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
-    const int32_t *__restrict__ parents, const float *__restrict__ uniforms, int B, int N, int V, int chunks,
-    double T, double invT, const double *__restrict__ stats, double *__restrict__ wbuf,
+    const int32_t *__restrict__ parents, const int32_t *__restrict__ sizes, const float *__restrict__ uniforms,
+    int B, int N, int V, int chunks, double T, double invT, const double *__restrict__ stats,
+    double *__restrict__ wbuf,
     unsigned long long *__restrict__ sync, int K, int slice, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ path, int32_t *__restrict__ bonus, unsigned long long *state) {
   __shared__ int s_err, s_ok, s_pick, s_cross, s_cross_last, s_lp;
   __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total, s_cprefix, s_wt_new, s_wt_old;
-  __shared__ double s_pa[64], s_qa[64], s_u[64];
-  __shared__ RowStat s_tst[64], s_dst[64];  // merged statistics of every target and draft row
-  __shared__ int s_tok[64], s_path[64];
-  __shared__ unsigned long long s_child[64];
+  __shared__ double s_pa[128], s_qa[128], s_u[128];
+  __shared__ RowStat s_tst[128], s_dst[128];  // merged statistics of every target and draft row
+  __shared__ int s_tok[128], s_path[128];
+  __shared__ unsigned long long s_child[128][2];  // children of each node: ids 0..63, 64..127
   __shared__ double s_part[kMaxGrid], s_xnew[kMaxGrid], s_xold[kMaxGrid];
   __shared__ int s_xlp[kMaxGrid];
   __shared__ double s_tab[64];
@@ -392,43 +489,60 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   const int64_t base = static_cast<int64_t>(b) * N;
   if (wid == 0) {
     exp_table_init(s_tab, lane);  // wavefront 0 fills it and uses it first
-    // validation with the same precedence as a serial check: a bad parent
-    // anywhere, then a draft token outside [0, V)
+    // validation with the same precedence as a serial check: a node count
+    // outside [1, N], a bad parent among the present nodes, then a draft
+    // token outside [0, V). Lane i holds nodes i and i + 64.
+    const int nb = sizes ? sizes[b] : N;
+    const bool bad_size = nb < 1 || nb > N;
     bool tree_bad = false, tok_bad = false;
-    int p = -1, t = 0;
-    if (lane < N) {
-      p = parents[base + lane];
-      tree_bad = p < -1 || p >= lane || (lane == 0 && p != -1);
-      if (lane >= 1) {
-        t = draft_tokens[base + lane];
-        tok_bad = t < 0 || t >= V;
+    int p[2], t[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      p[h] = -1;
+      t[h] = 0;
+      if (!bad_size && i < nb) {
+        p[h] = parents[base + i];
+        tree_bad |= p[h] < -1 || p[h] >= i || (i == 0 && p[h] != -1);
+        if (i >= 1) {
+          t[h] = draft_tokens[base + i];
+          tok_bad |= t[h] < 0 || t[h] >= V;
+        }
       }
-      s_u[lane] = static_cast<double>(uniforms[base + lane]);
+      if (i < N) s_u[i] = static_cast<double>(uniforms[base + i]);
     }
-    const int err = __builtin_amdgcn_ballot_w64(tree_bad) ? TV_ERR_INVALID_TREE
-                    : __builtin_amdgcn_ballot_w64(tok_bad) ? TV_ERR_INVALID_ARG
-                                                           : 0;
-    const bool live = !err && lane < N;
-    const RowStat st = live ? merge_stats(stats, base + lane, 0, chunks, s_tab) : RowStat{0.0, 1.0, 1.0};
-    const RowStat sd =
-        live && lane >= 1 ? merge_stats(stats, base + lane, 1, chunks, s_tab) : RowStat{0.0, 1.0, 1.0};
-    // the parent's target statistics, from its lane
-    const int src = p >= 0 ? p : lane;
-    const RowStat sp{__shfl(st.m, src), __shfl(st.Z, src), __shfl(st.invZ, src)};
-    if (live) {
-      s_tst[lane] = st;
-      s_dst[lane] = sd;
-      if (lane >= 1) {
-        s_tok[lane] = t;
-        if (p >= 0) {  // a node without a parent (forest) is never tested
-          s_pa[lane] = prob_at(target + (base + p) * V, t, T, invT, sp, s_tab);
-          s_qa[lane] = prob_at(draft + (base + lane) * V, t, T, invT, sd, s_tab);
+    const int err = bad_size                                 ? TV_ERR_INVALID_ARG
+                    : __builtin_amdgcn_ballot_w64(tree_bad) ? TV_ERR_INVALID_TREE
+                    : __builtin_amdgcn_ballot_w64(tok_bad)  ? TV_ERR_INVALID_ARG
+                                                            : 0;
+    // row statistics of every present node, then its first test's p(t_c)
+    // (under its parent's target row) and q_c(t_c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      if (!err && i < nb) {
+        s_tst[i] = merge_stats(stats, base + i, 0, chunks, s_tab);
+        s_dst[i] = i >= 1 ? merge_stats(stats, base + i, 1, chunks, s_tab) : RowStat{0.0, 1.0, 1.0};
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      if (!err && i >= 1 && i < nb) {
+        s_tok[i] = t[h];
+        if (p[h] >= 0) {  // a node without a parent (forest) is never tested
+          s_pa[i] = prob_at(target + (base + p[h]) * V, t[h], T, invT, s_tst[p[h]], s_tab);
+          s_qa[i] = prob_at(draft + (base + i) * V, t[h], T, invT, s_dst[i], s_tab);
         }
       }
     }
-    for (int n = 0; n < N; ++n) {
-      const uint64_t kids = __builtin_amdgcn_ballot_w64(!err && lane >= 1 && lane < N && p == n);
-      if (lane == 0) s_child[n] = kids;
+    for (int n = 0; n < (err ? 0 : nb); ++n) {
+      const uint64_t k0 = __builtin_amdgcn_ballot_w64(lane >= 1 && lane < nb && p[0] == n);
+      const uint64_t k1 = __builtin_amdgcn_ballot_w64(lane + 64 < nb && p[1] == n);
+      if (lane == 0) {
+        s_child[n][0] = k0;
+        s_child[n][1] = k1;
+      }
     }
     if (lane == 0) {
       s_err = err;
@@ -625,17 +739,23 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   for (;;) {
     const float *P = target + (base + node) * V;
     const RowStat sp = s_tst[node];
-    uint64_t kids = s_child[node];
+    uint64_t kids0 = s_child[node][0], kids1 = s_child[node][1];  // children still to test, in id order
     int acc = -1;
-    while (kids) {
-      const int c = __builtin_ctzll(kids);
-      kids &= kids - 1;
+    while (kids0 | kids1) {
+      int c;
+      if (kids0) {
+        c = __builtin_ctzll(kids0);
+        kids0 &= kids0 - 1;
+      } else {
+        c = 64 + __builtin_ctzll(kids1);
+        kids1 &= kids1 - 1;
+      }
       const double a = pi.w ? (wt * pi.invM) / s_qa[c] : s_pa[c] / s_qa[c];
       if (s_u[c - 1] < a) {
         acc = c;
         break;
       }
-      if (!kids) {  // the last sibling: its residual is built on the fly by the final draw
+      if (!(kids0 | kids1)) {  // the last sibling: its residual is built on the fly by the final draw
         pend = c;
         break;
       }
@@ -643,7 +763,8 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       const RowStat sq = s_dst[c];
       double local, prefix;
       int lastpos;
-      sweep(P, sp, pi, draft + (base + c) * V, sq, dst, s_tok[__builtin_ctzll(kids)], local, lastpos);
+      const int next = kids0 ? __builtin_ctzll(kids0) : 64 + __builtin_ctzll(kids1);
+      sweep(P, sp, pi, draft + (base + c) * V, sq, dst, s_tok[next], local, lastpos);
       scan(local, lastpos, prefix);
       if (!(ok = exchange())) break;
       double total = 0.0, wnew = 0.0, wold = 0.0;
@@ -783,9 +904,10 @@ size_t accept_ws_bytes(int B, int N, int V, tv_accept_mode mode) {
 }
 
 tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits,
-                        const int32_t *draft_tokens, const int32_t *parents, const float *uniforms, int B, int N,
-                        int V, tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path,
-                        int32_t *bonus, int32_t *target_argmax, void *workspace) {
+                        const int32_t *draft_tokens, const int32_t *parents, const int32_t *tree_sizes,
+                        const float *uniforms, int B, int N, int V, tv_accept_mode mode, float temperature,
+                        int32_t *accept_len, int32_t *path, int32_t *bonus, int32_t *target_argmax,
+                        void *workspace) {
   const int chunks = (V + kChunk - 1) / kChunk;
   const dim3 blk(kThreads);
   const bool vec = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0 &&
@@ -794,12 +916,20 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
     auto *keys = static_cast<unsigned long long *>(workspace);
     const dim3 g1(chunks, B * N);
     if (vec)
-      hipLaunchKernelGGL(argmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, V, chunks, keys);
+      hipLaunchKernelGGL(argmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, tree_sizes, N, V, chunks,
+                         keys);
     else
-      hipLaunchKernelGGL(argmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, V, chunks, keys);
+      hipLaunchKernelGGL(argmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, tree_sizes, N, V, chunks,
+                         keys);
     if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-    hipLaunchKernelGGL(greedy_path_kernel, dim3((B + 3) / 4), dim3(256), 0, ctx->stream, keys, chunks, draft_tokens,
-                       parents, B, N, V, accept_len, path, bonus, target_argmax, ctx->d_state);
+    if (N <= 64)
+      hipLaunchKernelGGL(greedy_path_kernel<1>, dim3((B + 3) / 4), dim3(256), 0, ctx->stream, keys, chunks,
+                         draft_tokens, parents, tree_sizes, B, N, V, accept_len, path, bonus, target_argmax,
+                         ctx->d_state);
+    else
+      hipLaunchKernelGGL(greedy_path_kernel<2>, dim3((B + 3) / 4), dim3(256), 0, ctx->stream, keys, chunks,
+                         draft_tokens, parents, tree_sizes, B, N, V, accept_len, path, bonus, target_argmax,
+                         ctx->d_state);
     return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
   }
   auto *stats = static_cast<double *>(workspace);
@@ -828,16 +958,17 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
   const dim3 g1(chunks, B * N, 2);
   unsigned long long *counters = K > 1 ? sync : nullptr;
   if (vec)
-    hipLaunchKernelGGL(softmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
-                       chunks, T, invT, stats, counters);
+    hipLaunchKernelGGL(softmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, draft_logits, tree_sizes,
+                       N, V, chunks, T, invT, stats, counters);
   else
-    hipLaunchKernelGGL(softmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, draft_logits, N, V,
-                       chunks, T, invT, stats, counters);
+    hipLaunchKernelGGL(softmax_chunk_kernel<false>, g1, blk, 0, ctx->stream, target_logits, draft_logits, tree_sizes,
+                       N, V, chunks, T, invT, stats, counters);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   unsigned long long *st = ctx->d_state;
   void *args[] = {const_cast<float **>(&target_logits), const_cast<float **>(&draft_logits),
                   const_cast<int32_t **>(&draft_tokens), const_cast<int32_t **>(&parents),
-                  const_cast<float **>(&uniforms), &B, &N, &V, const_cast<int *>(&chunks),
+                  const_cast<int32_t **>(&tree_sizes), const_cast<float **>(&uniforms), &B, &N, &V,
+                  const_cast<int *>(&chunks),
                   const_cast<double *>(&T), const_cast<double *>(&invT), &stats, &wbuf, &sync, &K,
                   const_cast<int *>(&slice), &accept_len, &path, &bonus, &st};
   const hipError_t e = K > 1 ? hipLaunchCooperativeKernel(path_fn, dim3(B * K), dim3(kPathThreads), args, 0,

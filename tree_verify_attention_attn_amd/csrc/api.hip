@@ -65,13 +65,13 @@ tv_status tv_set_stream(tv_ctx *ctx, void *hip_stream) {
   return TV_OK;
 }
 
-tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, int32_t B, int32_t N, uint64_t *mask,
-                        int32_t *depth) {
+tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, const int32_t *tree_sizes, int32_t B, int32_t N,
+                        uint64_t *mask, int32_t *depth) {
   if (!ctx || B < 0 || N < 0) return TV_ERR_INVALID_ARG;
-  if (N > 64) return TV_ERR_UNSUPPORTED;
+  if (N > 128) return TV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * N == 0) return TV_OK;
   if (!parents || !mask) return TV_ERR_INVALID_ARG;
-  return launch_build_mask(ctx, parents, B, N, mask, depth);
+  return launch_build_mask(ctx, parents, tree_sizes, B, N, mask, depth);
 }
 
 size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
@@ -82,13 +82,14 @@ size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t H
 
 tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const void *v_pages, int64_t num_pages,
                        const int32_t *page_table, int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len,
-                       const uint64_t *tree_mask, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                       float sm_scale, void *out, tv_dtype out_dtype, void *workspace, size_t workspace_bytes) {
+                       const uint64_t *tree_mask, const int32_t *tree_sizes, int32_t B, int32_t N, int32_t Hq,
+                       int32_t Hkv, int32_t D, float sm_scale, void *out, tv_dtype out_dtype, void *workspace,
+                       size_t workspace_bytes) {
   if (!ctx || B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || num_pages < 0 || maxp < 0 || max_prefix_len < 0)
     return TV_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return TV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
-  if (N > 64) return TV_ERR_UNSUPPORTED;
+  if (N > 128) return TV_ERR_UNSUPPORTED;
   if (!isfinite(sm_scale)) return TV_ERR_INVALID_ARG;
   if (out_dtype != TV_F32 && out_dtype != TV_BF16) return TV_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * N == 0) return TV_OK;
@@ -97,7 +98,7 @@ tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const vo
   const AttnPlan plan = plan_attention(ctx->cu_count, B, N, Hq, Hkv, D, max_prefix_len);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return TV_ERR_WORKSPACE;
   return launch_attention(ctx, plan, q, k_pages, v_pages, num_pages, page_table, maxp, prefix_lens, max_prefix_len,
-                          tree_mask, B, N, Hq, Hkv, D, sm_scale, out, out_dtype, workspace);
+                          tree_mask, tree_sizes, B, N, Hq, Hkv, D, sm_scale, out, out_dtype, workspace);
 }
 
 size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode mode) {
@@ -106,7 +107,8 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
 }
 
 tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
-                    const int32_t *parents, const float *uniforms, int32_t B, int32_t N, int32_t V,
+                    const int32_t *parents, const int32_t *tree_sizes, const float *uniforms, int32_t B, int32_t N,
+                    int32_t V,
                     tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path, int32_t *bonus_token,
                     int32_t *target_argmax, void *workspace, size_t workspace_bytes) {
   if (!ctx || B < 0 || V <= 0) return TV_ERR_INVALID_ARG;
@@ -114,13 +116,14 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
   if (mode == TV_STOCHASTIC && (!(temperature > 0.0f) || !isfinite(temperature))) return TV_ERR_INVALID_ARG;
   if (B == 0) return TV_OK;
   if (N < 1) return TV_ERR_INVALID_ARG;
-  if (N > 64) return TV_ERR_UNSUPPORTED;
+  if (N > 128) return TV_ERR_UNSUPPORTED;
   if (!target_logits || !draft_tokens || !parents || !accept_len || !path || !bonus_token) return TV_ERR_INVALID_ARG;
   if (mode == TV_STOCHASTIC && (!draft_logits || !uniforms)) return TV_ERR_INVALID_ARG;
   const size_t need = accept_ws_bytes(B, N, V, mode);
   if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
-  return launch_accept(ctx, target_logits, draft_logits, draft_tokens, parents, uniforms, B, N, V, mode, temperature,
-                       accept_len, path, bonus_token, mode == TV_GREEDY ? target_argmax : nullptr, workspace);
+  return launch_accept(ctx, target_logits, draft_logits, draft_tokens, parents, tree_sizes, uniforms, B, N, V, mode,
+                       temperature, accept_len, path, bonus_token, mode == TV_GREEDY ? target_argmax : nullptr,
+                       workspace);
 }
 
 tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages, const int32_t *page_table,
@@ -131,7 +134,7 @@ tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
   if (B == 0) return TV_OK;
   if (N < 1) return TV_ERR_INVALID_ARG;
-  if (N > 64) return TV_ERR_UNSUPPORTED;
+  if (N > 128) return TV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * Hkv > 0x7FFFFFFF) return TV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(maxp) * kPage < static_cast<int64_t>(max_prefix_len) + N) return TV_ERR_INVALID_ARG;
   if (!k_pages || !v_pages || !page_table || !prefix_lens || !draft_tokens || !path || !accept_len || !bonus_token ||
@@ -150,7 +153,7 @@ tv_status tv_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *
   if (k > 32) return TV_ERR_UNSUPPORTED;
   if (B == 0) return TV_OK;
   if (N < 1) return TV_ERR_INVALID_ARG;
-  if (N > 64) return TV_ERR_UNSUPPORTED;
+  if (N > 128) return TV_ERR_UNSUPPORTED;
   if (!root_tokens || !cand_tokens || !cand_probs || !parents || !tokens) return TV_ERR_INVALID_ARG;
   return launch_build_tree(ctx, root_tokens, cand_tokens, cand_probs, B, N, k, k_root, threshold, max_depth, parents,
                            tokens, depth, mask, scores, n_nodes);

@@ -50,6 +50,8 @@ struct AttnArgs {
   const uint16_t *q, *k, *v;
   const int32_t *page_table, *prefix_lens;
   const uint64_t *mask;
+  const int32_t *sizes;  // node count of each sequence, or null (all N)
+  int W;                 // mask words per row, ceil(N / 64)
   int64_t num_pages;
   int maxp, max_prefix_len;
   int B, N, Hq, Hkv, G, rows, rows_pad;
@@ -176,8 +178,15 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   const int b = bh / a.Hkv, g = bh % a.Hkv;
 
   const int L = a.prefix_lens[b];
-  const bool bad_len = L < 0 || L > a.max_prefix_len;
-  const int T = bad_len ? 0 : L + a.N;
+  // node count of this sequence: nodes past it are absent (no query rows,
+  // no keys); a count outside [1, N] is bad data, reported like a bad length
+  const int nb_in = a.sizes ? a.sizes[b] : a.N;
+  const bool bad_size = nb_in < 1 || nb_in > a.N;
+  const int nb = bad_size ? a.N : nb_in;
+  const int rows_b = nb * a.G;
+  if (rg * ROWS_WG >= rows_b) return;  // every row of this workgroup is absent
+  const bool bad_len = L < 0 || L > a.max_prefix_len || bad_size;
+  const int T = bad_len ? 0 : L + nb;
   const int tiles_b = (T + kKeys - 1) / kKeys;
   const int t_begin = s * a.chunk_tiles;
   const int t_end = min(t_begin + a.chunk_tiles, tiles_b);
@@ -186,12 +195,20 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 
   // ---- the wavefront's 32 query rows: B operands of S^T, kept in VGPRs
   const int row = rg * ROWS_WG + w * WROW + n;
-  const bool wave_active = rg * ROWS_WG + w * WROW < a.rows;
-  const bool row_ok = row < a.rows;
+  const bool wave_active = rg * ROWS_WG + w * WROW < rows_b;
+  const bool row_ok = row < rows_b;
   const int node = row_ok ? row / a.G : 0;
   const int head = g * a.G + (row_ok ? row % a.G : 0);
-  const uint64_t node_bits = a.N >= 64 ? ~0ull : ((1ull << a.N) - 1ull);  // tree positions that exist
-  const uint64_t mword = ((row_ok && a.mask) ? a.mask[static_cast<int64_t>(b) * a.N + node] : ~0ull) & node_bits;
+  // the row's ancestor mask over the present nodes: bits of nodes 0..63 in
+  // mw0, of nodes 64..127 in mw1 (all present nodes when there is no mask)
+  uint64_t mw0 = ~0ull, mw1 = ~0ull;
+  if (row_ok && a.mask) {
+    const int64_t mrow = (static_cast<int64_t>(b) * a.N + node) * a.W;
+    mw0 = a.mask[mrow];
+    mw1 = a.W > 1 ? a.mask[mrow + 1] : 0ull;
+  }
+  mw0 &= nb >= 64 ? ~0ull : ((1ull << nb) - 1ull);
+  mw1 &= nb <= 64 ? 0ull : (nb >= 128 ? ~0ull : ((1ull << (nb - 64)) - 1ull));
   bf16x8 qf[KS];
   {
     const uint16_t *qrow = a.q + ((static_cast<int64_t>(b) * a.N + node) * a.Hq + head) * D;
@@ -424,8 +441,20 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     // visibility (only tiles that reach the tree positions or the tail): one
     // 64-bit word per tile, bit k = key tile0 + k is visible to this row
     if (tile0 + kKeys > L) {
-      const int off = tile0 - L;  // key k of the tile is tree node off + k; -64 < off < N
-      const uint64_t tree = off >= 0 ? (mword >> off) : (mword << -off);
+      // key k of the tile is tree node off + k (-64 < off < nb): the 64-bit
+      // window of the row's 128-bit ancestor mask that starts at node off
+      const int off = tile0 - L;
+      uint64_t tree;
+      if (off < 0)
+        tree = mw0 << -off;
+      else if (off == 0)
+        tree = mw0;
+      else if (off < 64)
+        tree = (mw0 >> off) | (mw1 << (64 - off));
+      else if (off == 64)
+        tree = mw1;
+      else
+        tree = mw1 >> (off - 64);
       const int pre = L - tile0;  // keys k < pre belong to the prefix
       const uint64_t prefix = pre <= 0 ? 0ull : ((1ull << pre) - 1ull);
       const uint64_t vis64 = prefix | tree;
@@ -642,6 +671,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   if (r >= static_cast<int64_t>(a.B) * a.Hkv * a.rows) return;
   const int bh = static_cast<int>(r / a.rows), row = static_cast<int>(r % a.rows);
   const int b = bh / a.Hkv, g = bh % a.Hkv;
+  const int nb_in = a.sizes ? a.sizes[b] : a.N;
+  const int nb = (nb_in < 1 || nb_in > a.N) ? a.N : nb_in;
+  if (row >= nb * a.G) return;  // an absent node's row has no output
   const int64_t slot0 = static_cast<int64_t>(bh) * a.S * a.rows_pad + row;
   float M = -INFINITY;
   bool bad = false;
@@ -742,8 +774,9 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
 
 tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, const void *k_pages,
                            const void *v_pages, int64_t num_pages, const int32_t *page_table, int maxp,
-                           const int32_t *prefix_lens, int max_prefix_len, const uint64_t *tree_mask, int B, int N,
-                           int Hq, int Hkv, int D, float sm_scale, void *out, tv_dtype out_dtype, void *workspace) {
+                           const int32_t *prefix_lens, int max_prefix_len, const uint64_t *tree_mask,
+                           const int32_t *tree_sizes, int B, int N, int Hq, int Hkv, int D, float sm_scale, void *out,
+                           tv_dtype out_dtype, void *workspace) {
   AttnArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.k = static_cast<const uint16_t *>(k_pages);
@@ -751,6 +784,8 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   a.page_table = page_table;
   a.prefix_lens = prefix_lens;
   a.mask = tree_mask;
+  a.sizes = tree_sizes;
+  a.W = (N + 63) / 64;
   a.num_pages = num_pages;
   a.maxp = maxp;
   a.max_prefix_len = max_prefix_len;

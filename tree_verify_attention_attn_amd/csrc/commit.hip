@@ -10,10 +10,10 @@
 // ... < v_{n-1} is compacted to L..L+n-1: row L+m receives row L+v_m. Since
 // v_m >= m, only the rows after the path's identity prefix (v_m == m) move.
 //
-// One workgroup per (sequence, KV head). Every wavefront validates the
-// sequence itself (lane m = path entry m) and keeps the source / destination
-// row offsets in its lanes; the workgroup loads every moved row into
-// registers, waits for all of its loads, meets at a barrier, then stores.
+// One workgroup per (sequence, KV head). Thread m checks path entry m and
+// puts its source / destination row offsets in LDS; the workgroup loads
+// every moved row into registers, waits for all of its loads, meets at a
+// barrier, then stores.
 // Reading everything first makes overlapping moves (a row that is both a
 // source and a destination) safe. Workgroups touch disjoint rows: different
 // KV heads, or different sequences (which own the pages of their tree
@@ -35,32 +35,36 @@ __global__ void __launch_bounds__(kCommitThreads)
                   const int32_t *__restrict__ accept_len, const int32_t *__restrict__ bonus, int N, int Hkv,
                   int32_t *__restrict__ new_prefix_lens, int32_t *__restrict__ emitted, int32_t *__restrict__ next_root,
                   unsigned long long *state) {
-  constexpr int CH = D / 8;                                     // 16-byte chunks per row
-  constexpr int NPT = (63 * 2 * CH + kCommitThreads - 1) / kCommitThreads;  // chunks per thread, worst case
+  constexpr int CH = D / 8;                                       // 16-byte chunks per row
+  constexpr int NPT = (127 * 2 * CH + kCommitThreads - 1) / kCommitThreads;  // chunks per thread, worst case
+  __shared__ int s_v[128];                 // path entries
+  __shared__ int64_t s_src[128], s_dst[128];  // their source and destination rows, in chunks
   const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
-  const int tid = threadIdx.x, m = tid & 63;
+  const int tid = threadIdx.x, m = tid;  // threads 0..127: path entry m
 
   const int L = prefix_lens[b];
   const int len = accept_len[b];
   const int bon = bonus[b];
-  bool bad = L < 0 || L > max_prefix_len || len < 1 || len > N || bon < 0;
-  const bool live = !bad && m < len;
+  const bool bad0 = L < 0 || L > max_prefix_len || len < 1 || len > N || bon < 0;
+  const bool live = !bad0 && m < len;
   const int v = live ? path[static_cast<int64_t>(b) * N + m] : 0;
-  const int prev = __shfl(v, m == 0 ? 0 : m - 1);
+  if (m < 128) s_v[m] = v;
+  __syncthreads();
+  const int prev = m >= 1 && m < 128 ? s_v[m - 1] : 0;
   // a valid path has v_m >= m, so no page-table index below L is formed
   bool lane_bad = live && (m == 0 ? v != 0 : (v <= prev || v < m || v >= N));
-  int64_t src = 0, dst = 0;  // row offsets in chunks
   if (live && !lane_bad) {
     const int ts = L + v, td = L + m;
     const int ps = page_table[static_cast<int64_t>(b) * maxp + ts / kPage];
     const int pd = page_table[static_cast<int64_t>(b) * maxp + td / kPage];
     lane_bad = ps < 0 || ps >= num_pages || pd < 0 || pd >= num_pages;
-    src = ((static_cast<int64_t>(ps) * Hkv + g) * kPage + ts % kPage) * CH;
-    dst = ((static_cast<int64_t>(pd) * Hkv + g) * kPage + td % kPage) * CH;
+    s_src[m] = ((static_cast<int64_t>(ps) * Hkv + g) * kPage + ts % kPage) * CH;
+    s_dst[m] = ((static_cast<int64_t>(pd) * Hkv + g) * kPage + td % kPage) * CH;
   }
-  bad = bad || __ballot(lane_bad) != 0;
+  const bool bad = bad0 || __syncthreads_or(lane_bad);
   // the path starts with an identity run v_m == m; rows from m0 on move
-  const int m0 = bad ? len : __popcll(__ballot(live && v == m));
+  const int run = __syncthreads_count(live && v == m);
+  const int m0 = bad ? len : run;
   const int total = bad ? 0 : (len - m0) * 2 * CH;
 
   if (total > 0) {
@@ -71,8 +75,7 @@ __global__ void __launch_bounds__(kCommitThreads)
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int cc = min(tid + kCommitThreads * i, total - 1);
-      const int64_t s = __shfl(src, m0 + cc / (2 * CH));
-      r[i] = (((cc / CH) & 1) ? v_pages : k_pages)[s + cc % CH];
+      r[i] = (((cc / CH) & 1) ? v_pages : k_pages)[s_src[m0 + cc / (2 * CH)] + cc % CH];
     }
     // every row of this (sequence, head) is read before any is written
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -81,17 +84,15 @@ __global__ void __launch_bounds__(kCommitThreads)
     for (int i = 0; i < NPT; ++i) {
       const int c = tid + kCommitThreads * i;
       const int cc = min(c, total - 1);
-      const int64_t d = __shfl(dst, m0 + cc / (2 * CH));
-      if (c < total) (((cc / CH) & 1) ? v_pages : k_pages)[d + cc % CH] = r[i];
+      if (c < total) (((cc / CH) & 1) ? v_pages : k_pages)[s_dst[m0 + cc / (2 * CH)] + cc % CH] = r[i];
     }
   }
 
-  if (g == 0 && tid < 64) {
+  if (g == 0 && m < N) {
     // emitted: the accepted drafts (path nodes 1..len-1), then the bonus
-    const int vn = __shfl(v, min(m + 1, 63));
-    if (emitted && m < N) {
+    if (emitted) {
       int tok = -1;
-      if (!bad && m < len - 1) tok = draft_tokens[static_cast<int64_t>(b) * N + vn];
+      if (!bad && m < len - 1) tok = draft_tokens[static_cast<int64_t>(b) * N + s_v[m + 1]];
       if (!bad && m == len - 1) tok = bon;
       emitted[static_cast<int64_t>(b) * N + m] = tok;
     }

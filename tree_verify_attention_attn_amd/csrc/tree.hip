@@ -11,13 +11,14 @@
 // ancestor masks, ready for the attention call.
 //
 // One wavefront per sequence. The sequence's proposal table (row i: what the
-// draft head proposes for the node created i-th, at most 64 x 32 entries) is
+// draft head proposes for the node created i-th, at most 128 x 32 entries) is
 // copied into LDS first, so every pop is LDS and register work: a
 // lane-strided scan of the candidate pool for each lane's best (score, queue
 // position), a wavefront maximum of those pairs moved with DPP row shifts and
-// broadcasts, and the new node's fields kept in lane `node` (parent, token,
-// depth, score, ancestor mask). Accepted children are appended in slot order
-// through a ballot prefix, which keeps the queue order of the definition.
+// broadcasts, and the new node's fields kept by lane node % 64, half
+// node / 64 (parent, token, depth, score, two-word ancestor set). Accepted
+// children are appended in slot order through a ballot prefix, which keeps
+// the queue order of the definition.
 #include "tv_internal.h"
 
 namespace tv {
@@ -25,7 +26,8 @@ namespace tv {
 namespace {
 
 constexpr int kMaxK = 32;
-constexpr int kMaxPool = kMaxK + 63 * kMaxK;  // root proposals + k per other node
+constexpr int kMaxN = 128;
+constexpr int kMaxPool = kMaxK + (kMaxN - 1) * kMaxK;  // root proposals + k per other node
 
 // (score, position) of the better candidate: higher score, then the one
 // queued first
@@ -43,6 +45,12 @@ __device__ inline void best_step(double &s, int &j) {
     s = os;
     j = oj;
   }
+}
+
+__device__ inline uint64_t read_lane_u64(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v & 0xFFFFFFFFull), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // the best (score, position) of the wavefront, returned to every lane:
@@ -69,8 +77,8 @@ __global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restric
                                                         uint64_t *__restrict__ mask, double *__restrict__ scores,
                                                         int32_t *__restrict__ n_nodes,
                                                         unsigned long long *state) {
-  __shared__ float s_prob[64 * kMaxK];
-  __shared__ int32_t s_tok[64 * kMaxK];
+  __shared__ float s_prob[kMaxN * kMaxK];
+  __shared__ int32_t s_tok[kMaxN * kMaxK];
   __shared__ double s_score[kMaxPool];  // queued candidates; -1 once made a node
   __shared__ int16_t s_src[kMaxPool];   // proposer row * 32 + slot
   const int b = blockIdx.x;
@@ -89,10 +97,12 @@ __global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restric
   const int root_tok = root_tokens[b];
   __syncthreads();
 
-  // lane i holds node i
-  int my_parent = -1, my_token = root_tok, my_depth = 0;
-  double my_score = lane == 0 ? 1.0 : 0.0;
-  uint64_t my_mask = 1ull << lane;
+  // lane i holds nodes i (half 0) and i + 64 (half 1): parent, token,
+  // depth, cumulative score, ancestor set (nodes 0..63 in word 0, 64..127 in
+  // word 1)
+  int my_parent[2] = {-1, -1}, my_token[2] = {root_tok, root_tok}, my_depth[2] = {0, 0};
+  double my_score[2] = {lane == 0 ? 1.0 : 0.0, 0.0};
+  uint64_t my_m0[2] = {1ull << lane, 0ull}, my_m1[2] = {0ull, 1ull << lane};
   int n = 0;
   if (!bad) {
     n = 1;
@@ -119,16 +129,22 @@ __global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restric
       const int src = s_src[bj];
       const int row = src >> 5, slot = src & 31;
       const int id = n++;
-      const int pdepth = __shfl(my_depth, row);
-      const uint64_t pmask = shfl_u64(my_mask, row);
+      // the parent's fields, from the lane and half that hold it (the same
+      // for every lane)
+      const int ph = row >> 6, pl = row & 63;
+      const int pdepth = __builtin_amdgcn_readlane(ph ? my_depth[1] : my_depth[0], pl);
+      const uint64_t pm0 = read_lane_u64(ph ? my_m0[1] : my_m0[0], pl);
+      const uint64_t pm1 = read_lane_u64(ph ? my_m1[1] : my_m1[0], pl);
       __syncthreads();  // every lane has read s_score[bj] before it is retired
       if (lane == 0) s_score[bj] = -1.0;
-      if (lane == id) {
-        my_parent = row;
-        my_token = s_tok[row * kMaxK + slot];
-        my_depth = pdepth + 1;
-        my_score = bs;
-        my_mask = pmask | (1ull << id);
+      if (lane == (id & 63)) {
+        const int hh = id >> 6;
+        my_parent[hh] = row;
+        my_token[hh] = s_tok[row * kMaxK + slot];
+        my_depth[hh] = pdepth + 1;
+        my_score[hh] = bs;
+        my_m0[hh] = pm0 | (hh == 0 ? (1ull << lane) : 0ull);
+        my_m1[hh] = pm1 | (hh == 1 ? (1ull << lane) : 0ull);
       }
       if (pdepth + 1 < max_depth) {
         // the new node's proposals above the threshold, in slot order
@@ -149,14 +165,22 @@ __global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restric
       __syncthreads();
     }
   }
-  if (lane < N) {
-    const int64_t o = static_cast<int64_t>(b) * N + lane;
-    const bool live = lane < n;
-    parents[o] = live ? my_parent : -1;
-    tokens[o] = live ? my_token : root_tok;
-    if (depth) depth[o] = live ? my_depth : 0;
-    if (mask) mask[o] = live ? my_mask : (1ull << lane);
-    if (scores) scores[o] = live ? my_score : 0.0;
+  const int W = (N + 63) / 64;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int i = lane + 64 * hh;
+    if (i < N) {
+      const int64_t o = static_cast<int64_t>(b) * N + i;
+      const bool live = i < n;
+      parents[o] = live ? my_parent[hh] : -1;
+      tokens[o] = live ? my_token[hh] : root_tok;
+      if (depth) depth[o] = live ? my_depth[hh] : 0;
+      if (mask) {
+        mask[o * W] = live ? my_m0[hh] : (hh == 0 ? (1ull << lane) : 0ull);
+        if (W > 1) mask[o * W + 1] = live ? my_m1[hh] : (hh == 1 ? (1ull << lane) : 0ull);
+      }
+      if (scores) scores[o] = live ? my_score[hh] : 0.0;
+    }
   }
   if (lane == 0) {
     if (n_nodes) n_nodes[b] = n;

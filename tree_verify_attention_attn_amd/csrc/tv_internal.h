@@ -58,7 +58,8 @@ __device__ inline float wave_sum(float v) {
 }
 
 // Host-side launchers (defined in the kernels' translation units).
-tv_status launch_build_mask(tv_ctx *ctx, const int32_t *parents, int B, int N, uint64_t *mask, int32_t *depth);
+tv_status launch_build_mask(tv_ctx *ctx, const int32_t *parents, const int32_t *tree_sizes, int B, int N,
+                            uint64_t *mask, int32_t *depth);
 
 struct AttnPlan {
   int S;            // key splits per (sequence, KV head, row block)
@@ -72,14 +73,16 @@ struct AttnPlan {
 AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int max_prefix_len);
 tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, const void *k_pages,
                            const void *v_pages, int64_t num_pages, const int32_t *page_table, int maxp,
-                           const int32_t *prefix_lens, int max_prefix_len, const uint64_t *tree_mask, int B, int N,
-                           int Hq, int Hkv, int D, float sm_scale, void *out, tv_dtype out_dtype, void *workspace);
+                           const int32_t *prefix_lens, int max_prefix_len, const uint64_t *tree_mask,
+                           const int32_t *tree_sizes, int B, int N, int Hq, int Hkv, int D, float sm_scale, void *out,
+                           tv_dtype out_dtype, void *workspace);
 
 size_t accept_ws_bytes(int B, int N, int V, tv_accept_mode mode);
 tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits,
-                        const int32_t *draft_tokens, const int32_t *parents, const float *uniforms, int B, int N,
-                        int V, tv_accept_mode mode, float temperature, int32_t *accept_len, int32_t *path,
-                        int32_t *bonus, int32_t *target_argmax, void *workspace);
+                        const int32_t *draft_tokens, const int32_t *parents, const int32_t *tree_sizes,
+                        const float *uniforms, int B, int N, int V, tv_accept_mode mode, float temperature,
+                        int32_t *accept_len, int32_t *path, int32_t *bonus, int32_t *target_argmax,
+                        void *workspace);
 
 tv_status launch_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages, const int32_t *page_table,
                         int maxp, const int32_t *prefix_lens, int max_prefix_len, const int32_t *draft_tokens,
