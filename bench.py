@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--accept", default="default", choices=["default", "stochastic"],
                     help="stochastic: run the workload's tree with sampled acceptance (T = 1, draft rows and "
                          "uniforms from the same seeded streams, each node's token drawn from its draft row)")
+    ap.add_argument("--nodes", type=int, default=0,
+                    help="tree node slots per sequence (up to 128) instead of the workload's own N")
+    ap.add_argument("--ragged", action="store_true",
+                    help="give each sequence a seeded node count in [N/2, N] (tree_sizes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -45,34 +49,46 @@ def parse():
     return ap.parse_args()
 
 
-def workload_name(w, c):
+def workload_name(w, c, sizes=None):
     L = f"L~U[{c['L'][0]},{c['L'][1]}]" if isinstance(c["L"], tuple) else f"L{c['L']}"
-    return (f"cfg{w.cfg} {c['name']}: B{w.B} Hq{w.Hq}/Hkv{w.Hkv} D{w.D} {L} N{w.N} tree={c['tree']} "
+    n = f"N{w.N}" if sizes is None else f"N{w.N} ragged (node counts in [{int(sizes.min())}, {int(sizes.max())}])"
+    return (f"cfg{w.cfg} {c['name']}: B{w.B} Hq{w.Hq}/Hkv{w.Hkv} D{w.D} {L} {n} tree={c['tree']} "
             f"V{w.V} {w.mode}")
 
 
-def attention_bytes(w):
+def present(w, sizes):
+    """Node count of every sequence."""
+    return np.full(w.B, w.N, np.int64) if sizes is None else sizes.astype(np.int64)
+
+
+def attention_bytes(w, sizes=None):
     """Algorithmic HBM bytes of one tv_attention call: every visible K/V row
-    once, Q once, the output once, masks, page-table entries, prefix lengths."""
-    toks = int((w.prefix_lens.astype(np.int64) + w.N).sum())
+    once, Q once, the output once, masks, page-table entries, prefix lengths
+    (present nodes only)."""
+    n = present(w, sizes)
+    W = (w.N + 63) // 64
+    toks = int((w.prefix_lens.astype(np.int64) + n).sum())
     kv = toks * w.Hkv * w.D * 2 * 2
-    q = w.B * w.N * w.Hq * w.D * 2
-    out = w.B * w.N * w.Hq * w.D * 4
-    pages = int(((w.prefix_lens.astype(np.int64) + w.N + 15) // 16).sum()) * 4
-    return kv + q + out + w.B * w.N * 8 + pages + w.B * 4
+    rows = int(n.sum()) * w.Hq
+    q, out = rows * w.D * 2, rows * w.D * 4
+    pages = int(((w.prefix_lens.astype(np.int64) + n + 15) // 16).sum()) * 4
+    return kv + q + out + int(n.sum()) * 8 * W + pages + w.B * 4 * (2 if sizes is not None else 1)
 
 
-def attention_flops(w, depth):
+def attention_flops(w, depth, sizes=None):
     """4*D flops (QK^T and PV) per visible (query row, key) pair."""
-    vis = (w.prefix_lens.astype(np.int64)[:, None] + depth + 1).sum()  # keys seen by each node
+    n = present(w, sizes)
+    live = np.arange(w.N)[None, :] < n[:, None]
+    vis = ((w.prefix_lens.astype(np.int64)[:, None] + depth + 1) * live).sum()  # keys seen by each node
     return 4 * w.D * w.Hq * int(vis)
 
 
-def accept_bytes(w):
+def accept_bytes(w, sizes=None):
+    n = int(present(w, sizes).sum())
     if w.mode == "greedy":
-        return w.B * w.N * w.V * 4 + w.B * w.N * 4 * 3
-    # target rows, draft rows 1..N-1, and one re-read of a target and a draft row for the final draw
-    return (w.B * w.N + w.B * (w.N - 1)) * w.V * 4 + 2 * w.B * w.V * 4 + w.B * w.N * 4 * 3
+        return n * w.V * 4 + n * 4 * 3
+    # target rows, draft rows 1..n-1, and one re-read of a target and a draft row for the final draw
+    return (2 * n - w.B) * w.V * 4 + 2 * w.B * w.V * 4 + n * 4 * 3
 
 
 KERNEL_SOURCES = {"tv_attention": "attention.hip", "tv_accept": "accept.hip", "tv_build_mask": "mask.hip"}
@@ -106,30 +122,35 @@ def measured_traffic(call, key):
     return None
 
 
-def cpu_baseline(w, depth, target_s, threads):
+def cpu_baseline(w, depth, target_s, threads, sizes=None):
     """Times the fp64 oracle (attention for every head of the sampled nodes,
     then their acceptance) on the host, on whole sequences, growing the
     sample until it takes about `target_s` seconds or covers the batch."""
     import oracle
 
-    omask, _ = oracle.build_mask(w.parents)
+    n = present(w, sizes)
+    omask, _ = oracle.build_mask(w.parents, tree_sizes=sizes)
     nseq, elapsed, done = 1, 0.0, 0
     while True:
-        rows = np.array([[b, i, h] for b in range(nseq) for i in range(w.N) for h in range(w.Hq)], np.int32)
+        rows = np.array([[b, i, h] for b in range(nseq) for i in range(int(n[b])) for h in range(w.Hq)], np.int32)
+        ts = None if sizes is None else sizes[:nseq]
         t0 = time.perf_counter()
-        oracle.attention(w, omask, rows=rows, nthreads=threads)
+        oracle.attention(w, omask, rows=rows, nthreads=threads, tree_sizes=sizes)
         if w.mode == "greedy":
-            oracle.accept_greedy(w.target_logits[:nseq], w.draft_tokens[:nseq], w.parents[:nseq], nthreads=threads)
+            oracle.accept_greedy(w.target_logits[:nseq], w.draft_tokens[:nseq], w.parents[:nseq], nthreads=threads,
+                                 tree_sizes=ts)
         else:
             oracle.accept_stochastic(w.target_logits[:nseq], w.draft_logits[:nseq], w.draft_tokens[:nseq],
-                                     w.parents[:nseq], w.uniforms[:nseq], w.temperature, nthreads=threads)
+                                     w.parents[:nseq], w.uniforms[:nseq], w.temperature, nthreads=threads,
+                                     tree_sizes=ts)
         elapsed = time.perf_counter() - t0
         done = nseq
         if elapsed >= target_s or nseq >= w.B:
             break
         nseq = min(w.B, max(nseq + 1, int(nseq * min(8.0, 1.2 * target_s / max(elapsed, 1e-3)))))
-    return dict(value=done * w.N / elapsed, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{done} of {w.B} sequences ({done * w.N} tree tokens, {done * w.N * w.Hq} attention rows "
+    toks = int(n[:done].sum())
+    return dict(value=toks / elapsed, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{done} of {w.B} sequences ({toks} tree tokens, {toks * w.Hq} attention rows "
                        f"+ acceptance), {elapsed:.1f} s wall, fp64 C oracle, {threads} threads")
 
 
@@ -254,9 +275,22 @@ def main():
     dev = torch.device("cuda:0")
     c = tvgen.CONFIGS[args.config]
     stochastic = args.accept == "stochastic" and c["mode"] != "stochastic"
-    w = tvgen.make_workload(args.config, overrides=dict(mode="stochastic") if stochastic else None)
-    key = f"{args.config}-stochastic" if stochastic else str(args.config)
+    over = {}
+    if stochastic:
+        over["mode"] = "stochastic"
+    if args.nodes:
+        if not 1 <= args.nodes <= 128:
+            sys.exit("--nodes takes 1..128")
+        over["N"] = args.nodes
+    w = tvgen.make_workload(args.config, overrides=over or None)
+    key = str(args.config) + ("-stochastic" if stochastic else "") + (f"-N{args.nodes}" if args.nodes else "") + \
+        ("-ragged" if args.ragged else "")
     depth = np.stack([tvgen.tree_depths(p) for p in w.parents])
+    sizes = None
+    if args.ragged:
+        st = tvgen.Stream(w.seed, 41)
+        sizes = np.array([w.N - w.N // 2 + st.randint(w.N // 2 + 1) for _ in range(w.B)], np.int32)
+    n_present = present(w, sizes)
 
     def d(a, dtype=None):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -269,7 +303,8 @@ def main():
     dl = d(w.draft_logits) if w.draft_logits is not None else None
     un = d(w.uniforms) if w.uniforms is not None else None
     mode = tv.GREEDY if w.mode == "greedy" else tv.STOCHASTIC
-    mask = torch.empty((w.B, w.N, 1), dtype=torch.int64, device=dev)
+    mask = torch.empty((w.B, w.N, (w.N + 63) // 64), dtype=torch.int64, device=dev)
+    ts = d(sizes) if sizes is not None else None
     dep = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
     out = torch.empty((w.B, w.N, w.Hq, w.D), dtype=torch.float32, device=dev)
     aws = tv.tv_attention_workspace_bytes(dev, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
@@ -282,15 +317,15 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record()
-        tv.tv_build_mask(parents, mask, dep)
+        tv.tv_build_mask(parents, mask, dep, tree_sizes=ts)
         if ev:
             ev[1].record()
         tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, mask, float(w.sm_scale), out=out,
-                        workspace=attn_ws)
+                        workspace=attn_ws, tree_sizes=ts)
         if ev:
             ev[2].record()
         tv.tv_accept(tl, tokens, parents, mode=mode, draft_logits=dl, uniforms=un, temperature=w.temperature,
-                     outputs=outs, workspace=acc_ws)
+                     outputs=outs, workspace=acc_ws, tree_sizes=ts)
         if ev:
             ev[3].record()
 
@@ -318,8 +353,8 @@ def main():
     per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs]) * 1e-3  # seconds
     t_mask, t_attn, t_acc = per.mean(0)
     ms_per_step = wall / args.steps * 1e3
-    tokens = w.B * w.N
-    a_bytes, a_flops, c_bytes = attention_bytes(w), attention_flops(w, depth), accept_bytes(w)
+    tokens = int(n_present.sum())
+    a_bytes, a_flops, c_bytes = attention_bytes(w, sizes), attention_flops(w, depth, sizes), accept_bytes(w, sizes)
     kernels = {
         "tv_build_mask": dict(avg_us=t_mask * 1e6),
         "tv_attention": dict(avg_us=t_attn * 1e6, bytes=a_bytes, flops=a_flops, gbs=a_bytes / t_attn / 1e9,
@@ -344,7 +379,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload_name(w, c), "batch": w.B, "tree_nodes": w.N, "q_heads": w.Hq,
+        "config": {"workload": workload_name(w, c, sizes), "batch": w.B, "tree_nodes": w.N,
+                   "tree_tokens_per_step": tokens, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.D, "max_prefix_len": w.max_prefix_len, "vocab": w.V,
                    "accept": w.mode, "page_size": 16, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": f"{dom}: {CALL_KERNELS[dom]}", "achieved": dk["gbs"],
@@ -366,7 +402,7 @@ def main():
         e0.record()
         for _ in range(20):
             tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, m, float(w.sm_scale), out=out,
-                            workspace=attn_ws)
+                            workspace=attn_ws, tree_sizes=ts)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 20 * 1e3
@@ -377,9 +413,11 @@ def main():
     t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
     result["mask_overhead"] = {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
                                "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
-    if c["tree"] == "dynamic":
+    if c["tree"] == "dynamic" and sizes is None:
         result["build_tree"] = build_tree_timing(tv, torch, d, w, c)
-    result["commit"] = commit_timing(tv, torch, dev, w, depth, d, kp, vp, table, plens, d(w.draft_tokens), outs)
+    depth_present = np.where(np.arange(w.N)[None, :] < n_present[:, None], depth, -1)
+    result["commit"] = commit_timing(tv, torch, dev, w, depth_present, d, kp, vp, table, plens, d(w.draft_tokens),
+                                     outs)
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -389,7 +427,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
-        result["cpu_baseline"] = cpu_baseline(w, depth, args.cpu_seconds, threads)
+        result["cpu_baseline"] = cpu_baseline(w, depth, args.cpu_seconds, threads, sizes)
     print(json.dumps(result), flush=True)
 
 
