@@ -23,7 +23,8 @@
  * Conventions for every call
  *  - Pointers are DEVICE pointers unless marked (host). The caller allocates
  *    and owns every buffer, workspaces included; the library never allocates
- *    device memory in these calls (only tv_create does, 64 bytes).
+ *    device memory in these calls (only tv_create does: 64 bytes of
+ *    counters and flags plus 256 KB of per-sequence arrival counters).
  *  - Calls are asynchronous on the context's HIP stream, except tv_tau and
  *    tv_device_error, which synchronise that stream.
  *  - Host-detected errors return a status and launch nothing; outputs are
@@ -43,7 +44,8 @@
  *    are never read; mask rows are written 0 with depth -1, attention rows
  *    are not written, argmax rows are -1. A count outside [1, N] sets the
  *    sticky TV_ERR_INVALID_ARG (that sequence's outputs as for bad data).
- *  - A context is not thread-safe; use one per stream/thread.
+ *  - A context is not thread-safe; use one per thread. Its calls run in
+ *    issue order even across tv_set_stream (see there).
  */
 #ifndef TREEVERIFY_H
 #define TREEVERIFY_H
@@ -71,11 +73,16 @@ typedef enum tv_accept_mode { TV_GREEDY = 0, TV_STOCHASTIC = 1 } tv_accept_mode;
 typedef struct tv_ctx tv_ctx;
 
 /* Creates a context on `device` bound to `hip_stream` (a hipStream_t; NULL =
- * the default stream). Allocates 64 bytes of device memory for the tau
- * counters and the sticky error flag, zeroed. *ctx is host memory. */
+ * the default stream). Allocates, zeroed, 64 bytes of device memory for the
+ * tau counters and the sticky error flag and 256 KB of per-sequence arrival
+ * counters that small greedy tv_accept calls use (each call leaves them
+ * zero), plus one HIP event. *ctx is host memory. */
 tv_status tv_create(tv_ctx **ctx, int device, void *hip_stream);
 tv_status tv_destroy(tv_ctx *ctx);
-/* Rebinds the context to another stream of the same device. */
+/* Rebinds the context to another stream of the same device. Work already
+ * queued on the previous stream is ordered before later calls (an event
+ * recorded there that the new stream waits for), so the context's device
+ * counters are never used by two calls at once. */
 tv_status tv_set_stream(tv_ctx *ctx, void *hip_stream);
 
 /* Ancestor-or-self bitmask of every tree node ([EAGLE-2 page], reference
@@ -204,7 +211,9 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  *   from max(0, p - q) at the rejection (p if its mass is 0), or from
  *   p_{N-1} when every draft is accepted.
  * Adds sum(accept_len) and B to the context's tau counters. Requires
- * 1 <= N <= 128 when B > 0, V >= 1. */
+ * 1 <= N <= 128 when B > 0, V >= 1, and B * N * ceil(V / 8192) <= 2^24 - 1
+ * (one 256-thread workgroup per row and 8192-token chunk on a 1-D grid);
+ * larger calls return TV_ERR_UNSUPPORTED. */
 tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
                     const int32_t *parents, const int32_t *tree_sizes, const float *uniforms, int32_t B, int32_t N,
                     int32_t V,

@@ -72,6 +72,77 @@ def test_greedy_large_batch():
     greedy_compare(w, "B70000")
 
 
+@pytest.mark.parametrize("B,N,V", [(128, 2, 8), (129, 2, 8), (2, 128, 8192), (2, 128, 8193), (1, 15, 1024),
+                                   (3, 64, 24577)])
+def test_greedy_one_launch_limit(B, N, V):
+    # with at most 256 argmax workgroups (rows x 8192-token chunks), the
+    # argmax pass's last workgroup of each sequence runs the path logic (one
+    # launch); above, the path pass runs on its own
+    w = tvgen.make_workload(1, seed=B + N + V, with_kv=False,
+                            overrides=dict(B=B, N=N, V=V, max_depth=min(N - 1, 9), tree="random"))
+    tvgen.plant_random(w, 0.6, seed=5)
+    print(f"[accept] greedy B={B} N={N} V={V}", flush=True)
+    ref = greedy_compare(w, f"B{B}-N{N}-V{V}")
+    assert (ref["accept_len"] >= 2).any()
+
+
+def test_greedy_consecutive_calls_of_different_shapes():
+    # the per-sequence arrival counters are left at zero by every call, so
+    # calls of any shape can follow each other (several chunks per row, node
+    # counts, 65-128 nodes)
+    shapes = [dict(B=5, N=64, V=3000), dict(B=3, N=100, V=20000), dict(B=7, N=10, V=24577),
+              dict(B=5, N=64, V=3000), dict(B=40, N=128, V=100)]
+    for i, sh in enumerate(shapes):
+        w = tvgen.make_workload(2, seed=40 + i, with_kv=False, overrides=dict(tree="random", max_depth=9, **sh))
+        tvgen.plant_random(w, 0.7, seed=i)
+        print(f"[accept] consecutive call {i}: {sh}", flush=True)
+        greedy_compare(w, f"call{i}")
+        sizes = np.array([1 + (7 * b) % sh["N"] for b in range(sh["B"])], np.int32)
+        got = tv.tv_accept(dev(w.target_logits), dev(w.draft_tokens), dev(w.parents), tree_sizes=dev(sizes))
+        assert tv.tv_device_error(DEV) == 0
+        ref = oracle.accept_greedy(w.target_logits, w.draft_tokens, w.parents, tree_sizes=sizes)
+        for k in KEYS:
+            assert (host(got[k]) == ref[k]).all(), (i, k)
+
+
+def test_calls_on_two_streams_are_ordered():
+    # one context rebound from stream to stream: the second call starts after
+    # the first, so the two never share the arrival counters at once
+    import torch
+    # a one-launch shape (60 argmax workgroups) and a two-launch shape
+    ws = [tvgen.make_workload(2, seed=60 + i, with_kv=False, overrides=sh)
+          for i, sh in enumerate([dict(B=4, N=15, V=1024, max_depth=5), dict(B=8, N=64, V=128256)])]
+    for i, w in enumerate(ws):
+        tvgen.plant_random(w, 0.8, seed=i)
+    dws = [DevWorkload(w, kv=False) for w in ws]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for dw, st in zip(dws, streams):
+            with torch.cuda.stream(st):
+                outs.append((dw.w, dw.accept(tv.GREEDY)))
+    torch.cuda.synchronize()
+    assert tv.tv_device_error(DEV) == 0
+    for w, got in outs:
+        ref = oracle.accept_greedy(w.target_logits, w.draft_tokens, w.parents)
+        for k in KEYS:
+            assert (host(got[k]) == ref[k]).all(), k
+
+
+def test_greedy_grid_limit_is_reported():
+    # one workgroup per (row, 8192-token chunk) on a 1-D grid of at most
+    # 2^32 - 1 work-items: larger calls are refused before any launch
+    w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=2, N=4, V=16))
+    dw = DevWorkload(w, kv=False)
+    lib, p = tv.library(), tv._ptr
+    out = [dev(np.zeros(8, np.int32)) for _ in range(4)]
+    ws = dev(np.zeros(64, np.uint8))
+    st = lib.tv_accept(tv._ctx(DEV), p(dw.target_logits), None, p(dw.draft_tokens), p(dw.parents), None, None,
+                       1 << 20, 128, 128256, tv.GREEDY, 1.0, p(out[0]), p(out[1]), p(out[2]), p(out[3]), p(ws), 64)
+    assert st == tv.UNSUPPORTED
+
+
 def test_greedy_forest_nodes_never_accepted():
     w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=8, N=12, tree="forest", V=64))
     w.parents[:, 0] = -1

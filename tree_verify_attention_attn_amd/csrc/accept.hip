@@ -15,6 +15,9 @@
 //           mask has the larger bit-reversed value (node ids increase along a
 //           path, so the first differing path element is the lowest
 //           differing mask bit). Path, length, bonus and tau counters follow.
+//           When pass 1 has at most kMaxFusedGrid workgroups, both passes
+//           are one launch: the workgroup of pass 1 that completes a
+//           sequence's last chunk key runs pass 2 for that sequence.
 // Stochastic (Sonar page, draft-target section: acceptance compares the full
 // draft and target distributions; EAGLE-2 page: rejection sampling keeps the
 // target distribution), on chains and trees:
@@ -37,6 +40,7 @@ namespace tv {
 namespace {
 
 constexpr int kChunk = 8192;  // vocab entries per pass-1 workgroup
+constexpr int kMaxFusedGrid = 256;  // pass-1 workgroups up to which both greedy passes are one launch
 constexpr int kThreads = 256;
 
 __device__ inline uint32_t orderable(float f) {
@@ -55,17 +59,16 @@ __device__ inline unsigned long long umax64(unsigned long long a, unsigned long 
 
 __device__ inline int size_of(const int32_t *sizes, int64_t b, int N) { return sizes ? sizes[b] : N; }
 
+// Node count of sequence b. A count outside [1, N] is bad data: every row of
+// the sequence is then reduced, and the path logic reports the error.
+__device__ inline int present_nodes(const int32_t *sizes, int64_t b, int N) {
+  const int nb = sizes ? sizes[b] : N;
+  return (nb < 1 || nb > N) ? N : nb;
+}
+
+// Argmax key of p[x0, x1) over the workgroup; thread 0 receives it.
 template <bool kVec>
-__global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__restrict__ logits,
-                                                                const int32_t *__restrict__ sizes, int N, int V,
-                                                                int chunks, unsigned long long *__restrict__ keys) {
-  __shared__ unsigned long long red[kThreads / 64];
-  const int chunk = blockIdx.x;
-  const int64_t row = blockIdx.y;
-  if (sizes && row % N >= sizes[row / N]) return;  // an absent node: its row is never read
-  const float *p = logits + row * V;
-  const int x0 = chunk * kChunk;
-  const int x1 = min(x0 + kChunk, V);
+__device__ inline unsigned long long block_argmax(const float *p, int x0, int x1, unsigned long long *red) {
   unsigned long long best = 0ull;
   if (kVec) {
     // all of the thread's 16-byte loads are issued before any is used
@@ -94,26 +97,35 @@ __global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__r
   for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0)
     for (int i = 1; i < kThreads / 64; ++i) best = umax64(best, red[i]);
-    keys[row * chunks + chunk] = best;
-  }
+  return best;
+}
+
+// Workgroup (row, chunk) = (blockIdx.x / chunks, blockIdx.x % chunks).
+template <bool kVec>
+__global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__restrict__ logits,
+                                                                const int32_t *__restrict__ sizes, int N, int V,
+                                                                int chunks, unsigned long long *__restrict__ keys) {
+  __shared__ unsigned long long red[kThreads / 64];
+  const int chunk = static_cast<int>(blockIdx.x % static_cast<unsigned>(chunks));
+  const int64_t row = blockIdx.x / static_cast<unsigned>(chunks);
+  if (row % N >= present_nodes(sizes, row / N, N)) return;  // an absent node: its row is never read
+  const int x0 = chunk * kChunk;
+  const unsigned long long best = block_argmax<kVec>(logits + row * V, x0, min(x0 + kChunk, V), red);
+  if (threadIdx.x == 0) keys[row * chunks + chunk] = best;
 }
 
 // One wavefront per sequence; lane i holds node i (and node i + 64 when
 // H = 2). Ancestor sets are 128-bit (nodes 0..63 in word 0, 64..127 in word 1).
-template <int H>
-__global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long long *__restrict__ keys, int chunks,
-                                                          const int32_t *__restrict__ draft_tokens,
-                                                          const int32_t *__restrict__ parents,
-                                                          const int32_t *__restrict__ sizes, int B, int N, int V,
-                                                          int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-                                                          int32_t *__restrict__ bonus,
-                                                          int32_t *__restrict__ target_argmax,
-                                                          unsigned long long *state) {
-  const int lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (b >= B) return;
+// kCoherent: the keys were published by other workgroups of the same launch
+// (device-scope atomic swaps), so they are read with device-scope atomics.
+template <int H, bool kCoherent>
+__device__ void greedy_path_seq(int b, int lane, unsigned long long *keys, int chunks,
+                                const int32_t *__restrict__ draft_tokens, const int32_t *__restrict__ parents,
+                                const int32_t *__restrict__ sizes, int N, int V, int32_t *__restrict__ accept_len,
+                                int32_t *__restrict__ path, int32_t *__restrict__ bonus,
+                                int32_t *__restrict__ target_argmax, unsigned long long *state) {
   const int nb = size_of(sizes, b, N);
   const bool bad_size = nb < 1 || nb > N;
   bool live[H], bad_tree = false, bad_tok = false;
@@ -125,8 +137,17 @@ __global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long lo
     live[k] = !bad_size && i < nb;
     y[k] = -1;
     if (live[k]) {
+      // the row's chunk keys, 16 loads in flight at a time
       unsigned long long best = 0ull;
-      for (int c = 0; c < chunks; ++c) best = umax64(best, keys[idx * chunks + c]);
+      unsigned long long *kp = keys + idx * chunks;
+      for (int c0 = 0; c0 < chunks; c0 += 16) {
+        unsigned long long kv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          kv[q] = c0 + q >= chunks ? 0ull : kCoherent ? atomicAdd(kp + c0 + q, 0ull) : kp[c0 + q];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) best = umax64(best, kv[q]);
+      }
       y[k] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best & 0xFFFFFFFFull));
     }
     par[k] = live[k] ? parents[idx] : -1;
@@ -274,6 +295,56 @@ __global__ void __launch_bounds__(256) greedy_path_kernel(const unsigned long lo
   }
 }
 
+// Path pass on its own: one wavefront per sequence.
+template <int H>
+__global__ void __launch_bounds__(256) greedy_path_kernel(unsigned long long *keys, int chunks,
+                                                          const int32_t *__restrict__ draft_tokens,
+                                                          const int32_t *__restrict__ parents,
+                                                          const int32_t *__restrict__ sizes, int B, int N, int V,
+                                                          int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+                                                          int32_t *__restrict__ bonus,
+                                                          int32_t *__restrict__ target_argmax,
+                                                          unsigned long long *state) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= B) return;
+  greedy_path_seq<H, false>(b, threadIdx.x & 63, keys, chunks, draft_tokens, parents, sizes, N, V, accept_len, path,
+                            bonus, target_argmax, state);
+}
+
+// Both passes in one launch. Each workgroup publishes its chunk key with a
+// device-scope atomic swap, waits for the swap to complete, and counts itself
+// in on its sequence's arrival counter; the workgroup that arrives last (all
+// of the sequence's present rows times chunks) resets the counter to zero and
+// runs the path logic in its first wavefront. No workgroup waits for another.
+template <bool kVec, int H>
+__global__ void __launch_bounds__(kThreads) argmax_path_kernel(
+    const float *__restrict__ logits, const int32_t *__restrict__ sizes, int N, int V, int chunks,
+    unsigned long long *keys, unsigned int *arrivals, const int32_t *__restrict__ draft_tokens,
+    const int32_t *__restrict__ parents, int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
+    int32_t *__restrict__ bonus, int32_t *__restrict__ target_argmax, unsigned long long *state) {
+  __shared__ unsigned long long red[kThreads / 64];
+  __shared__ int s_last;
+  const int chunk = static_cast<int>(blockIdx.x % static_cast<unsigned>(chunks));
+  const int64_t row = blockIdx.x / static_cast<unsigned>(chunks);
+  const int b = static_cast<int>(row / N);
+  const int present = present_nodes(sizes, b, N);
+  if (row % N >= present) return;  // an absent node: its row is never read and it is not counted
+  const int x0 = chunk * kChunk;
+  const unsigned long long best = block_argmax<kVec>(logits + row * V, x0, min(x0 + kChunk, V), red);
+  if (threadIdx.x == 0) {
+    atomicExch(keys + row * chunks + chunk, best);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the key is in place before this workgroup is counted
+    const unsigned int arrived = atomicAdd(arrivals + b, 1u) + 1u;
+    const bool last = arrived == static_cast<unsigned int>(present) * static_cast<unsigned int>(chunks);
+    if (last) atomicExch(arrivals + b, 0u);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last || threadIdx.x >= 64) return;
+  greedy_path_seq<H, true>(b, threadIdx.x, keys, chunks, draft_tokens, parents, sizes, N, V, accept_len, path, bonus,
+                           target_argmax, state);
+}
+
 // ---------------------------------------------------------------- stochastic
 
 // e^x in fp64 for the arguments the acceptance step forms (a scaled logit
@@ -348,9 +419,9 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
                                                                  double *__restrict__ stats,
                                                                  unsigned long long *__restrict__ counters) {
   __shared__ double red[kThreads / 64];
-  const int chunk = blockIdx.x;
-  const int64_t row = blockIdx.y;  // b * N + j
-  const int which = blockIdx.z;    // 0 = target, 1 = draft
+  const int chunk = static_cast<int>(blockIdx.x % static_cast<unsigned>(chunks));
+  const int64_t row = blockIdx.x / static_cast<unsigned>(chunks);  // b * N + j
+  const int which = blockIdx.z;                                     // 0 = target, 1 = draft
   const int j = static_cast<int>(row % N);
   if (sizes && j > 0 && j >= sizes[row / N]) return;  // an absent node: its rows are never read
   double *out = stats + ((row * 2 + which) * chunks + chunk) * 2;
@@ -914,7 +985,19 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
                    (draft_logits == nullptr || (reinterpret_cast<uintptr_t>(draft_logits) & 15) == 0);
   if (mode == TV_GREEDY) {
     auto *keys = static_cast<unsigned long long *>(workspace);
-    const dim3 g1(chunks, B * N);
+    const dim3 g1(static_cast<unsigned>(static_cast<int64_t>(B) * N * chunks));
+    // one launch when the grid is small: the last workgroup of each sequence
+    // runs its path logic. Every workgroup then pays two device-scope atomics
+    // (about 7.5 ns each, measured across the chip), which outweighs the saved
+    // launch beyond a few hundred workgroups.
+    if (B <= kMaxFusedSeqs && static_cast<int64_t>(B) * N * chunks <= kMaxFusedGrid) {
+      auto *fn = vec ? (N <= 64 ? argmax_path_kernel<true, 1> : argmax_path_kernel<true, 2>)
+                     : (N <= 64 ? argmax_path_kernel<false, 1> : argmax_path_kernel<false, 2>);
+      hipLaunchKernelGGL(fn, g1, blk, 0, ctx->stream, target_logits, tree_sizes, N, V, chunks, keys,
+                         ctx->d_arrivals, draft_tokens, parents, accept_len, path, bonus, target_argmax,
+                         ctx->d_state);
+      return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+    }
     if (vec)
       hipLaunchKernelGGL(argmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, tree_sizes, N, V, chunks,
                          keys);
@@ -955,7 +1038,7 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
     }
   }
   const int slice = (((V + K - 1) / K) + 3) / 4 * 4;
-  const dim3 g1(chunks, B * N, 2);
+  const dim3 g1(static_cast<unsigned>(static_cast<int64_t>(B) * N * chunks), 1, 2);
   unsigned long long *counters = K > 1 ? sync : nullptr;
   if (vec)
     hipLaunchKernelGGL(softmax_chunk_kernel<true>, g1, blk, 0, ctx->stream, target_logits, draft_logits, tree_sizes,

@@ -13,6 +13,10 @@ __global__ void clear_words_kernel(unsigned long long *p, int n) {
   if (static_cast<int>(threadIdx.x) < n) p[threadIdx.x] = 0ull;
 }
 
+__global__ void clear_u32_kernel(unsigned int *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 }  // namespace
 
 tv_status launch_clear_state(tv_ctx *ctx, int first_word, int n_words) {
@@ -36,16 +40,22 @@ tv_status tv_create(tv_ctx **out, int device, void *hip_stream) {
   if (!ctx) return TV_ERR_HIP;
   ctx->device = device;
   ctx->stream = static_cast<hipStream_t>(hip_stream);
+  auto fail = [&]() {
+    if (ctx->d_state) (void)hipFree(ctx->d_state);
+    if (ctx->d_arrivals) (void)hipFree(ctx->d_arrivals);
+    if (ctx->rebind_event) (void)hipEventDestroy(ctx->rebind_event);
+    free(ctx);
+    return TV_ERR_HIP;
+  };
   if (hipDeviceGetAttribute(&ctx->cu_count, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
-      hipMalloc(reinterpret_cast<void **>(&ctx->d_state), 64) != hipSuccess) {
-    free(ctx);
-    return TV_ERR_HIP;
-  }
-  if (launch_clear_state(ctx, 0, 8) != TV_OK || hipStreamSynchronize(ctx->stream) != hipSuccess) {
-    (void)hipFree(ctx->d_state);
-    free(ctx);
-    return TV_ERR_HIP;
-  }
+      hipMalloc(reinterpret_cast<void **>(&ctx->d_state), 64) != hipSuccess ||
+      hipMalloc(reinterpret_cast<void **>(&ctx->d_arrivals), kMaxFusedSeqs * sizeof(unsigned int)) != hipSuccess ||
+      hipEventCreateWithFlags(&ctx->rebind_event, hipEventDisableTiming) != hipSuccess)
+    return fail();
+  hipLaunchKernelGGL(clear_u32_kernel, dim3(64), dim3(256), 0, ctx->stream, ctx->d_arrivals, kMaxFusedSeqs);
+  if (hipGetLastError() != hipSuccess || launch_clear_state(ctx, 0, 8) != TV_OK ||
+      hipStreamSynchronize(ctx->stream) != hipSuccess)
+    return fail();
   *out = ctx;
   return TV_OK;
 }
@@ -55,13 +65,23 @@ tv_status tv_destroy(tv_ctx *ctx) {
   (void)hipSetDevice(ctx->device);
   (void)hipStreamSynchronize(ctx->stream);
   (void)hipFree(ctx->d_state);
+  (void)hipFree(ctx->d_arrivals);
+  (void)hipEventDestroy(ctx->rebind_event);
   free(ctx);
   return TV_OK;
 }
 
 tv_status tv_set_stream(tv_ctx *ctx, void *hip_stream) {
   if (!ctx) return TV_ERR_INVALID_ARG;
-  ctx->stream = static_cast<hipStream_t>(hip_stream);
+  const hipStream_t next = static_cast<hipStream_t>(hip_stream);
+  if (next != ctx->stream) {
+    // the context's device counters are shared by its calls: calls on the
+    // new stream wait for what is already queued on the old one
+    if (hipEventRecord(ctx->rebind_event, ctx->stream) != hipSuccess ||
+        hipStreamWaitEvent(next, ctx->rebind_event, 0) != hipSuccess)
+      return TV_ERR_HIP;
+    ctx->stream = next;
+  }
   return TV_OK;
 }
 
@@ -119,6 +139,9 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
   if (N > 128) return TV_ERR_UNSUPPORTED;
   if (!target_logits || !draft_tokens || !parents || !accept_len || !path || !bonus_token) return TV_ERR_INVALID_ARG;
   if (mode == TV_STOCHASTIC && (!draft_logits || !uniforms)) return TV_ERR_INVALID_ARG;
+  // one workgroup of 256 threads per (row, 8192-token chunk), on a 1-D grid
+  if (static_cast<int64_t>(B) * N * ((static_cast<int64_t>(V) + 8191) / 8192) * 256 > 0xFFFFFFFFLL)
+    return TV_ERR_UNSUPPORTED;
   const size_t need = accept_ws_bytes(B, N, V, mode);
   if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
   return launch_accept(ctx, target_logits, draft_logits, draft_tokens, parents, tree_sizes, uniforms, B, N, V, mode,

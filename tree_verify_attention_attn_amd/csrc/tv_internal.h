@@ -15,11 +15,18 @@ struct tv_ctx {
   // resident workgroups per CU of the stochastic path pass (0 = not yet
   // queried, -1 = query failed)
   int path_blocks_per_cu;
+  // per-sequence arrival counters of the one-launch greedy acceptance
+  // (tv::kMaxFusedSeqs words, zero between calls)
+  unsigned int *d_arrivals;
+  // recorded on the old stream when the context is rebound, so that calls on
+  // the new stream start after the work already queued
+  hipEvent_t rebind_event;
 };
 
 namespace tv {
 
 constexpr int kPage = 16;
+constexpr int kMaxFusedSeqs = 65536;  // sequences with an arrival counter for one-launch greedy acceptance
 
 // Records the first device-detected error of a context (later ones are dropped).
 __device__ inline void raise_error(unsigned long long *state, int code) {
