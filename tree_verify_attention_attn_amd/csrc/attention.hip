@@ -661,13 +661,18 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 }
 
 // Merges the S partial (m, l, o) triples of each row in a fixed split order.
-// One wavefront per row (four rows per workgroup); lane i owns D/64
-// consecutive d, so each partial row is one coalesced load.
+// A row is D/4 lanes, each owning four consecutive d (one 16-byte load per
+// partial), so a wavefront holds 64*4/D rows. Partials are read eight splits
+// at a time with every load of a batch issued before any is used; the
+// running maximum is raised between batches (one batch when S <= 8, which is
+// then the plain max-then-sum merge).
 template <int D>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
-  constexpr int E = D / 64;  // d values per lane
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  constexpr int LPR = D / 4;     // lanes per row
+  constexpr int RPW = 64 / LPR;  // rows per wavefront
+  constexpr int kBatch = 8;
+  const int lane = threadIdx.x & 63, sub = lane % LPR;
+  const int64_t r = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
   if (r >= static_cast<int64_t>(a.B) * a.Hkv * a.rows) return;
   const int bh = static_cast<int>(r / a.rows), row = static_cast<int>(r % a.rows);
   const int b = bh / a.Hkv, g = bh % a.Hkv;
@@ -675,49 +680,53 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   const int nb = (nb_in < 1 || nb_in > a.N) ? a.N : nb_in;
   if (row >= nb * a.G) return;  // an absent node's row has no output
   const int64_t slot0 = static_cast<int64_t>(bh) * a.S * a.rows_pad + row;
-  float M = -INFINITY;
+  float M = -INFINITY, lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   bool bad = false;
-  for (int s = 0; s < a.S; ++s) {
-    const float ms = a.ws_ml[(slot0 + static_cast<int64_t>(s) * a.rows_pad) * 2];
-    bad |= isnan(ms);
-    M = fmaxf(M, ms);
-  }
-  float lsum = 0.f, acc[E];
+  for (int s0 = 0; s0 < a.S; s0 += kBatch) {
+    float2 ml[kBatch];
+    float4 ov[kBatch];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < a.S; ++s) {
-    const int64_t slot = slot0 + static_cast<int64_t>(s) * a.rows_pad;
-    const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + slot * 2);
-    const float wgt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-    lsum = fmaf(wgt, ml.y, lsum);
-    if (E == 2) {
-      const float2 o2 = *reinterpret_cast<const float2 *>(a.ws_o + slot * D + 2 * lane);
-      acc[0] = fmaf(wgt, o2.x, acc[0]);
-      acc[E - 1] = fmaf(wgt, o2.y, acc[E - 1]);
-    } else {
-      acc[0] = fmaf(wgt, a.ws_o[slot * D + lane], acc[0]);
+    for (int q = 0; q < kBatch; ++q) {
+      ml[q] = make_float2(-INFINITY, 0.f);
+      ov[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s0 + q < a.S) {
+        const int64_t slot = slot0 + static_cast<int64_t>(s0 + q) * a.rows_pad;
+        ml[q] = *reinterpret_cast<const float2 *>(a.ws_ml + slot * 2);
+        ov[q] = *reinterpret_cast<const float4 *>(a.ws_o + slot * D + 4 * sub);
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      bad |= isnan(ml[q].x);
+      Mb = fmaxf(Mb, ml[q].x);
+    }
+    if (Mb != M) {  // raise the running maximum (M = -inf holds nothing yet)
+      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+      lsum *= sc;
+      acc.x *= sc;
+      acc.y *= sc;
+      acc.z *= sc;
+      acc.w *= sc;
+      M = Mb;
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const float wgt = ml[q].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[q].x - M);
+      lsum = fmaf(wgt, ml[q].y, lsum);
+      acc.x = fmaf(wgt, ov[q].x, acc.x);
+      acc.y = fmaf(wgt, ov[q].y, acc.y);
+      acc.z = fmaf(wgt, ov[q].z, acc.z);
+      acc.w = fmaf(wgt, ov[q].w, acc.w);
     }
   }
   const int i = row / a.G, h = g * a.G + row % a.G;
-  const int64_t idx = ((static_cast<int64_t>(b) * a.N + i) * a.Hq + h) * D + E * lane;
+  const int64_t base = ((static_cast<int64_t>(b) * a.N + i) * a.Hq + h) * D;
   const float inv = 1.f / lsum;
-  float v[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = bad ? NAN : acc[e] * inv;
-  if (a.out_bf16) {
-    uint16_t *o = static_cast<uint16_t *>(a.out) + idx;
-    if (E == 2)
-      *reinterpret_cast<uint32_t *>(o) = float_to_bf16_bits(v[0]) | (static_cast<uint32_t>(float_to_bf16_bits(v[E - 1])) << 16);
-    else
-      o[0] = float_to_bf16_bits(v[0]);
-  } else {
-    float *o = static_cast<float *>(a.out) + idx;
-    if (E == 2)
-      *reinterpret_cast<float2 *>(o) = make_float2(v[0], v[E - 1]);
-    else
-      o[0] = v[0];
-  }
+  float v4[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  if (bad) v4[0] = v4[1] = v4[2] = v4[3] = NAN;
+  store_out(a, base, 4 * sub, v4);
 }
 
 constexpr int kStages = 4;
@@ -823,7 +832,8 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
     launch_dw<64>(plan.qb, plan.ksplit, flat, grid, block, ctx->stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
-    const dim3 cgrid(static_cast<unsigned>((static_cast<int64_t>(B) * Hkv * a.rows + 3) / 4));
+    const int rows_per_wg = 4 * (64 / (D / 4));  // four wavefronts, 64*4/D rows each
+    const dim3 cgrid(static_cast<unsigned>((static_cast<int64_t>(B) * Hkv * a.rows + rows_per_wg - 1) / rows_per_wg));
     if (D == 128)
       hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, ctx->stream, a);
     else
