@@ -93,8 +93,9 @@ def accept_bytes(w, sizes=None):
 
 KERNEL_SOURCES = {"tv_attention": "attention.hip", "tv_accept": "accept.hip", "tv_build_mask": "mask.hip"}
 CALL_KERNELS = {"tv_attention": "attn_mfma_kernel (+ attn_combine_kernel when the keys are split)",
-                "tv_accept": "argmax_chunk_kernel + greedy_path_kernel (greedy) or softmax_chunk_kernel + "
-                             "stochastic_path_kernel (stochastic)",
+                "tv_accept": "argmax_chunk_kernel + greedy_path_kernel (greedy; argmax_path_kernel alone for "
+                             "grids of at most 256 workgroups) or softmax_chunk_kernel + stochastic_path_kernel "
+                             "(stochastic)",
                 "tv_build_mask": "build_mask_kernel",
                 "tv_commit": "commit_kernel"}
 
