@@ -155,6 +155,18 @@ def cpu_baseline(w, depth, target_s, threads, sizes=None):
                        f"+ acceptance), {elapsed:.1f} s wall, fp64 C oracle, {threads} threads")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def commit_moves(w, path, lens):
     """Rows (per KV head) a commit moves: path entries after the identity run."""
     rows = 0
@@ -297,7 +309,7 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(a))
         return (t.view(dtype) if dtype is not None else t).to(dev)
 
-    parents, tokens = d(w.parents), d(w.draft_tokens)
+    parents, tokens_d = d(w.parents), d(w.draft_tokens)
     q, kp, vp = d(w.q, torch.bfloat16), d(w.k_pages, torch.bfloat16), d(w.v_pages, torch.bfloat16)
     table, plens = d(w.page_table), d(w.prefix_lens)
     tl = d(w.target_logits)
@@ -325,7 +337,7 @@ def main():
                         workspace=attn_ws, tree_sizes=ts)
         if ev:
             ev[2].record()
-        tv.tv_accept(tl, tokens, parents, mode=mode, draft_logits=dl, uniforms=un, temperature=w.temperature,
+        tv.tv_accept(tl, tokens_d, parents, mode=mode, draft_logits=dl, uniforms=un, temperature=w.temperature,
                      outputs=outs, workspace=acc_ws, tree_sizes=ts)
         if ev:
             ev[3].record()
@@ -356,6 +368,11 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     tokens = int(n_present.sum())
     a_bytes, a_flops, c_bytes = attention_bytes(w, sizes), attention_flops(w, depth, sizes), accept_bytes(w, sizes)
+    def spread(col):
+        us = per[:, col] * 1e6
+        return dict(median_us=float(np.median(us)), p10_us=float(np.percentile(us, 10)),
+                    p90_us=float(np.percentile(us, 90)), samples=int(len(us)))
+
     kernels = {
         "tv_build_mask": dict(avg_us=t_mask * 1e6),
         "tv_attention": dict(avg_us=t_attn * 1e6, bytes=a_bytes, flops=a_flops, gbs=a_bytes / t_attn / 1e9,
@@ -365,6 +382,8 @@ def main():
         "tv_accept": dict(avg_us=t_acc * 1e6, bytes=c_bytes, gbs=c_bytes / t_acc / 1e9,
                           hbm_frac=c_bytes / t_acc / 1e9 / HBM_PEAK_GBS),
     }
+    for col, name in enumerate(("tv_build_mask", "tv_attention", "tv_accept")):
+        kernels[name].update(spread(col))
     dom = "tv_attention" if t_attn >= t_acc else "tv_accept"
     dk = kernels[dom]
     result = {
@@ -414,6 +433,53 @@ def main():
     t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
     result["mask_overhead"] = {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
                                "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
+    # verify premium: the same call for the root row only (N = 1, a plain
+    # decode step) over the same KV, blocks of 20 calls, medians of 5 blocks
+    q1 = q[:, :1].contiguous()
+    out1 = torch.empty((w.B, 1, w.Hq, w.D), dtype=torch.float32, device=dev)
+    ws1 = torch.empty(max(tv.tv_attention_workspace_bytes(dev, w.B, 1, w.Hq, w.Hkv, w.D, w.max_prefix_len), 1),
+                      dtype=torch.uint8, device=dev)
+
+    def decode_block():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            tv.tv_attention(q1, kp, vp, table, plens, w.max_prefix_len, None, float(w.sm_scale), out=out1,
+                            workspace=ws1)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 20 * 1e3
+    t_dec = float(np.median([decode_block() for _ in range(5)]))
+    result["verify_premium"] = {"decode_us": t_dec, "verify_us": t_m, "premium": t_m / t_dec,
+                                "tree_tokens_per_decode_token": tokens / w.B,
+                                "note": "tv_attention over the same KV for the root row only (N = 1, no mask) "
+                                        "against the tree-verify call"}
+    # cold caches: before each timed call a 1 GiB buffer is written, which
+    # evicts the 4 MB L2s and the 256 MB MALL; 10 calls of each
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def cold(call, nbytes):
+        ts_ = []
+        for r in range(10):
+            flush.fill_(r & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts_.append(e0.elapsed_time(e1) * 1e3)
+        med = float(np.median(ts_))
+        return dict(median_us=med, p10_us=float(np.percentile(ts_, 10)), p90_us=float(np.percentile(ts_, 90)),
+                    gbs=nbytes / med / 1e3, hbm_frac=nbytes / med / 1e3 / HBM_PEAK_GBS)
+    result["cold_cache"] = {
+        "tv_attention": cold(lambda: tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, mask,
+                                                     float(w.sm_scale), out=out, workspace=attn_ws,
+                                                     tree_sizes=ts), a_bytes),
+        "tv_accept": cold(lambda: tv.tv_accept(tl, tokens_d, parents, mode=mode, draft_logits=dl, uniforms=un,
+                                               temperature=w.temperature, outputs=outs, workspace=acc_ws,
+                                               tree_sizes=ts), c_bytes),
+        "note": "one call after writing a 1 GiB buffer (L2 and MALL evicted); the step figures above are warm"}
+    del flush
     if c["tree"] == "dynamic" and sizes is None:
         result["build_tree"] = build_tree_timing(tv, torch, d, w, c)
     depth_present = np.where(np.arange(w.N)[None, :] < n_present[:, None], depth, -1)
@@ -429,6 +495,10 @@ def main():
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(w, depth, args.cpu_seconds, threads, sizes)
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
+        if args.config in (1, 2):  # the single-thread figure on the two small workloads
+            one = cpu_baseline(w, depth, min(args.cpu_seconds, 5.0), 1, sizes)
+            result["cpu_baseline"]["one_thread"] = {"value": one["value"], "sample": one["sample"]}
     print(json.dumps(result), flush=True)
 
 
