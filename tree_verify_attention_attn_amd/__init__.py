@@ -90,7 +90,9 @@ def _ctx(device: torch.device):
             raise TVError(s, "tv_create")
         _ctxs[idx] = h
     h = _ctxs[idx]
-    lib.tv_set_stream(h, ctypes.c_void_p(torch.cuda.current_stream(idx).cuda_stream))
+    s = lib.tv_set_stream(h, ctypes.c_void_p(torch.cuda.current_stream(idx).cuda_stream))
+    if s != OK:
+        raise TVError(s, "tv_set_stream")
     return h
 
 
