@@ -13,8 +13,8 @@
 // One wavefront per sequence. The sequence's proposal table (row i: what the
 // draft head proposes for the node created i-th, at most 128 x 32 entries) is
 // copied into LDS first, so every pop is LDS and register work: a
-// lane-strided scan of the candidate pool for each lane's best (score, queue
-// position), a wavefront maximum of those pairs moved with DPP row shifts and
+// lane-strided scan of the candidate pool (four loads in flight per lane) for
+// each lane's best (score, queue position), a wavefront maximum of those pairs moved with DPP row shifts and
 // broadcasts, and the new node's fields kept by lane node % 64, half
 // node / 64 (parent, token, depth, score, two-word ancestor set). Accepted
 // children are appended in slot order through a ballot prefix, which keeps
@@ -117,12 +117,16 @@ __global__ void __launch_bounds__(64) build_tree_kernel(const int32_t *__restric
       // best alive candidate: highest score, earliest queued on ties
       double bs = -1.0;
       int bj = 0x7FFFFFFF;
-      for (int j = lane; j < q; j += 64) {
-        const double sc = s_score[j];
-        if (sc > bs) {  // lane-strided j increases, so '>' keeps the earliest
-          bs = sc;
-          bj = j;
-        }
+      for (int j0 = lane; j0 < q; j0 += 64 * 4) {
+        double sc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sc[u] = j0 + 64 * u < q ? s_score[j0 + 64 * u] : -2.0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (sc[u] > bs) {  // positions increase, so '>' keeps the earliest
+            bs = sc[u];
+            bj = j0 + 64 * u;
+          }
       }
       wave_best(bs, bj);
       if (bs < 0.0) break;  // queue empty
