@@ -143,6 +143,32 @@ def test_greedy_grid_limit_is_reported():
     assert st == tv.UNSUPPORTED
 
 
+@pytest.mark.parametrize("N,V", [(1, 50), (6, 1), (1, 1), (1, 128256)])
+def test_degenerate_shapes_both_modes(N, V):
+    # root only (nothing to verify: the bonus is the root row's argmax or a
+    # draw from it), a one-token vocabulary (every draft matches, every
+    # distribution is the point mass), both
+    w = tvgen.make_workload(5, seed=N * 10 + V, with_kv=False, overrides=dict(B=5, N=N, V=V))
+    w.draft_tokens[:, :] = np.minimum(w.draft_tokens, V - 1)
+    print(f"[accept] degenerate N={N} V={V}", flush=True)
+    ref = greedy_compare(w, f"N{N}-V{V}")
+    assert (ref["accept_len"] == N).all() if V == 1 else (ref["accept_len"] == 1).all()
+    stochastic_compare(w, f"N{N}-V{V}-stochastic")
+
+
+def test_empty_batch_launches_nothing():
+    lib, p = tv.library(), tv._ptr
+    w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=1, N=2, V=4))
+    dw = DevWorkload(w, kv=False)
+    out = [dev(np.full(4, 7, np.int32)) for _ in range(4)]
+    for mode in (tv.GREEDY, tv.STOCHASTIC):
+        st = lib.tv_accept(tv._ctx(DEV), p(dw.target_logits), p(dw.draft_logits), p(dw.draft_tokens), p(dw.parents),
+                           None, p(dw.uniforms), 0, 2, 4, mode, 1.0, p(out[0]), p(out[1]), p(out[2]), p(out[3]), None, 0)
+        assert st == tv.OK
+    assert all((host(o) == 7).all() for o in out)
+    assert tv.tv_device_error(DEV) == 0
+
+
 def test_greedy_forest_nodes_never_accepted():
     w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=8, N=12, tree="forest", V=64))
     w.parents[:, 0] = -1
