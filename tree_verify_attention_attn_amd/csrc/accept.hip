@@ -472,8 +472,13 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
   for (int i = 1; i < kThreads / 64; ++i) mf = fmaxf(mf, redf[i]);
   const double mx = div_t(mf, T, invT);
   double zs = 0.0;
+  if (T == 1.0) {  // x / 1 = x exactly
 #pragma unroll 8
-  for (int it = 0; it < kPer; ++it) zs += exp_tab(div_t(v[it], T, invT) - mx, s_tab);  // -inf (padding) gives 0
+    for (int it = 0; it < kPer; ++it) zs += exp_tab(static_cast<double>(v[it]) - mx, s_tab);
+  } else {
+#pragma unroll 8
+    for (int it = 0; it < kPer; ++it) zs += exp_tab(div_t(v[it], T, invT) - mx, s_tab);  // -inf (padding) gives 0
+  }
   for (int m = 32; m >= 1; m >>= 1) zs += __shfl_xor(zs, m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = zs;
   __syncthreads();
