@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--ragged", action="store_true",
                     help="give each sequence a seeded node count in [N/2, N] (tree_sizes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="stop after the timed steps (no mask-cost, decode, cold-cache, builder or commit timings), "
+                         "so that a counter run sees the step's kernels only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one device-to-device copy of this many MiB (an HBM counter "
@@ -167,6 +170,16 @@ def cpu_baseline(w, depth, target_s, threads, sizes=None):
                        f"+ acceptance), {elapsed:.2f} s wall"
                        f"{f' (median of {len(runs)} runs)' if len(runs) > 1 else ''}, fp64 C oracle, "
                        f"{threads} threads", host_cores=os.cpu_count())
+
+
+def copy_for_calibration(torch, dev, mib):
+    """One device-to-device copy of `mib` MiB, whose counter readings calibrate
+    rocprofv3's FETCH_SIZE and WRITE_SIZE against known bytes."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def cpu_model():
@@ -428,6 +441,11 @@ def main():
         "tau": tau,
         "tau_cycles": cycles,
     }
+    if args.step_only:
+        if args.copy_mib > 0:
+            copy_for_calibration(torch, dev, args.copy_mib)
+        print(json.dumps(result), flush=True)
+        return
     # tree-mask cost: tv_attention with the tree mask against the same call
     # with tree_mask = NULL (every tree key visible), interleaved in blocks of
     # 20 calls so that clock drift affects both alike; medians of 5 blocks
@@ -516,12 +534,7 @@ def main():
     result["commit"] = commit_timing(tv, torch, dev, w, depth_present, d, kp, vp, table, plens, d(w.draft_tokens),
                                      outs)
     if args.copy_mib > 0:
-        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_for_calibration(torch, dev, args.copy_mib)
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(w, depth, args.cpu_seconds, threads, sizes)
