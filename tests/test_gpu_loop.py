@@ -2,8 +2,8 @@
 
 Each cycle builds the dynamic tree from the draft head's proposals
 (tv_build_tree), writes the tree nodes' K/V into the paged cache, runs
-tv_build_mask, tv_attention and greedy tv_accept, and commits the accepted
-path (tv_commit). The next cycle starts from what the commit left on the
+tv_build_mask, tv_attention and tv_accept (greedy, or sampled with uniforms
+passed in), and commits the accepted path (tv_commit). The next cycle starts from what the commit left on the
 device: the compacted cache, the grown prefix lengths and the next root
 token. Every step is compared with the oracle run on the same state: trees,
 masks, acceptance, committed pools and commit outputs bit-exact, attention
@@ -37,8 +37,8 @@ def proposals(seed, B, N, depth, k, V):
     return roots, toks, probs
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_draft_verify_cycles(D):
+@pytest.mark.parametrize("D,mode", [(64, "greedy"), (128, "greedy"), (128, "stochastic")])
+def test_draft_verify_cycles(D, mode):
     B, N, Hq, Hkv, V, k, depth, cycles = 3, 24, 8, 2, 600, 4, 5, 3
     w = tvgen.make_workload(2, seed=4242 + D, with_kv=False, with_logits=False,
                             overrides=dict(B=B, N=N, Hq=Hq, Hkv=Hkv, D=D, V=V, L=(20, 90), tree="chain"))
@@ -55,7 +55,7 @@ def test_draft_verify_cycles(D):
     roots = None
     accepted = 0
     for c in range(cycles):
-        print(f"[loop] D={D} cycle {c}: prefix lengths {lens.tolist()}", flush=True)
+        print(f"[loop] D={D} {mode} cycle {c}: prefix lengths {lens.tolist()}", flush=True)
         # 1. the dynamic tree, from this cycle's proposals and the last cycle's next root
         r0, toks, probs = proposals(900 + 10 * D + c, B, N, depth, k, V)
         roots = r0 if roots is None else roots
@@ -87,12 +87,22 @@ def test_draft_verify_cycles(D):
                                  max_prefix_len=max_len, page_table=table, num_pages=P, q=q, k_pages=host_k,
                                  v_pages=host_v)
         check_attention(host(out), oracle.attention(cw, ref_tree["mask"]), tight=TIGHT, what=f"cycle {c}")
-        # 4. greedy acceptance on logits that follow the tree part of the time
+        # 4. acceptance: greedy on logits that follow the tree part of the time;
+        # sampled with each node's draft row close to its parent's target row
         cw.target_logits = tvgen.normal_f32(700 + c, 4 + D, (B, N, V))
-        tvgen.plant_random(cw, 0.7, seed=c + D)
-        got = tv.tv_accept(dev(cw.target_logits), dev(tokens), dev(parents))
+        if mode == "greedy":
+            tvgen.plant_random(cw, 0.7, seed=c + D)
+            got = tv.tv_accept(dev(cw.target_logits), dev(tokens), dev(parents))
+            ref = oracle.accept_greedy(cw.target_logits, tokens, parents)
+        else:
+            near = tvgen.normal_f32(701 + c, 5 + D, (B, N, V), sigma=0.3)
+            draft = cw.target_logits[np.arange(B)[:, None], np.maximum(parents, 0)] + near
+            uni = tvgen.uniform_f32(702 + c, 6 + D, (B, N))
+            got = tv.tv_accept(dev(cw.target_logits), dev(tokens), dev(parents), mode=tv.STOCHASTIC,
+                               draft_logits=dev(draft), uniforms=dev(uni), temperature=1.0)
+            ref = oracle.accept_stochastic(cw.target_logits, draft, tokens, parents, uni, 1.0)
+            assert (ref["margins"] > 1e-9).all(), "a decision too close to call"
         assert tv.tv_device_error(DEV) == 0
-        ref = oracle.accept_greedy(cw.target_logits, tokens, parents)
         for key in ("accept_len", "path", "bonus"):
             assert (host(got[key]) == ref[key]).all(), (c, key)
         accepted += int((ref["accept_len"] - 1).sum())
