@@ -264,6 +264,22 @@ tv_status tv_device_error(tv_ctx *ctx, int32_t *code);
 
 const char *tv_status_string(tv_status s);
 
+/* Node budget of a draft tree for the current concurrency ([EAGLE-2 page],
+ * production guideline on switching by batch size: past about 32 concurrent
+ * requests verification becomes compute-bound, so the tree shrinks
+ * 64 -> 32 -> 16, and past a batch of 64 speculation is switched off). Host
+ * only; needs no context or GPU. The page gives the two thresholds and the
+ * three sizes; the reading taken here:
+ *   concurrency <= 32        max_nodes
+ *   32 < concurrency <= 48   max_nodes / 2   (the page places the second
+ *   48 < concurrency <= 64   max_nodes / 4    step nowhere; the midpoint)
+ *   concurrency > 64         1 (the root alone: a plain decode step, which
+ *                            the same calls run with N = 1)
+ * never below 1. Returns -1 if concurrency < 0 or max_nodes is outside
+ * [1, 128]. A caller passes the budget as N to tv_build_tree, or as the
+ * tree_sizes entries of buffers laid out for max_nodes. */
+int32_t tv_tree_budget(int32_t concurrency, int32_t max_nodes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,3 +49,14 @@ def test_product_path_never_loads_the_oracle():
             text = open(f).read()
             assert not re.search(r"\boracle\b", text), f
             assert "tvgen" not in text, f
+
+
+def test_tree_budget_follows_the_concurrency_schedule():
+    # the page's schedule: the full tree up to 32 concurrent requests, then
+    # 64 -> 32 -> 16, and plain decoding (the root alone) past 64
+    cases = {(0, 64): 64, (1, 64): 64, (32, 64): 64, (33, 64): 32, (48, 64): 32, (49, 64): 16, (64, 64): 16,
+             (65, 64): 1, (4096, 64): 1, (1, 128): 128, (40, 128): 64, (50, 128): 32, (60, 2): 1, (40, 1): 1}
+    for (c, n), want in cases.items():
+        assert tv.tv_tree_budget(c, n) == want, (c, n)
+    for c, n in ((-1, 64), (10, 0), (10, 129)):
+        assert tv.tv_tree_budget(c, n) == -1

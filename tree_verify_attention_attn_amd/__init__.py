@@ -65,6 +65,8 @@ def _load():
         lib.tv_device_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
         lib.tv_status_string.argtypes = [ctypes.c_int]
         lib.tv_status_string.restype = ctypes.c_char_p
+        lib.tv_tree_budget.argtypes = [i32, i32]
+        lib.tv_tree_budget.restype = i32
         for f in ("tv_create", "tv_destroy", "tv_set_stream", "tv_build_mask", "tv_attention", "tv_accept",
                   "tv_commit", "tv_build_tree", "tv_tau", "tv_tau_reset", "tv_device_error"):
             getattr(lib, f).restype = st
@@ -179,6 +181,11 @@ def tv_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
                                 Hq, Hkv, D,
                                 float(sm_scale), _ptr(out), odt, _ptr(workspace), ws_bytes), "tv_attention")
     return out
+
+
+def tv_tree_budget(concurrency: int, max_nodes: int = 64) -> int:
+    """Node budget of a draft tree at this concurrency (-1 for bad arguments)."""
+    return int(_load().tv_tree_budget(concurrency, max_nodes))
 
 
 def tv_accept_workspace_bytes(B, N, V, mode=GREEDY) -> int:

@@ -209,6 +209,18 @@ tv_status tv_device_error(tv_ctx *ctx, int32_t *code) {
   return TV_OK;
 }
 
+int32_t tv_tree_budget(int32_t concurrency, int32_t max_nodes) {
+  if (concurrency < 0 || max_nodes < 1 || max_nodes > 128) return -1;
+  int32_t n = max_nodes;
+  if (concurrency > 64)
+    n = 1;
+  else if (concurrency > 48)
+    n = max_nodes / 4;
+  else if (concurrency > 32)
+    n = max_nodes / 2;
+  return n < 1 ? 1 : n;
+}
+
 const char *tv_status_string(tv_status s) {
   switch (s) {
     case TV_OK: return "ok";
