@@ -1,6 +1,7 @@
 """Host-side checks of bench.py (no GPU): the algorithmic byte and FLOP
-figures its roofline divides by, against the survey's roofline table
-(computed separately from the workload definitions), and the one-GPU guard."""
+figures its roofline divides by, against figures worked out by hand from the
+workload definitions (KV, Q, output, mask and page-table bytes; one read of
+the logits), and the one-GPU guard."""
 import os
 import subprocess
 import sys
@@ -16,7 +17,7 @@ import bench  # noqa: E402
 
 
 @pytest.mark.parametrize("cfg,mb", [(1, 0.060), (2, 81.8), (3, 639.2), (4, 544.2)])
-def test_attention_bytes_match_the_roofline_table(cfg, mb):
+def test_attention_bytes_match_hand_figures(cfg, mb):
     w = tvgen.make_workload(cfg, with_kv=False, with_logits=False)
     assert bench.attention_bytes(w) / 1e6 == pytest.approx(mb, abs=0.05 if mb > 1 else 0.001)
 
