@@ -672,7 +672,10 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   constexpr int RPW = 64 / LPR;  // rows per wavefront
   constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63, sub = lane % LPR;
-  const int64_t r = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  // the rows of one (b, g) on the XCD whose L2 took that unit's partials
+  int64_t blk = blockIdx.x;
+  if (a.xcd_remap && (gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
+  const int64_t r = (blk * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
   if (r >= static_cast<int64_t>(a.B) * a.Hkv * a.rows) return;
   const int bh = static_cast<int>(r / a.rows), row = static_cast<int>(r % a.rows);
   const int b = bh / a.Hkv, g = bh % a.Hkv;
