@@ -82,7 +82,9 @@ tv_status tv_destroy(tv_ctx *ctx);
 /* Rebinds the context to another stream of the same device. Work already
  * queued on the previous stream is ordered before later calls (an event
  * recorded there that the new stream waits for), so the context's device
- * counters are never used by two calls at once. */
+ * counters are never used by two calls at once. The previous stream must
+ * still exist when this is called; rebinding to the same stream does
+ * nothing. */
 tv_status tv_set_stream(tv_ctx *ctx, void *hip_stream);
 
 /* Ancestor-or-self bitmask of every tree node ([EAGLE-2 page], reference
