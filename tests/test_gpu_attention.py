@@ -66,6 +66,19 @@ def test_bf16_output():
     check_attention(got, ref, what="bf16 out")
 
 
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 1e-3, 2.0])
+def test_unusual_scales(scale):
+    # a negative scale (Q is negated, |scale| used), zero (every visible key
+    # weighs the same), tiny, and large (a peaked softmax whose running max
+    # keeps jumping, so the lazy rescale runs)
+    import dataclasses
+    w = small("random", N=24, L=(100, 900), seed=11)
+    w = dataclasses.replace(w, sm_scale=np.float32(scale))
+    print(f"[attn] sm_scale={scale}", flush=True)
+    got, ref = run_full(w)
+    check_attention(got, ref, what=f"scale {scale}")
+
+
 def test_deterministic_and_page_permutation_invariant():
     w = small("random", N=30, L=(500, 900), seed=8)
     dw = DevWorkload(w, logits=False)
