@@ -265,6 +265,21 @@ def test_stochastic_tree_shapes(tree):
     stochastic_compare(w, f"tree-{tree}")
 
 
+@pytest.mark.parametrize("T", [0.6, 1.7])
+def test_stochastic_tree_temperatures(T):
+    # sampled acceptance on dynamic trees away from T = 1 (logits divided by
+    # T in fp64 on both sides)
+    w = tvgen.make_workload(2, seed=62, with_kv=False,
+                            overrides=dict(B=24, N=40, V=5000, tree="dynamic", max_depth=5, topk=6, mode="stochastic"))
+    near = tvgen.normal_f32(62, 96, w.draft_logits.shape, sigma=0.3)
+    for b in range(w.B):
+        for c in range(1, w.N):
+            w.draft_logits[b, c] = w.target_logits[b, w.parents[b, c]] + near[b, c]
+    w.temperature = T
+    ref = stochastic_compare(w, f"tree-T{T}")
+    assert ref["accept_len"].max() >= 3
+
+
 def test_stochastic_tree_hand_worked_fixture():
     import json
     import os
