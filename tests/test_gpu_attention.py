@@ -79,6 +79,16 @@ def test_unusual_scales(scale):
     check_attention(got, ref, what=f"scale {scale}")
 
 
+def test_many_short_row_groups_of_mixed_lengths():
+    # more one-workgroup units than CUs (the MTP-chain shape: at most 32 rows
+    # per KV head) with prefixes from 0 to 3000: the units are dispatched
+    # longest first; every row against the oracle
+    w = small("chain", B=300, Hq=4, Hkv=1, D=128, L=(0, 3000), N=3, seed=21)
+    print(f"[attn] mixed lengths B={w.B} rows/unit={w.N * w.Hq // w.Hkv}", flush=True)
+    got, ref = run_full(w)
+    check_attention(got, ref, what="mixed lengths")
+
+
 def test_deterministic_and_page_permutation_invariant():
     w = small("random", N=30, L=(500, 900), seed=8)
     dw = DevWorkload(w, logits=False)

@@ -63,6 +63,7 @@ struct AttnArgs {
   float *ws_o, *ws_ml;
   int S, chunk_tiles;
   int xcd_remap;   // block ids are laid out so one (b, g) stays on one XCD
+  const int32_t *order;  // or null: workgroup i runs unit order[i] (one split, one row group)
   unsigned long long *state;
 };
 
@@ -171,7 +172,10 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 
   // block -> (b, g, row group, split); consecutive logical ids share an XCD
   int id = blockIdx.x;
-  if (a.xcd_remap) id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
+  if (a.order)
+    id = a.order[id];  // one workgroup per (b, g): the longest units are dispatched first
+  else if (a.xcd_remap)
+    id = (id & 7) * (gridDim.x >> 3) + (id >> 3);
   const int s = id % a.S;
   const int rg = (id / a.S) % a.row_groups;
   const int bh = id / (a.S * a.row_groups);
@@ -732,6 +736,52 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   store_out(a, base, 4 * sub, v4);
 }
 
+// Orders the (b, g) units of a one-split plan by their number of 64-key tiles,
+// longest first, so that a batch with very different prefix lengths does not
+// end on its longest units (workgroups are dispatched in block order). One
+// workgroup: a counting sort over tile counts (clamped to kOrderBuckets - 1).
+// Only the schedule changes; every unit computes the same result.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = kOrderThreads;
+
+__global__ void __launch_bounds__(kOrderThreads) order_units_kernel(const int32_t *__restrict__ prefix_lens,
+                                                                    const int32_t *__restrict__ sizes, int B, int N,
+                                                                    int Hkv, int max_prefix_len,
+                                                                    int32_t *__restrict__ order) {
+  __shared__ int s_cnt[kOrderBuckets];
+  __shared__ int s_wsum[kOrderThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  auto bucket = [&](int b) {  // bucket 0 holds the most tiles
+    const int L = prefix_lens[b];
+    const int nb_in = sizes ? sizes[b] : N;
+    const bool bad = L < 0 || L > max_prefix_len || nb_in < 1 || nb_in > N;
+    const int t = bad ? 0 : (L + nb_in + 63) / 64;
+    return kOrderBuckets - 1 - min(t, kOrderBuckets - 1);
+  };
+  s_cnt[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < B; b += kOrderThreads) atomicAdd(&s_cnt[bucket(b)], 1);
+  __syncthreads();
+  // exclusive scan of the bucket counts: within each wavefront, then over
+  // the wavefront totals
+  const int c = s_cnt[tid];
+  int incl = c;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) s_wsum[tid >> 6] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < (tid >> 6); ++i) off += s_wsum[i];
+  s_cnt[tid] = off + incl - c;
+  __syncthreads();
+  for (int b = tid; b < B; b += kOrderThreads) {
+    const int64_t pos = atomicAdd(&s_cnt[bucket(b)], 1);
+    for (int g = 0; g < Hkv; ++g) order[pos * Hkv + g] = b * Hkv + g;
+  }
+}
+
 constexpr int kStages = 4;
 
 template <int D, bool FLAT>
@@ -781,6 +831,10 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
   if (p.S < 1) p.S = 1;
   p.ws_bytes =
       p.S > 1 ? static_cast<size_t>(B) * Hkv * p.S * p.row_blocks * p.row_block * (D + 2) * sizeof(float) : 0;
+  // many one-workgroup units (the key-split shape: short rows, many
+  // sequences) whose prefix lengths may differ: dispatch the longest first
+  p.order = (p.ksplit && p.S == 1 && base > cu_count) ? 1 : 0;
+  if (p.order) p.ws_bytes = static_cast<size_t>(B) * Hkv * sizeof(int32_t);
   return p;
 }
 
@@ -824,6 +878,12 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   }
   const int blocks = B * Hkv * plan.row_blocks * plan.S;
   a.xcd_remap = (blocks % 8) == 0;
+  if (plan.order) {
+    a.order = static_cast<const int32_t *>(workspace);
+    hipLaunchKernelGGL(order_units_kernel, dim3(1), dim3(kOrderThreads), 0, ctx->stream, prefix_lens, tree_sizes, B,
+                       N, Hkv, max_prefix_len, static_cast<int32_t *>(workspace));
+    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  }
   const dim3 grid(blocks);
   const dim3 block(64 * plan.qb);
   // one buffer resource per pool when the pool is below 2 GiB (page offsets

@@ -75,7 +75,8 @@ struct AttnPlan {
   int ksplit;       // 1: two wavefronts share one 32-row block and split its tiles
   int row_block;    // query rows (node, head-in-group) per workgroup
   int row_blocks;   // ceil(G*N / row_block)
-  size_t ws_bytes;  // fp32 partials + (m, l)
+  int order;        // 1: workgroups take (sequence, KV head) units longest first (order in the workspace)
+  size_t ws_bytes;  // fp32 partials + (m, l), or the unit order
 };
 AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int max_prefix_len);
 tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, const void *k_pages,
