@@ -136,9 +136,13 @@ tv_status tv_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *
                         int32_t *n_nodes);
 
 /* Workspace (bytes) tv_attention needs for these host scalars: fp32 partial
- * results when one sequence's keys are split over several workgroups. The
- * split plan depends only on these arguments and the device's CU count, so
- * repeated calls are bitwise reproducible. May be 0. */
+ * results when one sequence's keys are split over several workgroups, or,
+ * for many short row groups (at most 32 query rows per KV head, more
+ * (sequence, KV head) units than CUs), the order in which the units are
+ * dispatched (longest prefix first; B * Hkv int32). The plan depends only on
+ * these arguments and the device's CU count, and results do not depend on
+ * the dispatch order, so repeated calls are bitwise reproducible. May be 0;
+ * its contents need no initialisation. */
 size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                     int32_t max_prefix_len);
 
