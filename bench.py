@@ -169,7 +169,7 @@ def cpu_baseline(w, depth, target_s, threads, sizes=None):
     toks = int(n[:done].sum())
     return dict(value=toks / elapsed, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{done} of {w.B} sequences ({toks} tree tokens, {toks * w.Hq} attention rows "
-                       f"+ acceptance), {elapsed:.2f} s wall"
+                       f"+ acceptance), {elapsed:.3g} s wall"
                        f"{f' (median of {len(runs)} runs)' if len(runs) > 1 else ''}, fp64 C oracle, "
                        f"{threads} threads", host_cores=os.cpu_count())
 
