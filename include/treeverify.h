@@ -142,7 +142,8 @@ tv_status tv_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *
  * dispatched (longest prefix first; B * Hkv int32). The plan depends only on
  * these arguments and the device's CU count, and results do not depend on
  * the dispatch order, so repeated calls are bitwise reproducible. May be 0;
- * its contents need no initialisation. */
+ * its contents need no initialisation. Also 0 for shapes tv_attention
+ * refuses (N > 128, max_prefix_len > 2^30). */
 size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                     int32_t max_prefix_len);
 
@@ -165,7 +166,9 @@ size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t H
  *                written and their keys are never read
  *   out          [B][N][Hq][D] in out_dtype (TV_F32 or TV_BF16)
  *   workspace    >= tv_attention_workspace_bytes(...) bytes (may be NULL if 0)
- * Requires D in {64, 128}, Hq % Hkv == 0, 0 <= N <= 128. Accumulates in fp32. */
+ * Requires D in {64, 128}, Hq % Hkv == 0, 0 <= N <= 128. Accumulates in fp32.
+ * Returns TV_ERR_UNSUPPORTED when max_prefix_len > 2^30 or when the launch
+ * would need more than 2^31 - 1 workgroups (B * Hkv * row groups * splits). */
 tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const void *v_pages, int64_t num_pages,
                        const int32_t *page_table, int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len,
                        const uint64_t *tree_mask, const int32_t *tree_sizes, int32_t B, int32_t N, int32_t Hq,
@@ -253,7 +256,7 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
  * [0, num_pages) at a touched position is left unchanged (new length L,
  * next root -1, emitted -1) and sets the sticky TV_ERR_INVALID_ARG.
  * Requires D in {64, 128}, 1 <= N <= 128 when B > 0, maxp * 16 >=
- * max_prefix_len + N. */
+ * max_prefix_len + N; max_prefix_len > 2^30 returns TV_ERR_UNSUPPORTED. */
 tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages, const int32_t *page_table,
                     int32_t maxp, const int32_t *prefix_lens, int32_t max_prefix_len, const int32_t *draft_tokens,
                     const int32_t *path, const int32_t *accept_len, const int32_t *bonus_token, int32_t B, int32_t N,

@@ -197,3 +197,23 @@ def test_host_detected_errors():
     if need > 0:
         assert call(workspace=torch.empty(need - 1, dtype=torch.uint8, device=DEV)) == tv.WORKSPACE
     assert tv.tv_device_error(DEV) == 0
+
+
+def test_size_limits_are_reported():
+    # token positions and key counts are int32 inside the kernels: a prefix
+    # bound above 2^30 is refused before any launch, by tv_attention and by
+    # tv_commit, and the workspace query returns 0 for it
+    lib, p = tv.library(), tv._ptr
+    ctx = tv._ctx(DEV)
+    big = (1 << 30) + 1
+    maxp = (big + 16 + 15) // 16
+    buf = dev(np.zeros(64, np.int32))
+    assert lib.tv_attention_workspace_bytes(ctx, 1, 2, 4, 1, 64, big) == 0
+    assert lib.tv_attention_workspace_bytes(ctx, 1, 2, 4, 1, 64, 1 << 30) > 0
+    st = lib.tv_attention(ctx, p(buf), p(buf), p(buf), 1, p(buf), maxp, p(buf), big, None, None, 1, 2, 4, 1, 64,
+                          1.0, p(buf), tv.F32, None, 0)
+    assert st == tv.UNSUPPORTED
+    st = lib.tv_commit(ctx, p(buf), p(buf), 1, p(buf), maxp, p(buf), big, p(buf), p(buf), p(buf), p(buf), 1, 2, 1, 64,
+                       p(buf), None, p(buf))
+    assert st == tv.UNSUPPORTED
+    assert tv.tv_device_error(DEV) == 0

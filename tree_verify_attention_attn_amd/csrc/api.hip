@@ -97,6 +97,7 @@ tv_status tv_build_mask(tv_ctx *ctx, const int32_t *parents, const int32_t *tree
 size_t tv_attention_workspace_bytes(tv_ctx *ctx, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                     int32_t max_prefix_len) {
   if (!ctx || B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_prefix_len < 0) return 0;
+  if (N > 128 || max_prefix_len > kMaxPrefix) return 0;
   return plan_attention(ctx->cu_count, B, N, Hq, Hkv, D, max_prefix_len).ws_bytes;
 }
 
@@ -109,13 +110,15 @@ tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const vo
     return TV_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return TV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
-  if (N > 128) return TV_ERR_UNSUPPORTED;
+  if (N > 128 || max_prefix_len > kMaxPrefix) return TV_ERR_UNSUPPORTED;
   if (!isfinite(sm_scale)) return TV_ERR_INVALID_ARG;
   if (out_dtype != TV_F32 && out_dtype != TV_BF16) return TV_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * N == 0) return TV_OK;
   if (static_cast<int64_t>(maxp) * kPage < static_cast<int64_t>(max_prefix_len) + N) return TV_ERR_INVALID_ARG;
   if (!q || !k_pages || !v_pages || !page_table || !prefix_lens || !out) return TV_ERR_INVALID_ARG;
   const AttnPlan plan = plan_attention(ctx->cu_count, B, N, Hq, Hkv, D, max_prefix_len);
+  // one workgroup per (b, g, row group, split) on a 1-D grid of int32 block ids
+  if (static_cast<int64_t>(B) * Hkv * plan.row_blocks * plan.S > 0x7FFFFFFF) return TV_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return TV_ERR_WORKSPACE;
   return launch_attention(ctx, plan, q, k_pages, v_pages, num_pages, page_table, maxp, prefix_lens, max_prefix_len,
                           tree_mask, tree_sizes, B, N, Hq, Hkv, D, sm_scale, out, out_dtype, workspace);
@@ -157,7 +160,7 @@ tv_status tv_commit(tv_ctx *ctx, void *k_pages, void *v_pages, int64_t num_pages
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
   if (B == 0) return TV_OK;
   if (N < 1) return TV_ERR_INVALID_ARG;
-  if (N > 128) return TV_ERR_UNSUPPORTED;
+  if (N > 128 || max_prefix_len > kMaxPrefix) return TV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * Hkv > 0x7FFFFFFF) return TV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(maxp) * kPage < static_cast<int64_t>(max_prefix_len) + N) return TV_ERR_INVALID_ARG;
   if (!k_pages || !v_pages || !page_table || !prefix_lens || !draft_tokens || !path || !accept_len || !bonus_token ||

@@ -26,6 +26,7 @@ struct tv_ctx {
 namespace tv {
 
 constexpr int kPage = 16;
+constexpr int kMaxPrefix = 1 << 30;  // largest max_prefix_len: token positions and key counts stay in int32
 constexpr int kMaxFusedSeqs = 65536;  // sequences with an arrival counter for one-launch greedy acceptance
 
 // Records the first device-detected error of a context (later ones are dropped).
