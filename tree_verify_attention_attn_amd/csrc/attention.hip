@@ -181,6 +181,24 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   const int bh = id / (a.S * a.row_groups);
   const int b = bh / a.Hkv, g = bh % a.Hkv;
 
+  // this split's page-table entries, read before the sequence's length and
+  // node count are known so that the two reads overlap (entries past the
+  // sequence's last page are dropped once the length is in; the read stays
+  // inside the table's row). All of a thread's loads are issued at once.
+  constexpr int kPidPerThread = kMaxChunkTiles * (kKeys / kPage) / (64 * NW);
+  const int t_begin = s * a.chunk_tiles;
+  const int64_t pt_row = static_cast<int64_t>(b) * a.maxp;
+  int pid_in[kPidPerThread];
+  {
+    const int p0 = t_begin * (kKeys / kPage);
+    const int avail = min(a.chunk_tiles * (kKeys / kPage), a.maxp - p0);
+#pragma unroll
+    for (int e = 0; e < kPidPerThread; ++e) {
+      const int i = tid + e * 64 * NW;
+      pid_in[e] = i < avail ? a.page_table[pt_row + p0 + i] : -1;
+    }
+  }
+
   const int L = a.prefix_lens[b];
   // node count of this sequence: nodes past it are absent (no query rows,
   // no keys); a count outside [1, N] is bad data, reported like a bad length
@@ -192,7 +210,6 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   const bool bad_len = L < 0 || L > a.max_prefix_len || bad_size;
   const int T = bad_len ? 0 : L + nb;
   const int tiles_b = (T + kKeys - 1) / kKeys;
-  const int t_begin = s * a.chunk_tiles;
   const int t_end = min(t_begin + a.chunk_tiles, tiles_b);
   const int ntiles = max(t_end - t_begin, 0);
   if (tid == 0) s_bad = 0;
@@ -253,7 +270,6 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   const int page_elems = a.Hkv * kPage * D;
   const int page_bytes = page_elems * 2;
   const uint32_t npages32 = static_cast<uint32_t>(min(a.num_pages, static_cast<int64_t>(0x7FFFFFFF)));
-  const int64_t pt_row = static_cast<int64_t>(b) * a.maxp;
   const uint32_t smem_base = lds_addr_of(&smem[0][0][0]);
   bool load_bad = false;
   int dma_off[IPW];  // byte offset of the lane's chunk inside its page (row slot, KV head, chunk)
@@ -340,7 +356,11 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   {
     const int p0 = t_begin * (kKeys / kPage);
     const int used = min(t_end * (kKeys / kPage), (T + kPage - 1) / kPage) - p0;
-    for (int i = tid; i < ntiles * (kKeys / kPage); i += 64 * NW) s_pid[i] = i < used ? a.page_table[pt_row + p0 + i] : -1;
+#pragma unroll
+    for (int e = 0; e < kPidPerThread; ++e) {
+      const int i = tid + e * 64 * NW;
+      if (i < ntiles * (kKeys / kPage)) s_pid[i] = i < used ? pid_in[e] : -1;
+    }
     __syncthreads();
   }
 
