@@ -217,3 +217,30 @@ def test_size_limits_are_reported():
                        p(buf), None, p(buf))
     assert st == tv.UNSUPPORTED
     assert tv.tv_device_error(DEV) == 0
+
+
+def test_binding_checks_arguments():
+    # mixed devices, wrong dtypes and wrong shapes are refused by the binding
+    # before any pointer reaches the library
+    w = small("random", N=10, L=(40, 90), B=2)
+    dw = DevWorkload(w, logits=False)
+    mask, _ = tv.tv_build_mask(dw.parents)
+    base = dict(q=dw.q, k_pages=dw.k, v_pages=dw.v, page_table=dw.page_table, prefix_lens=dw.prefix_lens,
+                max_prefix_len=w.max_prefix_len, tree_mask=mask, sm_scale=float(w.sm_scale))
+
+    def refused(exc, **kw):
+        args = dict(base)
+        args.update(kw)
+        with pytest.raises(exc):
+            tv.tv_attention(**args)
+
+    refused(ValueError, prefix_lens=dw.prefix_lens.cpu())
+    refused(TypeError, page_table=dw.page_table.long())
+    refused(ValueError, prefix_lens=dw.prefix_lens[:1].contiguous())
+    refused(ValueError, tree_mask=torch.zeros((w.B, w.N, 2), dtype=torch.int64, device=DEV))
+    refused(ValueError, v_pages=dw.v[:, :, :8].contiguous())
+    refused(ValueError, out=torch.empty((w.B, w.N, w.Hq, w.D + 1), dtype=torch.float32, device=DEV))
+    refused(TypeError, out=torch.empty((w.B, w.N, w.Hq, w.D), dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError):
+        tv.tv_build_mask(dw.parents, mask=torch.zeros((w.B, w.N, 2), dtype=torch.int64, device=DEV))
+    assert tv.tv_device_error(DEV) == 0

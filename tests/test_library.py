@@ -5,6 +5,8 @@ import glob
 import os
 import re
 
+import pytest
+
 import tree_verify_attention_attn_amd as tv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -60,3 +62,25 @@ def test_tree_budget_follows_the_concurrency_schedule():
         assert tv.tv_tree_budget(c, n) == want, (c, n)
     for c, n in ((-1, 64), (10, 0), (10, 129)):
         assert tv.tv_tree_budget(c, n) == -1
+
+
+def test_binding_refuses_host_tensors():
+    # a host tensor's address means nothing to the kernels: the binding
+    # refuses it before the library is called (no GPU needed)
+    import torch
+    import tree_verify_attention_attn_amd as tv
+    q = torch.zeros((1, 2, 4, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 1, 16, 64), dtype=torch.bfloat16)
+    i32 = torch.zeros((1, 2), dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        tv.tv_attention(q, kv, kv, i32, torch.zeros(1, dtype=torch.int32), 8, None, 1.0)
+    with pytest.raises(ValueError, match="GPU"):
+        tv.tv_build_mask(i32)
+    with pytest.raises(ValueError, match="GPU"):
+        tv.tv_accept(torch.zeros((1, 2, 8)), i32, i32)
+    with pytest.raises(ValueError, match="GPU"):
+        tv.tv_commit(kv, kv, i32, torch.zeros(1, dtype=torch.int32), 8, i32, i32, torch.zeros(1, dtype=torch.int32),
+                     torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        tv.tv_build_tree(torch.zeros(1, dtype=torch.int32), torch.zeros((1, 2, 3), dtype=torch.int32),
+                         torch.zeros((1, 2, 3)), 3, 0.0, 2)

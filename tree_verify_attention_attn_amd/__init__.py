@@ -24,6 +24,7 @@ GREEDY, STOCHASTIC = 0, 1
 
 _lib = None
 _ctxs = {}
+_bound = {}  # device index -> stream handle the context is bound to
 
 
 class TVError(RuntimeError):
@@ -87,14 +88,19 @@ def _ctx(device: torch.device):
     lib = _load()
     if idx not in _ctxs:
         h = ctypes.c_void_p()
-        s = lib.tv_create(ctypes.byref(h), idx, ctypes.c_void_p(torch.cuda.current_stream(idx).cuda_stream))
+        st0 = torch.cuda.current_stream(idx).cuda_stream
+        s = lib.tv_create(ctypes.byref(h), idx, ctypes.c_void_p(st0))
         if s != OK:
             raise TVError(s, "tv_create")
         _ctxs[idx] = h
+        _bound[idx] = st0
     h = _ctxs[idx]
-    s = lib.tv_set_stream(h, ctypes.c_void_p(torch.cuda.current_stream(idx).cuda_stream))
-    if s != OK:
-        raise TVError(s, "tv_set_stream")
+    st = torch.cuda.current_stream(idx).cuda_stream
+    if _bound.get(idx) != st:  # rebinding orders the new stream after the old one's queued work
+        s = lib.tv_set_stream(h, ctypes.c_void_p(st))
+        if s != OK:
+            raise TVError(s, "tv_set_stream")
+        _bound[idx] = st
     return h
 
 
@@ -106,6 +112,52 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _arg(t, name: str, dtype: torch.dtype, shape: tuple, dev: torch.device, optional: bool = False):
+    """Checks a tensor argument before its pointer reaches the library: a
+    contiguous tensor of this dtype and shape (None matches any extent) on the
+    call's GPU. A host tensor or another device's would be read by the kernels
+    at a meaningless address. The common case costs about a microsecond; the
+    message is built only on failure."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    try:
+        ok = t.dtype is dtype and t.get_device() == dev.index and t.is_contiguous()
+        shp = t.shape
+    except AttributeError:
+        raise TypeError(f"{name} must be a torch.Tensor") from None
+    if ok and len(shp) == len(shape):
+        for e, x in zip(shape, shp):
+            if e is not None and x != e:
+                break
+        else:
+            return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+    raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
+def _device_of(t: torch.Tensor, name: str) -> torch.device:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, not {t.device}")
+    return t.device if t.device.index is not None else torch.device("cuda", torch.cuda.current_device())
+
+
+def _p(t: Optional[torch.Tensor]):
+    """Pointer of a tensor that _arg has already checked."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
 def _check(s: int, what: str):
     if s != OK:
         raise TVError(s, what)
@@ -115,15 +167,20 @@ def tv_build_mask(parents: torch.Tensor, mask: Optional[torch.Tensor] = None, de
                   tree_sizes: Optional[torch.Tensor] = None):
     """parents int32 [B][N] (N <= 128), tree_sizes int32 [B] or None ->
     (mask uint64-as-int64 [B][N][ceil(N/64)], depth int32 [B][N])."""
+    dev = _device_of(parents, "parents")
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B][N]")
     B, N = parents.shape
-    dev = parents.device
     W = max((N + 63) // 64, 1)
     if mask is None:
         mask = torch.empty((B, N, W), dtype=torch.int64, device=dev)
     if depth is None:
         depth = torch.empty((B, N), dtype=torch.int32, device=dev)
-    assert parents.dtype == torch.int32
-    _check(_load().tv_build_mask(_ctx(dev), _ptr(parents), _ptr(tree_sizes), B, N, _ptr(mask), _ptr(depth)),
+    _arg(parents, "parents", torch.int32, (B, N), dev)
+    _arg(tree_sizes, "tree_sizes", torch.int32, (B,), dev, optional=True)
+    _arg(mask, "mask", torch.int64, (B, N, W), dev)
+    _arg(depth, "depth", torch.int32, (B, N), dev, optional=True)
+    _check(_load().tv_build_mask(_ctx(dev), _p(parents), _p(tree_sizes), B, N, _p(mask), _p(depth)),
            "tv_build_mask")
     return mask, depth
 
@@ -132,10 +189,13 @@ def tv_build_tree(root_tokens: torch.Tensor, cand_tokens: torch.Tensor, cand_pro
                   threshold: float, max_depth: int, outputs: Optional[dict] = None) -> dict:
     """root_tokens int32 [B]; cand_tokens int32 / cand_probs fp32 [B][N][k] ->
     dict(parents, tokens, depth [B][N] int32, mask int64 [B][N][W], scores fp64 [B][N], n_nodes [B])."""
+    dev = _device_of(cand_tokens, "cand_tokens")
+    if cand_tokens.dim() != 3:
+        raise ValueError("cand_tokens must be [B][N][k]")
     B, N, k = cand_tokens.shape
-    assert cand_probs.shape == cand_tokens.shape and cand_probs.dtype == torch.float32
-    assert cand_tokens.dtype == torch.int32 and root_tokens.dtype == torch.int32
-    dev = cand_tokens.device
+    _arg(cand_tokens, "cand_tokens", torch.int32, (B, N, k), dev)
+    _arg(cand_probs, "cand_probs", torch.float32, (B, N, k), dev)
+    _arg(root_tokens, "root_tokens", torch.int32, (B,), dev)
     if outputs is None:
         outputs = dict(parents=torch.empty((B, N), dtype=torch.int32, device=dev),
                        tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
@@ -144,10 +204,17 @@ def tv_build_tree(root_tokens: torch.Tensor, cand_tokens: torch.Tensor, cand_pro
                        scores=torch.empty((B, N), dtype=torch.float64, device=dev),
                        n_nodes=torch.empty(B, dtype=torch.int32, device=dev))
     o = outputs
-    _check(_load().tv_build_tree(_ctx(dev), _ptr(root_tokens), _ptr(cand_tokens), _ptr(cand_probs), B, N, k, k_root,
-                                 float(threshold), max_depth, _ptr(o["parents"]), _ptr(o["tokens"]),
-                                 _ptr(o.get("depth")), _ptr(o.get("mask")), _ptr(o.get("scores")),
-                                 _ptr(o.get("n_nodes"))), "tv_build_tree")
+    W = (N + 63) // 64
+    _arg(o.get("parents"), "outputs['parents']", torch.int32, (B, N), dev)
+    _arg(o.get("tokens"), "outputs['tokens']", torch.int32, (B, N), dev)
+    _arg(o.get("depth"), "outputs['depth']", torch.int32, (B, N), dev, optional=True)
+    _arg(o.get("mask"), "outputs['mask']", torch.int64, (B, N, W), dev, optional=True)
+    _arg(o.get("scores"), "outputs['scores']", torch.float64, (B, N), dev, optional=True)
+    _arg(o.get("n_nodes"), "outputs['n_nodes']", torch.int32, (B,), dev, optional=True)
+    _check(_load().tv_build_tree(_ctx(dev), _p(root_tokens), _p(cand_tokens), _p(cand_probs), B, N, k, k_root,
+                                 float(threshold), max_depth, _p(o["parents"]), _p(o["tokens"]),
+                                 _p(o.get("depth")), _p(o.get("mask")), _p(o.get("scores")),
+                                 _p(o.get("n_nodes"))), "tv_build_tree")
     return outputs
 
 
@@ -162,24 +229,37 @@ def tv_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     """q bf16 [B][N][Hq][D]; k/v_pages bf16 [P][Hkv][16][D]; page_table int32 [B][maxp];
     prefix_lens int32 [B]; tree_mask int64 [B][N][W] or None; tree_sizes int32 [B] or None
     -> out [B][N][Hq][D] (rows of absent nodes are not written)."""
+    dev = _device_of(q, "q")
+    if q.dim() != 4 or not isinstance(k_pages, torch.Tensor) or k_pages.dim() != 4:
+        raise ValueError("q must be [B][N][Hq][D] and k_pages [P][Hkv][16][D]")
     B, N, Hq, D = q.shape
-    P, Hkv, page, D2 = k_pages.shape
-    assert page == 16 and D2 == D and q.dtype == torch.bfloat16 and k_pages.dtype == torch.bfloat16
-    assert v_pages.shape == k_pages.shape and v_pages.dtype == torch.bfloat16
-    assert page_table.dtype == torch.int32 and prefix_lens.dtype == torch.int32
-    dev = q.device
+    P, Hkv = k_pages.shape[0], k_pages.shape[1]
+    _arg(q, "q", torch.bfloat16, (B, N, Hq, D), dev)
+    _arg(k_pages, "k_pages", torch.bfloat16, (P, Hkv, 16, D), dev)
+    _arg(v_pages, "v_pages", torch.bfloat16, (P, Hkv, 16, D), dev)
+    _arg(page_table, "page_table", torch.int32, (None, None), dev)
+    if page_table.shape[0] < B:  # rows past B (a larger table) are never read
+        raise ValueError(f"page_table has {page_table.shape[0]} rows, fewer than the batch's {B}")
+    _arg(prefix_lens, "prefix_lens", torch.int32, (B,), dev)
+    _arg(tree_mask, "tree_mask", torch.int64, (B, N, max((N + 63) // 64, 1)), dev, optional=True)
+    _arg(tree_sizes, "tree_sizes", torch.int32, (B,), dev, optional=True)
     if out is None:
         out = torch.empty((B, N, Hq, D), dtype=out_dtype, device=dev)
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be a float32 or bfloat16 tensor")
+    _arg(out, "out", out.dtype, (B, N, Hq, D), dev)
+    _arg(workspace, "workspace", torch.uint8, (None,), dev, optional=True)
     odt = {torch.float32: F32, torch.bfloat16: BF16}[out.dtype]
     h = _ctx(dev)
-    need = int(_load().tv_attention_workspace_bytes(h, B, N, Hq, Hkv, D, max_prefix_len))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:  # a given workspace's size is checked by the library
+        need = int(_load().tv_attention_workspace_bytes(h, B, N, Hq, Hkv, D, max_prefix_len))
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_load().tv_attention(h, _ptr(q), _ptr(k_pages), _ptr(v_pages), P, _ptr(page_table), page_table.shape[1],
-                                _ptr(prefix_lens), int(max_prefix_len), _ptr(tree_mask), _ptr(tree_sizes), B, N,
+    _check(_load().tv_attention(h, _p(q), _p(k_pages), _p(v_pages), P, _p(page_table), page_table.shape[1],
+                                _p(prefix_lens), int(max_prefix_len), _p(tree_mask), _p(tree_sizes), B, N,
                                 Hq, Hkv, D,
-                                float(sm_scale), _ptr(out), odt, _ptr(workspace), ws_bytes), "tv_attention")
+                                float(sm_scale), _p(out), odt, _p(workspace), ws_bytes), "tv_attention")
     return out
 
 
@@ -197,23 +277,34 @@ def tv_accept(target_logits: torch.Tensor, draft_tokens: torch.Tensor, parents: 
               temperature: float = 1.0, outputs: Optional[dict] = None, want_argmax: bool = True,
               workspace: Optional[torch.Tensor] = None, tree_sizes: Optional[torch.Tensor] = None) -> dict:
     """Returns dict(accept_len [B], path [B][N], bonus [B], target_argmax [B][N] (greedy))."""
+    dev = _device_of(target_logits, "target_logits")
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B][N][V]")
     B, N, V = target_logits.shape
-    dev = target_logits.device
-    assert target_logits.dtype == torch.float32 and draft_tokens.dtype == torch.int32 and parents.dtype == torch.int32
+    _arg(target_logits, "target_logits", torch.float32, (B, N, V), dev)
+    _arg(draft_tokens, "draft_tokens", torch.int32, (B, N), dev)
+    _arg(parents, "parents", torch.int32, (B, N), dev)
+    _arg(draft_logits, "draft_logits", torch.float32, (B, N, V), dev, optional=True)
+    _arg(uniforms, "uniforms", torch.float32, (B, N), dev, optional=True)
+    _arg(tree_sizes, "tree_sizes", torch.int32, (B,), dev, optional=True)
     if outputs is None:
         outputs = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
                        path=torch.empty((B, N), dtype=torch.int32, device=dev),
                        bonus=torch.empty(B, dtype=torch.int32, device=dev))
         if mode == GREEDY and want_argmax:
             outputs["target_argmax"] = torch.empty((B, N), dtype=torch.int32, device=dev)
-    need = tv_accept_workspace_bytes(B, N, V, mode)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _arg(outputs.get("accept_len"), "outputs['accept_len']", torch.int32, (B,), dev)
+    _arg(outputs.get("path"), "outputs['path']", torch.int32, (B, N), dev)
+    _arg(outputs.get("bonus"), "outputs['bonus']", torch.int32, (B,), dev)
+    _arg(outputs.get("target_argmax"), "outputs['target_argmax']", torch.int32, (B, N), dev, optional=True)
+    if workspace is None:  # a given workspace's size is checked by the library
+        workspace = torch.empty(max(tv_accept_workspace_bytes(B, N, V, mode), 1), dtype=torch.uint8, device=dev)
+    _arg(workspace, "workspace", torch.uint8, (None,), dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(_load().tv_accept(_ctx(dev), _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(parents),
-                             _ptr(tree_sizes), _ptr(uniforms), B, N, V, mode, float(temperature), _ptr(outputs["accept_len"]),
-                             _ptr(outputs["path"]), _ptr(outputs["bonus"]), _ptr(outputs.get("target_argmax")),
-                             _ptr(workspace), ws_bytes), "tv_accept")
+    _check(_load().tv_accept(_ctx(dev), _p(target_logits), _p(draft_logits), _p(draft_tokens), _p(parents),
+                             _p(tree_sizes), _p(uniforms), B, N, V, mode, float(temperature), _p(outputs["accept_len"]),
+                             _p(outputs["path"]), _p(outputs["bonus"]), _p(outputs.get("target_argmax")),
+                             _p(workspace), ws_bytes), "tv_accept")
     return outputs
 
 
@@ -224,22 +315,33 @@ def tv_commit(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Te
 
     Returns dict(new_prefix_lens [B], emitted [B][N] (if wanted), next_root [B]);
     outputs must not overlap any input."""
+    dev = _device_of(k_pages, "k_pages")
+    if k_pages.dim() != 4 or not isinstance(draft_tokens, torch.Tensor) or draft_tokens.dim() != 2:
+        raise ValueError("k_pages must be [P][Hkv][16][D] and draft_tokens [B][N]")
     B, N = draft_tokens.shape
-    P, Hkv, page, D = k_pages.shape
-    assert page == 16 and v_pages.shape == k_pages.shape
-    assert k_pages.dtype == torch.bfloat16 and v_pages.dtype == torch.bfloat16
-    for t in (page_table, prefix_lens, draft_tokens, path, accept_len, bonus):
-        assert t.dtype == torch.int32
-    dev = k_pages.device
+    P, Hkv, D = k_pages.shape[0], k_pages.shape[1], k_pages.shape[3]
+    _arg(k_pages, "k_pages", torch.bfloat16, (P, Hkv, 16, D), dev)
+    _arg(v_pages, "v_pages", torch.bfloat16, (P, Hkv, 16, D), dev)
+    _arg(page_table, "page_table", torch.int32, (None, None), dev)
+    if page_table.shape[0] < B:  # rows past B (a larger table) are never read
+        raise ValueError(f"page_table has {page_table.shape[0]} rows, fewer than the batch's {B}")
+    _arg(prefix_lens, "prefix_lens", torch.int32, (B,), dev)
+    _arg(draft_tokens, "draft_tokens", torch.int32, (B, N), dev)
+    _arg(path, "path", torch.int32, (B, N), dev)
+    _arg(accept_len, "accept_len", torch.int32, (B,), dev)
+    _arg(bonus, "bonus", torch.int32, (B,), dev)
     if outputs is None:
         outputs = dict(new_prefix_lens=torch.empty(B, dtype=torch.int32, device=dev),
                        next_root=torch.empty(B, dtype=torch.int32, device=dev))
         if want_emitted:
             outputs["emitted"] = torch.empty((B, N), dtype=torch.int32, device=dev)
-    _check(_load().tv_commit(_ctx(dev), _ptr(k_pages), _ptr(v_pages), P, _ptr(page_table), page_table.shape[1],
-                             _ptr(prefix_lens), int(max_prefix_len), _ptr(draft_tokens), _ptr(path),
-                             _ptr(accept_len), _ptr(bonus), B, N, Hkv, D, _ptr(outputs["new_prefix_lens"]),
-                             _ptr(outputs.get("emitted")), _ptr(outputs["next_root"])), "tv_commit")
+    _arg(outputs.get("new_prefix_lens"), "outputs['new_prefix_lens']", torch.int32, (B,), dev)
+    _arg(outputs.get("next_root"), "outputs['next_root']", torch.int32, (B,), dev)
+    _arg(outputs.get("emitted"), "outputs['emitted']", torch.int32, (B, N), dev, optional=True)
+    _check(_load().tv_commit(_ctx(dev), _p(k_pages), _p(v_pages), P, _p(page_table), page_table.shape[1],
+                             _p(prefix_lens), int(max_prefix_len), _p(draft_tokens), _p(path),
+                             _p(accept_len), _p(bonus), B, N, Hkv, D, _p(outputs["new_prefix_lens"]),
+                             _p(outputs.get("emitted")), _p(outputs["next_root"])), "tv_commit")
     return outputs
 
 
