@@ -531,6 +531,41 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     }
   };
 
+  // Writes this wavefront's rows: the outputs (one split) or the split's
+  // partial (o, m, l). With `nan` the outputs, or the partial's m, are NaN:
+  // the workgroup met bad data. Every lane of the wavefront takes part (the
+  // row sum's half swap).
+  auto emit = [&](bool nan) __attribute__((always_inline)) {
+    const float l_tot = swap_halves_sum(l);
+    if (!row_ok) return;
+    if (a.S == 1) {
+      const int64_t base = ((static_cast<int64_t>(b) * a.N + node) * a.Hq + head) * D;
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = nan ? NAN : o[db][4 * i + j] * inv;
+          store_out(a, base, db * 32 + 8 * i + 4 * h, v4);
+        }
+    } else {
+      const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4 *>(a.ws_o + slot * D + db * 32 + 8 * i + 4 * h) =
+              make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
+      if (h == 0) {
+        a.ws_ml[slot * 2] = nan ? NAN : m_ref;
+        a.ws_ml[slot * 2 + 1] = l_tot;
+      }
+    }
+  };
+  bool emitted = false, emitted_nan = false;
+
   if constexpr (KSPLIT) {
     // Key split (row groups of at most 32 rows): wavefront w takes tiles
     // w, w + 2, w + 4, ... of the split with its own running max, sum and O,
@@ -620,6 +655,14 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     if (!first) wait_for(k + 1);
     barrier_only();
   }
+  // The first half ran its last products one half-step before the second
+  // half: it writes its rows while the second half finishes. If another
+  // wavefront turns out to have met bad data, the rows are marked again below.
+  if (first && wave_active) {
+    emitted_nan = bad_len || load_bad;
+    emit(emitted_nan);
+    emitted = true;
+  }
   if (first) barrier_only();
   }
   if (load_bad) s_bad = 1;
@@ -654,34 +697,7 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     }
   }
   if (!wave_active) return;
-
-  const float l_tot = swap_halves_sum(l);
-  if (!row_ok) return;
-  if (a.S == 1) {
-    const int64_t base = ((static_cast<int64_t>(b) * a.N + node) * a.Hq + head) * D;
-    const float inv = 1.f / l_tot;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = bad ? NAN : o[db][4 * i + j] * inv;
-        store_out(a, base, db * 32 + 8 * i + 4 * h, v4);
-      }
-  } else {
-    const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float4 *>(a.ws_o + slot * D + db * 32 + 8 * i + 4 * h) =
-            make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
-    if (h == 0) {
-      a.ws_ml[slot * 2] = bad ? NAN : m_ref;
-      a.ws_ml[slot * 2 + 1] = l_tot;
-    }
-  }
+  if (!emitted || (bad && !emitted_nan)) emit(bad);
 }
 
 // Merges the S partial (m, l, o) triples of each row in a fixed split order.
