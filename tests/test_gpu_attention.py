@@ -244,3 +244,28 @@ def test_binding_checks_arguments():
     with pytest.raises(ValueError):
         tv.tv_build_mask(dw.parents, mask=torch.zeros((w.B, w.N, 2), dtype=torch.int64, device=DEV))
     assert tv.tv_device_error(DEV) == 0
+
+
+@pytest.mark.parametrize("L,slot", [((38, 40), 1), ((38, 40), 2), ((70, 90), 1), ((70, 90), 2)],
+                         ids=["one-split-first-half", "one-split-second-half", "split-first-half",
+                              "split-second-half"])
+def test_bad_page_seen_by_either_half(L, slot):
+    # a bad page id is found by the wavefronts whose share of the tile it
+    # falls in: page slot 1 of a tile by the first half of the workgroup,
+    # slot 2 by the second. The first half writes its rows before the final
+    # barrier, so a bad page found by the second half must still turn every
+    # row of the sequence into NaN, for one key split (outputs written
+    # directly) and for several (partials merged afterwards)
+    w = small("random", N=10, L=L, B=2)
+    bad = w.page_table.copy()
+    bad[1, slot] = w.num_pages + 5
+    st, _ = oracle.status_attention(w.q, w.k_pages, w.v_pages, bad, w.prefix_lens, None, B=w.B, N=w.N, Hq=w.Hq,
+                                    Hkv=w.Hkv, D=w.D, sm_scale=w.sm_scale)
+    assert st == oracle.INVALID_ARG
+    dw = DevWorkload(w, logits=False)
+    dw.page_table = dev(bad)
+    print(f"[attention] bad page slot {slot}, prefix lengths {w.prefix_lens.tolist()}", flush=True)
+    out = host(dw.attention(None))
+    assert tv.tv_device_error(DEV) == oracle.INVALID_ARG
+    assert np.isnan(out[1]).all()
+    assert np.isfinite(out[0]).all()
