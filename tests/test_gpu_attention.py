@@ -246,17 +246,19 @@ def test_binding_checks_arguments():
     assert tv.tv_device_error(DEV) == 0
 
 
-@pytest.mark.parametrize("L,slot", [((38, 40), 1), ((38, 40), 2), ((70, 90), 1), ((70, 90), 2)],
+@pytest.mark.parametrize("N,L,slot", [(10, (38, 40), 1), (10, (38, 40), 2), (10, (70, 90), 1), (10, (70, 90), 2),
+                                       (40, (10, 20), 2), (40, (150, 200), 2)],
                          ids=["one-split-first-half", "one-split-second-half", "split-first-half",
-                              "split-second-half"])
-def test_bad_page_seen_by_either_half(L, slot):
+                              "split-second-half", "8-waves-one-split-second-half", "8-waves-split-second-half"])
+def test_bad_page_seen_by_either_half(N, L, slot):
     # a bad page id is found by the wavefronts whose share of the tile it
     # falls in: page slot 1 of a tile by the first half of the workgroup,
     # slot 2 by the second. The first half writes its rows before the final
     # barrier, so a bad page found by the second half must still turn every
     # row of the sequence into NaN, for one key split (outputs written
-    # directly) and for several (partials merged afterwards)
-    w = small("random", N=10, L=L, B=2)
+    # directly) and for several (partials merged afterwards), with two
+    # wavefronts per workgroup (40 rows) and with eight (160 rows)
+    w = small("random", N=N, L=L, B=2)
     bad = w.page_table.copy()
     bad[1, slot] = w.num_pages + 5
     st, _ = oracle.status_attention(w.q, w.k_pages, w.v_pages, bad, w.prefix_lens, None, B=w.B, N=w.N, Hq=w.Hq,
