@@ -5,11 +5,17 @@ One step = one verification pass over one batch: tv_build_mask, tv_attention
 workload). Inputs are seeded synthetic tensors of the workload's shapes,
 resident in HBM before timing starts. Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--calls 200]
 
---config picks the workload (1..5, default 2: the Llama-3-8B layer shape with
-an EAGLE-2 64-node tree); --accept stochastic runs a greedy workload's tree
-with sampled acceptance instead. Only one GPU is supported.
+The headline workload is --config 4 (32K-token context, B4, 32/8 heads, D128,
+64-node dynamic trees). `value` is verified tree tokens per second of one
+attention layer: B*N over the mean tv_attention duration, from a block of
+--calls back-to-back calls timed with HIP events on the launch stream. The
+K whole steps are timed as well (ms_per_step, step_tokens_per_s). The other
+workloads (--extra-configs) are measured the same way afterwards and reported
+under "other_configs", each with its own roofline (MFMA-bound above the bf16
+ridge point, HBM-bound below it). --accept stochastic runs a greedy workload's
+tree with sampled acceptance instead. Only one GPU is supported.
 """
 from __future__ import annotations
 
@@ -33,7 +39,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--calls", type=int, default=200,
+                    help="back-to-back calls per timed block of each kernel call (at least 100)")
+    ap.add_argument("--extra-configs", default="1,2,3,5",
+                    help="other workloads measured after the headline one and reported as extra keys "
+                         "(comma-separated config numbers; empty for none)")
     ap.add_argument("--accept", default="default", choices=["default", "stochastic"],
                     help="stochastic: run the workload's tree with sampled acceptance (T = 1, draft rows and "
                          "uniforms from the same seeded streams, each node's token drawn from its draft row)")
@@ -43,8 +54,8 @@ def parse():
                     help="give each sequence a seeded node count in [N/2, N] (tree_sizes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
-                    help="stop after the timed steps (no mask-cost, decode, cold-cache, builder or commit timings), "
-                         "so that a counter run sees the step's kernels only")
+                    help="stop after the timed region (steps and call blocks; no mask-cost, decode, cold-cache, "
+                         "builder, commit or other-workload timings), so that a trace sees the step's kernels only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one device-to-device copy of this many MiB (an HBM counter "
@@ -301,6 +312,185 @@ def commit_timing(tv, torch, dev, w, depth, d, kp, vp, table, plens, tokens, out
     return res
 
 
+RIDGE_FLOP_PER_BYTE = BF16_DENSE_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # 312.5: above it the MFMA peak binds
+
+
+def usable_cores():
+    """Host cores this process may use: its CPU affinity, capped by a cgroup
+    CPU quota and by OMP_NUM_THREADS when either is set (the share a shared
+    host grants one job)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as fh:
+            quota, period = fh.read().split()[:2]
+            if quota != "max":
+                n = min(n, max(1, int(-(-int(quota) // int(period)))))
+    except (OSError, ValueError):
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(n, 1)
+
+
+def block_us(torch, call, n):
+    """Mean device time (us) of `call` over a block of n back-to-back calls,
+    with HIP events recorded on the launch stream around the whole block."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def roofline_entry(name, us, nbytes, flops, traffic=None, kernel=None):
+    """The roofline of one call: HBM when its arithmetic intensity is below
+    the bf16 ridge point, MFMA above it."""
+    if flops and flops / nbytes > RIDGE_FLOP_PER_BYTE:
+        ach = flops / us / 1e6  # TFLOP/s
+        r = {"bound": "mfma", "achieved": ach, "peak": BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+             "frac": ach / BF16_DENSE_TFLOPS, "algorithmic_flops": flops,
+             "hbm_gbs": nbytes / us / 1e3, "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS}
+    else:
+        ach = nbytes / us / 1e3  # GB/s
+        r = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
+        if flops:
+            r["mfma_frac"] = flops / us / 1e6 / BF16_DENSE_TFLOPS
+    r["traffic"] = traffic
+    r["algorithmic_bytes"] = nbytes
+    r["call_us"] = us
+    if kernel:
+        r["kernel"] = kernel
+    return r
+
+
+class Setup:
+    """One workload's inputs and outputs resident on the GPU, and its calls."""
+
+    def __init__(self, torch, tv, cfg, stochastic=False, nodes=0, ragged=False):
+        import tvgen
+
+        self.torch, self.tv, self.cfg = torch, tv, cfg
+        dev = self.dev = torch.device("cuda:0")
+        self.c = c = tvgen.CONFIGS[cfg]
+        over = {}
+        if stochastic:
+            over["mode"] = "stochastic"
+        if nodes:
+            over["N"] = nodes
+        self.w = w = tvgen.make_workload(cfg, overrides=over or None)
+        self.key = str(cfg) + ("-stochastic" if stochastic else "") + (f"-N{nodes}" if nodes else "") + \
+            ("-ragged" if ragged else "")
+        self.depth = np.stack([tvgen.tree_depths(p) for p in w.parents])
+        self.sizes = None
+        if ragged:
+            st = tvgen.Stream(w.seed, 41)
+            self.sizes = np.array([w.N - w.N // 2 + st.randint(w.N // 2 + 1) for _ in range(w.B)], np.int32)
+        self.n_present = present(w, self.sizes)
+        self.tokens = int(self.n_present.sum())
+        d = self.d
+        self.parents, self.tokens_d = d(w.parents), d(w.draft_tokens)
+        self.q, self.kp, self.vp = d(w.q, torch.bfloat16), d(w.k_pages, torch.bfloat16), d(w.v_pages, torch.bfloat16)
+        self.table, self.plens = d(w.page_table), d(w.prefix_lens)
+        self.tl = d(w.target_logits)
+        self.dl = d(w.draft_logits) if w.draft_logits is not None else None
+        self.un = d(w.uniforms) if w.uniforms is not None else None
+        self.mode = tv.GREEDY if w.mode == "greedy" else tv.STOCHASTIC
+        self.mask = torch.empty((w.B, w.N, (w.N + 63) // 64), dtype=torch.int64, device=dev)
+        self.ts = d(self.sizes) if self.sizes is not None else None
+        self.dep = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
+        self.out = torch.empty((w.B, w.N, w.Hq, w.D), dtype=torch.float32, device=dev)
+        aws = tv.tv_attention_workspace_bytes(dev, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
+        self.attn_ws = torch.empty(max(aws, 1), dtype=torch.uint8, device=dev)
+        self.acc_ws = torch.empty(max(tv.tv_accept_workspace_bytes(w.B, w.N, w.V, self.mode), 1), dtype=torch.uint8,
+                                  device=dev)
+        self.outs = dict(accept_len=torch.empty(w.B, dtype=torch.int32, device=dev),
+                         path=torch.empty((w.B, w.N), dtype=torch.int32, device=dev),
+                         bonus=torch.empty(w.B, dtype=torch.int32, device=dev))
+        self.a_bytes = attention_bytes(w, self.sizes)
+        self.a_flops = attention_flops(w, self.depth, self.sizes)
+        self.c_bytes = accept_bytes(w, self.sizes)
+        tv.tv_build_mask(self.parents, self.mask, self.dep, tree_sizes=self.ts)
+
+    def d(self, a, dtype=None):
+        t = self.torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(dtype) if dtype is not None else t).to(self.dev)
+
+    def build_mask(self):
+        self.tv.tv_build_mask(self.parents, self.mask, self.dep, tree_sizes=self.ts)
+
+    def attention(self, mask="tree"):
+        w = self.w
+        self.tv.tv_attention(self.q, self.kp, self.vp, self.table, self.plens, w.max_prefix_len,
+                             self.mask if mask == "tree" else None, float(w.sm_scale), out=self.out,
+                             workspace=self.attn_ws, tree_sizes=self.ts)
+
+    def accept(self):
+        w = self.w
+        self.tv.tv_accept(self.tl, self.tokens_d, self.parents, mode=self.mode, draft_logits=self.dl,
+                          uniforms=self.un, temperature=w.temperature, outputs=self.outs, workspace=self.acc_ws,
+                          tree_sizes=self.ts)
+
+    def step(self):
+        self.build_mask()
+        self.attention()
+        self.accept()
+
+    def name(self):
+        return workload_name(self.w, self.c, self.sizes)
+
+    def calls(self, n):
+        """tv_attention, tv_accept and tv_build_mask, each timed over a block
+        of n back-to-back calls."""
+        torch = self.torch
+        for _ in range(3):
+            self.step()
+        t_attn = block_us(torch, self.attention, n)
+        t_acc = block_us(torch, self.accept, n)
+        t_mask = block_us(torch, self.build_mask, n)
+        return t_attn, t_acc, t_mask
+
+    def mask_cost(self):
+        """tv_attention with the tree mask against the same call with
+        tree_mask = NULL (every tree key visible), interleaved in blocks of 20
+        calls so that clock drift affects both alike; medians of 5 blocks."""
+        masked, unmasked = [], []
+        for _ in range(5):
+            masked.append(block_us(self.torch, lambda: self.attention("tree"), 20))
+            unmasked.append(block_us(self.torch, lambda: self.attention(None), 20))
+        t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
+        return {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
+                "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
+
+
+ATTN_KERNEL = "tv_attention: attn_mfma_kernel (+ attn_combine_kernel when the keys are split)"
+
+
+def extra_config(torch, tv, cfg, n):
+    """Attention and acceptance of another workload, as extra keys of the line."""
+    s = Setup(torch, tv, cfg)
+    t_attn, t_acc, t_mask = s.calls(n)
+    assert tv.tv_device_error(s.dev) == 0
+    res = {"workload": s.name(), "tree_tokens": s.tokens,
+           "tokens_per_s": s.tokens / t_attn * 1e6,
+           "roofline": roofline_entry("tv_attention", t_attn, s.a_bytes, s.a_flops,
+                                      measured_traffic("tv_attention", s.key), ATTN_KERNEL),
+           "tv_accept": {"avg_us": t_acc, "bytes": s.c_bytes, "gbs": s.c_bytes / t_acc / 1e3,
+                         "hbm_frac": s.c_bytes / t_acc / 1e3 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("tv_accept", s.key)},
+           "tv_build_mask_us": t_mask,
+           "mask_overhead": s.mask_cost(),
+           "calls_per_block": n}
+    if cfg == 1:
+        res["note"] = "launch-bound: 60 KB per call"
+    del s
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -310,114 +500,55 @@ def main():
 
     import torch
 
-    import tvgen
     import tree_verify_attention_attn_amd as tv
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    c = tvgen.CONFIGS[args.config]
-    stochastic = args.accept == "stochastic" and c["mode"] != "stochastic"
-    over = {}
-    if stochastic:
-        over["mode"] = "stochastic"
-    if args.nodes:
-        if not 1 <= args.nodes <= 128:
-            sys.exit("--nodes takes 1..128")
-        over["N"] = args.nodes
-    w = tvgen.make_workload(args.config, overrides=over or None)
-    key = str(args.config) + ("-stochastic" if stochastic else "") + (f"-N{args.nodes}" if args.nodes else "") + \
-        ("-ragged" if args.ragged else "")
-    depth = np.stack([tvgen.tree_depths(p) for p in w.parents])
-    sizes = None
-    if args.ragged:
-        st = tvgen.Stream(w.seed, 41)
-        sizes = np.array([w.N - w.N // 2 + st.randint(w.N // 2 + 1) for _ in range(w.B)], np.int32)
-    n_present = present(w, sizes)
-
-    def d(a, dtype=None):
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        return (t.view(dtype) if dtype is not None else t).to(dev)
-
-    parents, tokens_d = d(w.parents), d(w.draft_tokens)
-    q, kp, vp = d(w.q, torch.bfloat16), d(w.k_pages, torch.bfloat16), d(w.v_pages, torch.bfloat16)
-    table, plens = d(w.page_table), d(w.prefix_lens)
-    tl = d(w.target_logits)
-    dl = d(w.draft_logits) if w.draft_logits is not None else None
-    un = d(w.uniforms) if w.uniforms is not None else None
-    mode = tv.GREEDY if w.mode == "greedy" else tv.STOCHASTIC
-    mask = torch.empty((w.B, w.N, (w.N + 63) // 64), dtype=torch.int64, device=dev)
-    ts = d(sizes) if sizes is not None else None
-    dep = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
-    out = torch.empty((w.B, w.N, w.Hq, w.D), dtype=torch.float32, device=dev)
-    aws = tv.tv_attention_workspace_bytes(dev, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
-    attn_ws = torch.empty(max(aws, 1), dtype=torch.uint8, device=dev)
-    acc_ws = torch.empty(max(tv.tv_accept_workspace_bytes(w.B, w.N, w.V, mode), 1), dtype=torch.uint8, device=dev)
-    outs = dict(accept_len=torch.empty(w.B, dtype=torch.int32, device=dev),
-                path=torch.empty((w.B, w.N), dtype=torch.int32, device=dev),
-                bonus=torch.empty(w.B, dtype=torch.int32, device=dev))
-
-    def step(ev=None):
-        if ev:
-            ev[0].record()
-        tv.tv_build_mask(parents, mask, dep, tree_sizes=ts)
-        if ev:
-            ev[1].record()
-        tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, mask, float(w.sm_scale), out=out,
-                        workspace=attn_ws, tree_sizes=ts)
-        if ev:
-            ev[2].record()
-        tv.tv_accept(tl, tokens_d, parents, mode=mode, draft_logits=dl, uniforms=un, temperature=w.temperature,
-                     outputs=outs, workspace=acc_ws, tree_sizes=ts)
-        if ev:
-            ev[3].record()
+    s = Setup(torch, tv, args.config, stochastic=args.accept == "stochastic" and
+              tvgen_mode(args.config) != "stochastic", nodes=args.nodes, ragged=args.ragged)
+    w, dev = s.w, s.dev
+    ncalls = max(args.calls, 100)
 
     for _ in range(args.warmup):
-        step()
+        s.step()
     torch.cuda.synchronize()
     tv.tv_tau_reset(dev)
     if tv.tv_device_error(dev) != 0:
         raise RuntimeError("device error during warm-up")
 
-    # per-call HIP events on every EVENT_EVERY-th step only: each event record
-    # costs the stream a few microseconds, which would otherwise inflate the
-    # step time that `value` is computed from
-    EVENT_EVERY = 8
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(0, args.steps, EVENT_EVERY)]
+    # the timed region: K whole steps (mask, attention, accept), then a block
+    # of back-to-back calls of each kernel call, with HIP events on the launch
+    # stream around each block
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k // EVENT_EVERY] if k % EVENT_EVERY == 0 else None)
+    for _ in range(args.steps):
+        s.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tau, cycles = tv.tv_tau(dev)
+    t_attn, t_acc, t_mask = s.calls(ncalls)
     assert tv.tv_device_error(dev) == 0
 
-    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs]) * 1e-3  # seconds
-    t_mask, t_attn, t_acc = per.mean(0)
     ms_per_step = wall / args.steps * 1e3
-    tokens = int(n_present.sum())
-    a_bytes, a_flops, c_bytes = attention_bytes(w, sizes), attention_flops(w, depth, sizes), accept_bytes(w, sizes)
-    def spread(col):
-        us = per[:, col] * 1e6
-        return dict(median_us=float(np.median(us)), p10_us=float(np.percentile(us, 10)),
-                    p90_us=float(np.percentile(us, 90)), samples=int(len(us)))
-
+    tokens = s.tokens
     kernels = {
-        "tv_build_mask": dict(avg_us=t_mask * 1e6),
-        "tv_attention": dict(avg_us=t_attn * 1e6, bytes=a_bytes, flops=a_flops, gbs=a_bytes / t_attn / 1e9,
-                             hbm_frac=a_bytes / t_attn / 1e9 / HBM_PEAK_GBS,
-                             mfma_frac=a_flops / t_attn / 1e12 / BF16_DENSE_TFLOPS,
-                             tokens_per_s=tokens / t_attn),
-        "tv_accept": dict(avg_us=t_acc * 1e6, bytes=c_bytes, gbs=c_bytes / t_acc / 1e9,
-                          hbm_frac=c_bytes / t_acc / 1e9 / HBM_PEAK_GBS),
+        "tv_build_mask": dict(avg_us=t_mask),
+        "tv_attention": dict(avg_us=t_attn, bytes=s.a_bytes, flops=s.a_flops, gbs=s.a_bytes / t_attn / 1e3,
+                             hbm_frac=s.a_bytes / t_attn / 1e3 / HBM_PEAK_GBS,
+                             mfma_frac=s.a_flops / t_attn / 1e6 / BF16_DENSE_TFLOPS,
+                             tokens_per_s=tokens / t_attn * 1e6),
+        "tv_accept": dict(avg_us=t_acc, bytes=s.c_bytes, gbs=s.c_bytes / t_acc / 1e3,
+                          hbm_frac=s.c_bytes / t_acc / 1e3 / HBM_PEAK_GBS,
+                          traffic=measured_traffic("tv_accept", s.key)),
+        "calls_per_block": ncalls,
     }
-    for col, name in enumerate(("tv_build_mask", "tv_attention", "tv_accept")):
-        kernels[name].update(spread(col))
-    dom = "tv_attention" if t_attn >= t_acc else "tv_accept"
-    dk = kernels[dom]
+    roof = roofline_entry("tv_attention", t_attn, s.a_bytes, s.a_flops, measured_traffic("tv_attention", s.key),
+                          ATTN_KERNEL)
+    roof["note"] = ("achieved = algorithmic bytes (or flops) per tv_attention call / its mean duration over a block "
+                    "of back-to-back calls (HIP events on the launch stream around the block); traffic = calibrated "
+                    "rocprofv3 FETCH_SIZE + WRITE_SIZE bytes per call, null when not measured for this source")
     result = {
         "metric": "verified tree tokens/sec per attention layer; achieved HBM GB/s vs peak",
-        "value": tokens * args.steps / wall,
+        "value": tokens / t_attn * 1e6,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -428,17 +559,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload_name(w, c, sizes), "batch": w.B, "tree_nodes": w.N,
+        "config": {"workload": s.name(), "batch": w.B, "tree_nodes": w.N,
                    "tree_tokens_per_step": tokens, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.D, "max_prefix_len": w.max_prefix_len, "vocab": w.V,
                    "accept": w.mode, "page_size": 16, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": f"{dom}: {CALL_KERNELS[dom]}", "achieved": dk["gbs"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["gbs"] / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(dom, key),
-                     "algorithmic_bytes": dk["bytes"],
-                     "note": "achieved = algorithmic bytes per call / mean call duration (HIP events on the "
-                             "launch stream around every 8th timed step); traffic = calibrated rocprofv3 "
-                             "FETCH_SIZE + WRITE_SIZE bytes per call, null when not measured for this source"},
+        "value_note": ("value = B*N tree tokens / mean tv_attention duration (one attention layer) over a block of "
+                       "back-to-back calls; step_tokens_per_s = the same tokens / the whole step (mask + attention + "
+                       "acceptance), from the wall clock around the K timed steps"),
+        "step_tokens_per_s": tokens * args.steps / wall,
+        "roofline": roof,
         "kernels": kernels,
         "tau": tau,
         "tau_cycles": cycles,
@@ -448,42 +577,19 @@ def main():
             copy_for_calibration(torch, dev, args.copy_mib)
         print(json.dumps(result), flush=True)
         return
-    # tree-mask cost: tv_attention with the tree mask against the same call
-    # with tree_mask = NULL (every tree key visible), interleaved in blocks of
-    # 20 calls so that clock drift affects both alike; medians of 5 blocks
-    def attn_block(m):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(20):
-            tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, m, float(w.sm_scale), out=out,
-                            workspace=attn_ws, tree_sizes=ts)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 20 * 1e3
-    masked, unmasked = [], []
-    for _ in range(5):
-        masked.append(attn_block(mask))
-        unmasked.append(attn_block(None))
-    t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
-    result["mask_overhead"] = {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
-                               "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
+    result["mask_overhead"] = s.mask_cost()
     # verify premium: the same call for the root row only (N = 1, a plain
     # decode step) over the same KV, blocks of 20 calls, medians of 5 blocks
-    q1 = q[:, :1].contiguous()
+    q1 = s.q[:, :1].contiguous()
     out1 = torch.empty((w.B, 1, w.Hq, w.D), dtype=torch.float32, device=dev)
     ws1 = torch.empty(max(tv.tv_attention_workspace_bytes(dev, w.B, 1, w.Hq, w.Hkv, w.D, w.max_prefix_len), 1),
                       dtype=torch.uint8, device=dev)
 
-    def decode_block():
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(20):
-            tv.tv_attention(q1, kp, vp, table, plens, w.max_prefix_len, None, float(w.sm_scale), out=out1,
-                            workspace=ws1)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 20 * 1e3
-    t_dec = float(np.median([decode_block() for _ in range(5)]))
+    def decode():
+        tv.tv_attention(q1, s.kp, s.vp, s.table, s.plens, w.max_prefix_len, None, float(w.sm_scale), out=out1,
+                        workspace=ws1)
+    t_dec = float(np.median([block_us(torch, decode, 20) for _ in range(5)]))
+    t_m = result["mask_overhead"]["masked_us"]
     result["verify_premium"] = {"decode_us": t_dec, "verify_us": t_m, "premium": t_m / t_dec,
                                 "tree_tokens_per_decode_token": tokens / w.B,
                                 "note": "tv_attention over the same KV for the root row only (N = 1, no mask) "
@@ -506,13 +612,9 @@ def main():
         return dict(median_us=med, p10_us=float(np.percentile(ts_, 10)), p90_us=float(np.percentile(ts_, 90)),
                     gbs=nbytes / med / 1e3, hbm_frac=nbytes / med / 1e3 / HBM_PEAK_GBS)
     result["cold_cache"] = {
-        "tv_attention": cold(lambda: tv.tv_attention(q, kp, vp, table, plens, w.max_prefix_len, mask,
-                                                     float(w.sm_scale), out=out, workspace=attn_ws,
-                                                     tree_sizes=ts), a_bytes),
-        "tv_accept": cold(lambda: tv.tv_accept(tl, tokens_d, parents, mode=mode, draft_logits=dl, uniforms=un,
-                                               temperature=w.temperature, outputs=outs, workspace=acc_ws,
-                                               tree_sizes=ts), c_bytes),
-        "note": "one call after writing a 1 GiB buffer (L2 and MALL evicted); the step figures above are warm"}
+        "tv_attention": cold(s.attention, s.a_bytes),
+        "tv_accept": cold(s.accept, s.c_bytes),
+        "note": "one call after writing a 1 GiB buffer (L2 and MALL evicted); the block figures above are warm"}
     # a measured stream copy on this machine: 1 GiB device to device (2 GiB moved),
     # median of 5; the kernels' bandwidth is also reported as a fraction of it
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
@@ -530,21 +632,34 @@ def main():
                              "tv_accept_frac_of_copy": kernels["tv_accept"]["gbs"] / copy_gbs,
                              "note": "1 GiB device-to-device copy (read + write), median of 5 after one warm-up"}
     del flush, src
-    if c["tree"] == "dynamic" and sizes is None:
-        result["build_tree"] = build_tree_timing(tv, torch, d, w, c)
-    depth_present = np.where(np.arange(w.N)[None, :] < n_present[:, None], depth, -1)
-    result["commit"] = commit_timing(tv, torch, dev, w, depth_present, d, kp, vp, table, plens, d(w.draft_tokens),
-                                     outs)
+    if s.c["tree"] == "dynamic" and s.sizes is None:
+        result["build_tree"] = build_tree_timing(tv, torch, s.d, w, s.c)
+    depth_present = np.where(np.arange(w.N)[None, :] < s.n_present[:, None], s.depth, -1)
+    result["commit"] = commit_timing(tv, torch, dev, w, depth_present, s.d, s.kp, s.vp, s.table, s.plens,
+                                     s.d(w.draft_tokens), s.outs)
     if args.copy_mib > 0:
         copy_for_calibration(torch, dev, args.copy_mib)
+    # the other workloads: attention and acceptance of each, as extra keys
+    extras = [int(x) for x in args.extra_configs.split(",") if x.strip()] if args.extra_configs else []
+    extras = [x for x in extras if x != args.config]
+    depth, sizes = s.depth, s.sizes  # host arrays, kept for the CPU baseline
+    if extras:
+        del s
+        torch.cuda.empty_cache()
+        result["other_configs"] = {f"cfg{x}": extra_config(torch, tv, x, ncalls) for x in extras}
     if not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
+        threads = usable_cores()
         result["cpu_baseline"] = cpu_baseline(w, depth, args.cpu_seconds, threads, sizes)
         result["cpu_baseline"]["cpu_model"] = cpu_model()
         if args.config in (1, 2):  # the single-thread figure on the two small workloads
             one = cpu_baseline(w, depth, min(args.cpu_seconds, 5.0), 1, sizes)
             result["cpu_baseline"]["one_thread"] = {"value": one["value"], "sample": one["sample"]}
     print(json.dumps(result), flush=True)
+
+
+def tvgen_mode(cfg):
+    import tvgen
+    return tvgen.CONFIGS[cfg]["mode"]
 
 
 if __name__ == "__main__":

@@ -14,6 +14,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# an alternative build (the sanitizer test loads ASan/UBSan builds this way)
+_LIB_OVERRIDE = os.environ.get("TVO_LIB")
 _lib = None
 
 OK, INVALID_ARG, INVALID_TREE, UNSUPPORTED, WORKSPACE, RUNTIME = range(6)
@@ -39,7 +41,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(_LIB_OVERRIDE or _LIB_PATH)
         vp, i32, i64, f32, c_int = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int
         lib.tvo_build_mask.argtypes = [vp, vp, i32, i32, vp, vp]
         lib.tvo_attention.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp,

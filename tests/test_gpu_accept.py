@@ -212,10 +212,13 @@ def test_stochastic_variants(variant):
     got = dw.accept(tv.STOCHASTIC)
     assert tv.tv_device_error(DEV) == 0
     ref = oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms, T)
-    near = (ref["margins"] <= 1e-9).any(1)
+    m = ref["margins"]
+    print(f"[accept] variant {variant}: min decision margin {np.nanmin(m):.3e}", flush=True)
+    # every decision of the seeded inputs is far from a coin flip, so any
+    # difference is a bug, not rounding
+    assert (m > 1e-9).all(), variant
     for k in ("accept_len", "path", "bonus"):
-        g = host(got[k])
-        assert (g[~near] == ref[k][~near]).all(), k
+        assert (host(got[k]) == ref[k]).all(), k
     if variant == "p-equals-q":
         assert (ref["accept_len"] == w.N).all()
 
@@ -230,10 +233,12 @@ def stochastic_compare(w, what, T=None):
     near = (m <= 1e-9).any(1)
     print(f"[accept] {what}: B={w.B} N={w.N} V={w.V} min margin {m.min():.3e}, near-tie sequences "
           f"{int(near.sum())}, accept_len histogram {np.bincount(ref['accept_len']).tolist()}", flush=True)
-    assert near.mean() < 0.05, what
+    # every decision of the seeded inputs is far from a coin flip, so any
+    # difference is a bug, not rounding
+    assert int(near.sum()) == 0, f"{what}: sequences with a decision margin <= 1e-9: {np.argwhere(near)[:5, 0]}"
     for k in ("accept_len", "path", "bonus"):
         g = host(got[k])
-        bad = np.argwhere((g != ref[k]).reshape(w.B, -1).any(1) & ~near)
+        bad = np.argwhere((g != ref[k]).reshape(w.B, -1).any(1))
         assert bad.size == 0, f"{what}: {k} differs for sequences {bad[:5, 0].tolist()}"
     return ref
 

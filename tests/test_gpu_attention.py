@@ -271,3 +271,56 @@ def test_bad_page_seen_by_either_half(N, L, slot):
     assert tv.tv_device_error(DEV) == oracle.INVALID_ARG
     assert np.isnan(out[1]).all()
     assert np.isfinite(out[0]).all()
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_full_size_one_whole_unit(cfg):
+    # every row of one whole (sequence, KV head) unit - all N nodes x G query
+    # heads - of the full-size workload, in the launch configuration the
+    # bench times (the last sequence and KV head, so a unit the sampled test
+    # rarely reaches)
+    w = tvgen.make_workload(cfg, with_logits=False)
+    G = w.Hq // w.Hkv
+    b, g = w.B - 1, w.Hkv - 1
+    rows = np.array([[b, i, h] for i in range(w.N) for h in range(g * G, (g + 1) * G)], np.int32)
+    print(f"[attn] cfg{cfg} full size, whole unit b={b} g={g}: {len(rows)} rows", flush=True)
+    dw = DevWorkload(w, logits=False)
+    mask = tv.tv_build_mask(dw.parents)[0]
+    out = host(dw.attention(mask))
+    assert tv.tv_device_error(DEV) == 0
+    ref = oracle.attention(w, oracle.build_mask(w.parents)[0], rows=rows)
+    got = out[rows[:, 0], rows[:, 1], rows[:, 2]]
+    check_attention(got, ref, tight=TIGHT, what=f"cfg{cfg} unit ({b}, {g})")
+
+
+@pytest.mark.parametrize("case", ["key-split-one-split", "key-split-last-split", "negative-id", "last-split"])
+def test_bad_page_variants(case):
+    # a bad page id turns every row of its sequence into NaN and reports
+    # INVALID_ARG: in the key-split template (at most 32 rows per KV head:
+    # the two wavefronts merge through LDS after the bad page is seen), with
+    # one key split and with the bad page in the last of several splits; a
+    # negative id (-1) inside the sequence's pages; and a bad page in the last
+    # split of the ping-pong template
+    if case.startswith("key-split"):
+        L = (38, 40) if case == "key-split-one-split" else (900, 1000)
+        w = small("random", N=5, Hq=4, Hkv=1, L=L, B=2)
+    elif case == "negative-id":
+        w = small("random", N=10, L=(150, 200), B=2)
+    else:
+        w = small("random", N=40, L=(900, 1000), B=2)
+    bad = w.page_table.copy()
+    last = (int(w.prefix_lens[1]) + w.N - 1) // 16
+    slot = {"key-split-one-split": 1, "key-split-last-split": last, "negative-id": 2, "last-split": last}[case]
+    bad[1, slot] = -1 if case == "negative-id" else w.num_pages + 7
+    st, _ = oracle.status_attention(w.q, w.k_pages, w.v_pages, bad, w.prefix_lens, None, B=w.B, N=w.N, Hq=w.Hq,
+                                    Hkv=w.Hkv, D=w.D, sm_scale=w.sm_scale)
+    assert st == oracle.INVALID_ARG
+    plan_ws = tv.tv_attention_workspace_bytes(DEV, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
+    print(f"[attention] bad page case {case}: slot {slot} of {last + 1}, prefix lengths {w.prefix_lens.tolist()}, "
+          f"rows per KV head {w.N * w.Hq // w.Hkv}, workspace {plan_ws} B", flush=True)
+    dw = DevWorkload(w, logits=False)
+    dw.page_table = dev(bad)
+    out = host(dw.attention(None))
+    assert tv.tv_device_error(DEV) == oracle.INVALID_ARG
+    assert np.isnan(out[1]).all()
+    assert np.isfinite(out[0]).all()

@@ -9,6 +9,7 @@ not built, or no GPU is present, calls fail loudly.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from typing import Optional
@@ -75,6 +76,19 @@ def _load():
     return _lib
 
 
+def _teardown():
+    """Destroys every context at interpreter exit, while the HIP runtime is
+    still fully alive: each context's stream is synchronised, then its device
+    counters and event are released by tv_destroy. Without it they are left
+    to the runtime's own exit-time destructors."""
+    if _lib is None:
+        return
+    for idx, h in list(_ctxs.items()):
+        _lib.tv_destroy(h)
+    _ctxs.clear()
+    _bound.clear()
+
+
 def library() -> ctypes.CDLL:
     """The loaded libtreeverify (raises if it is not built)."""
     return _load()
@@ -92,6 +106,8 @@ def _ctx(device: torch.device):
         s = lib.tv_create(ctypes.byref(h), idx, ctypes.c_void_p(st0))
         if s != OK:
             raise TVError(s, "tv_create")
+        if not _ctxs:
+            atexit.register(_teardown)
         _ctxs[idx] = h
         _bound[idx] = st0
     h = _ctxs[idx]

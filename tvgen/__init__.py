@@ -30,6 +30,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtvgen.so")
+# an alternative build (the sanitizer test loads ASan/UBSan builds this way)
+_LIB_OVERRIDE = os.environ.get("TVG_LIB")
 _lib = None
 
 # tensor ids: each tensor of a workload draws from its own stream
@@ -61,7 +63,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(_LIB_OVERRIDE or _LIB_PATH)
         u64, i64, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
         lib.tvg_key.restype = u64
         lib.tvg_key.argtypes = [u64, u64]
