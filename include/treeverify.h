@@ -175,6 +175,27 @@ tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const vo
                        int32_t Hkv, int32_t D, float sm_scale, void *out, tv_dtype out_dtype, void *workspace,
                        size_t workspace_bytes);
 
+/* tv_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (minus the workspace), checks, plan, kernels and results
+ * as tv_attention; the plan's split partials or unit order go to a scratch
+ * array that the library holds on each device it runs on, from set-up
+ * (tv_create) until the process ends: TV_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * device. Allocates nothing itself (no hipMalloc, hipFree or allocating
+ * library call); the caller still passes q, the pools, the tables and out.
+ * Returns TV_ERR_WORKSPACE, launching nothing, when the plan needs more
+ * scratch than that (tv_attention_workspace_bytes(...) tells how much).
+ * Every call on one device shares the array, which keeps the last call's
+ * contents; nothing in it needs clearing. Calls that overlap on one device
+ * (concurrent streams, or two contexts) race on the array: order them on
+ * one stream. */
+#define TV_NOALLOC_SCRATCH_BYTES (64ull << 20)
+tv_status tv_attention_noalloc(tv_ctx *ctx, const void *q, const void *k_pages, const void *v_pages,
+                               int64_t num_pages, const int32_t *page_table, int32_t maxp,
+                               const int32_t *prefix_lens, int32_t max_prefix_len, const uint64_t *tree_mask,
+                               const int32_t *tree_sizes, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                               float sm_scale, void *out, tv_dtype out_dtype);
+
 /* Workspace (bytes) tv_accept needs: per-row partial vocab reductions, and
  * in stochastic mode two residual rows of V doubles per sequence. */
 size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode mode);

@@ -56,6 +56,8 @@ def _load():
         lib.tv_attention_workspace_bytes.restype = sz
         lib.tv_attention.argtypes = [vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, f32,
                                      vp, ctypes.c_int, vp, sz]
+        lib.tv_attention_noalloc.argtypes = [vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                             f32, vp, ctypes.c_int]
         lib.tv_accept_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
         lib.tv_accept_workspace_bytes.restype = sz
         lib.tv_accept.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, f32, vp, vp, vp, vp, vp,
@@ -69,7 +71,8 @@ def _load():
         lib.tv_status_string.restype = ctypes.c_char_p
         lib.tv_tree_budget.argtypes = [i32, i32]
         lib.tv_tree_budget.restype = i32
-        for f in ("tv_create", "tv_destroy", "tv_set_stream", "tv_build_mask", "tv_attention", "tv_accept",
+        for f in ("tv_create", "tv_destroy", "tv_set_stream", "tv_build_mask", "tv_attention", "tv_attention_noalloc",
+                  "tv_accept",
                   "tv_commit", "tv_build_tree", "tv_tau", "tv_tau_reset", "tv_device_error"):
             getattr(lib, f).restype = st
         _lib = lib
@@ -276,6 +279,38 @@ def tv_attention(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
                                 _p(prefix_lens), int(max_prefix_len), _p(tree_mask), _p(tree_sizes), B, N,
                                 Hq, Hkv, D,
                                 float(sm_scale), _p(out), odt, _p(workspace), ws_bytes), "tv_attention")
+    return out
+
+
+def tv_attention_noalloc(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
+                         prefix_lens: torch.Tensor, max_prefix_len: int, tree_mask: Optional[torch.Tensor],
+                         sm_scale: float, out: torch.Tensor, tree_sizes: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """tv_attention without a workspace and without any allocation: the
+    library's per-device scratch (TV_NOALLOC_SCRATCH_BYTES) holds the plan's
+    partials. `out` must be given. Calls that overlap on one GPU race on the
+    scratch."""
+    dev = _device_of(q, "q")
+    if q.dim() != 4 or not isinstance(k_pages, torch.Tensor) or k_pages.dim() != 4:
+        raise ValueError("q must be [B][N][Hq][D] and k_pages [P][Hkv][16][D]")
+    B, N, Hq, D = q.shape
+    P, Hkv = k_pages.shape[0], k_pages.shape[1]
+    _arg(q, "q", torch.bfloat16, (B, N, Hq, D), dev)
+    _arg(k_pages, "k_pages", torch.bfloat16, (P, Hkv, 16, D), dev)
+    _arg(v_pages, "v_pages", torch.bfloat16, (P, Hkv, 16, D), dev)
+    _arg(page_table, "page_table", torch.int32, (None, None), dev)
+    if page_table.shape[0] < B:
+        raise ValueError(f"page_table has {page_table.shape[0]} rows, fewer than the batch's {B}")
+    _arg(prefix_lens, "prefix_lens", torch.int32, (B,), dev)
+    _arg(tree_mask, "tree_mask", torch.int64, (B, N, max((N + 63) // 64, 1)), dev, optional=True)
+    _arg(tree_sizes, "tree_sizes", torch.int32, (B,), dev, optional=True)
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be a float32 or bfloat16 tensor")
+    _arg(out, "out", out.dtype, (B, N, Hq, D), dev)
+    odt = {torch.float32: F32, torch.bfloat16: BF16}[out.dtype]
+    _check(_load().tv_attention_noalloc(_ctx(dev), _p(q), _p(k_pages), _p(v_pages), P, _p(page_table),
+                                        page_table.shape[1], _p(prefix_lens), int(max_prefix_len), _p(tree_mask),
+                                        _p(tree_sizes), B, N, Hq, Hkv, D, float(sm_scale), _p(out), odt),
+           "tv_attention_noalloc")
     return out
 
 

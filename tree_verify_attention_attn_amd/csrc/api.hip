@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -18,6 +20,33 @@ __global__ void clear_u32_kernel(unsigned int *p, int n) {
 }
 
 }  // namespace
+
+// Scratch of tv_attention_noalloc: split partials or the unit order of the
+// attention plan, for callers that cannot allocate. The array is a device
+// global of the code object, so each GPU holds its own copy at its own
+// address from the module's load until the process ends; host code uses the
+// per-device address that hipGetSymbolAddress returns, never the array's
+// name. Every tv_attention_noalloc call on a device shares it.
+static __device__ __align__(256) unsigned char scratch[TV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // device address of `scratch` on each device, or null
+}  // namespace
+
+// The device address of `scratch` on `device` (which must be current),
+// looked up once per device; null if the lookup fails.
+void *scratch_address(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[device] = p;
+  }
+  return g_scratch[device];
+}
 
 tv_status launch_clear_state(tv_ctx *ctx, int first_word, int n_words) {
   hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0, ctx->stream, ctx->d_state + first_word, n_words);
@@ -52,6 +81,10 @@ tv_status tv_create(tv_ctx **out, int device, void *hip_stream) {
       hipMalloc(reinterpret_cast<void **>(&ctx->d_arrivals), kMaxFusedSeqs * sizeof(unsigned int)) != hipSuccess ||
       hipEventCreateWithFlags(&ctx->rebind_event, hipEventDisableTiming) != hipSuccess)
     return fail();
+  // the no-allocation entry point's scratch on this device (its address is
+  // looked up here, at set-up, with the device current)
+  ctx->scratch = scratch_address(device);
+  if (!ctx->scratch) return fail();
   hipLaunchKernelGGL(clear_u32_kernel, dim3(64), dim3(256), 0, ctx->stream, ctx->d_arrivals, kMaxFusedSeqs);
   if (hipGetLastError() != hipSuccess || launch_clear_state(ctx, 0, 8) != TV_OK ||
       hipStreamSynchronize(ctx->stream) != hipSuccess)
@@ -122,6 +155,24 @@ tv_status tv_attention(tv_ctx *ctx, const void *q, const void *k_pages, const vo
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return TV_ERR_WORKSPACE;
   return launch_attention(ctx, plan, q, k_pages, v_pages, num_pages, page_table, maxp, prefix_lens, max_prefix_len,
                           tree_mask, tree_sizes, B, N, Hq, Hkv, D, sm_scale, out, out_dtype, workspace);
+}
+
+tv_status tv_attention_noalloc(tv_ctx *ctx, const void *q, const void *k_pages, const void *v_pages,
+                               int64_t num_pages, const int32_t *page_table, int32_t maxp,
+                               const int32_t *prefix_lens, int32_t max_prefix_len, const uint64_t *tree_mask,
+                               const int32_t *tree_sizes, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                               float sm_scale, void *out, tv_dtype out_dtype) {
+  if (!ctx || !ctx->scratch) return TV_ERR_INVALID_ARG;
+  if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_prefix_len < 0) return TV_ERR_INVALID_ARG;
+  if (N <= 128 && max_prefix_len <= kMaxPrefix && static_cast<int64_t>(B) * N > 0) {
+    const AttnPlan plan = plan_attention(ctx->cu_count, B, N, Hq, Hkv, D, max_prefix_len);
+    if (plan.ws_bytes > TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_WORKSPACE;
+  }
+  // the same checks, plan and kernels as tv_attention, with the device's
+  // scratch as the workspace
+  return tv_attention(ctx, q, k_pages, v_pages, num_pages, page_table, maxp, prefix_lens, max_prefix_len, tree_mask,
+                      tree_sizes, B, N, Hq, Hkv, D, sm_scale, out, out_dtype, ctx->scratch,
+                      TV_NOALLOC_SCRATCH_BYTES);
 }
 
 size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode mode) {

@@ -21,6 +21,8 @@ struct tv_ctx {
   // recorded on the old stream when the context is rebound, so that calls on
   // the new stream start after the work already queued
   hipEvent_t rebind_event;
+  // device address of tv_attention_noalloc's scratch on this context's device
+  void *scratch;
 };
 
 namespace tv {
