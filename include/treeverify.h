@@ -243,7 +243,15 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  * Adds sum(accept_len) and B to the context's tau counters. Requires
  * 1 <= N <= 128 when B > 0, V >= 1, and B * N * ceil(V / 8192) <= 2^24 - 1
  * (one 256-thread workgroup per row and 8192-token chunk on a 1-D grid);
- * larger calls return TV_ERR_UNSUPPORTED. */
+ * larger calls return TV_ERR_UNSUPPORTED.
+ * In STOCHASTIC mode a small batch splits each sequence's vocabulary over
+ * several workgroups that exchange partial sums and wait for each other
+ * (bounded); the grid fits the device when nothing else runs on it. Two
+ * such calls running at the same time on one device (two contexts on
+ * different streams) can each hold part of the device; a workgroup that
+ * waits past the bound marks its sequence -1 (accept_len, bonus, path) and
+ * sets the sticky TV_ERR_HIP. Order concurrent stochastic calls on one
+ * stream. */
 tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_logits, const int32_t *draft_tokens,
                     const int32_t *parents, const int32_t *tree_sizes, const float *uniforms, int32_t B, int32_t N,
                     int32_t V,

@@ -1025,8 +1025,12 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
   auto *sync = reinterpret_cast<unsigned long long *>(wbuf + static_cast<size_t>(B) * 2 * V);
   const double T = static_cast<double>(temperature), invT = 1.0 / T;
   // workgroups per sequence for the path pass: enough to fill the chip when
-  // the batch is small, all co-resident (cooperative launch), each with a
-  // slice of at most about 4096 tokens (8 per thread)
+  // the batch is small, each with a slice of at most about 4096 tokens (8 per
+  // thread). The K workgroups of a sequence wait for each other, so the grid
+  // stays within what the chip holds at once. It is a plain launch: a
+  // workgroup held back past the bounded wait (another stream's pass holding
+  // part of the chip at the same time) makes the call report TV_ERR_HIP
+  // rather than hang.
   const void *path_fn = vec ? reinterpret_cast<const void *>(stochastic_path_kernel<true>)
                             : reinterpret_cast<const void *>(stochastic_path_kernel<false>);
   int K = 1;
@@ -1037,9 +1041,9 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
       ctx->path_blocks_per_cu = nb;
     }
     if (ctx->path_blocks_per_cu > 0) {
-      // splitting pays only when it gives each sequence several workgroups
+      // split when every sequence gets at least two workgroups
       const int cap = min(kMaxGrid, ctx->path_blocks_per_cu * ctx->cu_count);
-      if (cap / B >= 4) K = max(1, min(min(cap / B, (V + 4095) / 4096), 64));
+      if (cap / B >= 2) K = max(1, min(min(cap / B, (V + 4095) / 4096), 64));
     }
   }
   const int slice = (((V + K - 1) / K) + 3) / 4 * 4;
@@ -1059,9 +1063,7 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
                   const_cast<int *>(&chunks),
                   const_cast<double *>(&T), const_cast<double *>(&invT), &stats, &wbuf, &sync, &K,
                   const_cast<int *>(&slice), &accept_len, &path, &bonus, &st};
-  const hipError_t e = K > 1 ? hipLaunchCooperativeKernel(path_fn, dim3(B * K), dim3(kPathThreads), args, 0,
-                                                          ctx->stream)
-                             : hipLaunchKernel(path_fn, dim3(B), dim3(kPathThreads), args, 0, ctx->stream);
+  const hipError_t e = hipLaunchKernel(path_fn, dim3(B * K), dim3(kPathThreads), args, 0, ctx->stream);
   return e == hipSuccess && hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
