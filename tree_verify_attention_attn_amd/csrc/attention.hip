@@ -30,6 +30,8 @@
 // previous tile (Y phase) on the vector ALU.
 #include <math.h>
 
+#include <type_traits>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -42,6 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kKeys = 64;      // keys per tile
+constexpr int kLook = 6;      // X phase: fragment reads run this many products ahead
 constexpr int kMaxChunkTiles = 256;  // tiles per key split (bounds the LDS copy of its page ids)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
@@ -395,65 +398,66 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 
   // X phase of tile j (matrix cores): when j > 0, O += V_{j-1}^T P_{j-1}^T,
   // then S_j = K_j Q^T. PV goes first so that P_{j-1} is dead before S_j is
-  // born. Fragment reads run two steps ahead of the products that use them,
-  // and the four O chains and the two S chains alternate, so no MFMA waits on
-  // the one before it. For j == n the S products read a stale
-  // stage; their result is never used.
+  // born. The products form one unrolled stream (16 PV, then 16 S at
+  // D = 128); the A-operand fragment of product m is read from LDS kLook
+  // products ahead, one read group per product: at most about 12 LDS reads
+  // are in flight, so each product waits only for its own fragment (with
+  // more than the 4-bit LDS counter's 15 reads outstanding, or a different
+  // count on different paths into the phase, the wait would be for all of
+  // them). The four O chains and the two S chains alternate, so
+  // no MFMA waits on the one before it. For j == n the S products read a
+  // stale stage; their result is never used.
   auto X = [&](int j, int jp) __attribute__((always_inline)) {
     const int ks = j % STAGES, vs = (jp + STAGES) % STAGES;
-    bf16x8 kf[3][2];
-    __builtin_amdgcn_sched_barrier(0);
-    if (jp >= 0) {
-      bf16x4 vh[3][DB][2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          vh[f][db][0] = vread(vs, db, f, 0);
-          vh[f][db][1] = vread(vs, db, f, 1);
-        }
+    constexpr int NPV = 4 * DB;  // PV products: 16-key step f, 32-d block db
+    constexpr int NS = 2 * KS;   // S products: 16-d step t, 32-key block kb
+    constexpr int LA = kLook;
+    // A operand of product m (m < NPV: V^T fragment, two transpose reads;
+    // else a K fragment, one 16-byte read)
+    auto frag = [&](int m) __attribute__((always_inline)) -> bf16x8 {
+      if (m < NPV) {
+        const int f = m / DB, db = m % DB;
+        return __builtin_shufflevector(vread(vs, db, f, 0), vread(vs, db, f, 1), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      return kread(ks, (m - NPV) & 1, (m - NPV) >> 1);
+    };
+    auto product = [&](int m, const bf16x8 &a) __attribute__((always_inline)) {
+      if (m < NPV) {
+        const int f = m / DB, db = m % DB;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[f >> 1][f & 1], o[db], 0, 0, 0);
+      } else {
+        const int kb = (m - NPV) & 1, t = (m - NPV) >> 1;
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sc[kb], 0, 0, 0);
+      }
+    };
+    auto run = [&](auto m0c) __attribute__((always_inline)) {
+      constexpr int M0 = decltype(m0c)::value;
+      constexpr int NM = NPV + NS - M0;
+      bf16x8 ring[LA];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (f + 2 < 4) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            vh[(f + 2) % 3][db][0] = vread(vs, db, f + 2, 0);
-            vh[(f + 2) % 3][db][1] = vread(vs, db, f + 2, 1);
-          }
-        } else {
-          kf[f - 2][0] = kread(ks, 0, f - 2);
-          kf[f - 2][1] = kread(ks, 1, f - 2);
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 va = __builtin_shufflevector(vh[f % 3][db][0], vh[f % 3][db][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[f >> 1][f & 1], o[db], 0, 0, 0);
-        }
+      for (int i = 0; i < LA; ++i) {
+        ring[i] = frag(M0 + i);
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        kf[t][0] = kread(ks, 0, t);
-        kf[t][1] = kread(ks, 1, t);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
       __builtin_amdgcn_sched_barrier(0);
-    }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
-#pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      if (t + 2 < KS) {
-        kf[(t + 2) % 3][0] = kread(ks, 0, t + 2);
-        kf[(t + 2) % 3][1] = kread(ks, 1, t + 2);
+      for (int i = 0; i < NM; ++i) {
+        bf16x8 nx;
+        if (i + LA < NM) nx = frag(M0 + i + LA);
+        product(M0 + i, ring[i % LA]);
+        if (i + LA < NM) ring[i % LA] = nx;
+        __builtin_amdgcn_sched_barrier(0);
       }
-      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % 3][0], qf[t], sc[0], 0, 0, 0);
-      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % 3][1], qf[t], sc[1], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    if (jp >= 0)
+      run(std::integral_constant<int, 0>());
+    else
+      run(std::integral_constant<int, NPV>());
   };
 
   // Y phase of tile j (vector ALU): tree/tail visibility, running max, lazy
@@ -649,8 +653,11 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     }
     if (first) wait_for(k);
     barrier_only();
-    if (kt + 1 < n_t) fetch(kt + 1, pid_k);  // page ids for the next Y phase
-    if (vt + 1 < n_t) fetch(vt + 1, pid_v);
+    // page ids for the next Y phase, read unconditionally (a clamped index;
+    // the value is used only when that tile exists) so that the LDS reads
+    // in flight are the same on every path
+    fetch(min(kt + 1, kMaxChunkTiles - 1), pid_k);
+    fetch(min(vt + 1, kMaxChunkTiles - 1), pid_v);
     if (wave_active && n_t > 0) X(k, k - 1);
     if (!first) wait_for(k + 1);
     barrier_only();
