@@ -135,8 +135,10 @@ tv_status tv_build_tree(tv_ctx *ctx, const int32_t *root_tokens, const int32_t *
                         int32_t *parents, int32_t *tokens, int32_t *depth, uint64_t *mask, double *scores,
                         int32_t *n_nodes);
 
-/* Workspace (bytes) tv_attention needs for these host scalars: fp32 partial
- * results when one sequence's keys are split over several workgroups, or,
+/* Workspace (bytes) tv_attention needs for these host scalars: partial
+ * results when one sequence's keys are split over several workgroups (per
+ * row and split: the normalised partial output in fp16, or in fp32 for rows
+ * whose values exceed 4 in magnitude, and its fp32 maximum and sum), or,
  * for many short row groups (at most 32 query rows per KV head, more
  * (sequence, KV head) units than CUs), the order in which the units are
  * dispatched (longest prefix first; B * Hkv int32). The plan depends only on

@@ -324,3 +324,24 @@ def test_bad_page_variants(case):
     assert tv.tv_device_error(DEV) == oracle.INVALID_ARG
     assert np.isnan(out[1]).all()
     assert np.isfinite(out[0]).all()
+
+
+def test_split_partials_wide_rows():
+    # a split plan (several key splits per sequence) where the KV head 1's
+    # values are scaled by 64 (exact in bf16): its rows' partials O/l exceed
+    # the fp16 bound and go to HBM in fp32, the other head's in fp16; both
+    # must merge to the oracle's output
+    w = small("random", N=24, L=(900, 1000), B=2, Hq=8, Hkv=2, seed=17)
+    v = tvgen.bf16_to_f32(w.v_pages)
+    v[:, 1] *= 64.0
+    w.v_pages = (v.view(np.uint32) >> 16).astype(np.uint16)
+    need = tv.tv_attention_workspace_bytes(DEV, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
+    print(f"[attn] wide partials: L={w.prefix_lens.tolist()}, workspace {need} B", flush=True)
+    assert need > 0
+    got, ref = run_full(w)
+    assert np.abs(ref[:, :, 4:]).max() > 4.0  # head group 1 is wide
+    check_attention(got[:, :, :4], ref[:, :, :4], what="fp16 partials")
+    # the outputs are linear in V: the scaled group, brought back to the
+    # unscaled values' size, meets the same bar (the bf16 rounding of P
+    # moves outputs in proportion to |V|)
+    check_attention(got[:, :, 4:] / 64.0, ref[:, :, 4:] / 64.0, what="fp32 partials")

@@ -48,6 +48,11 @@ constexpr int kLook = 6;      // X phase: fragment reads run this many products 
 constexpr int kMaxChunkTiles = 256;  // tiles per key split (bounds the LDS copy of its page ids)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
+// Split partials O/l go to HBM in fp16 when every element of the row is at
+// most this large (fp16 then rounds each within 2^-12 * 4 < 1e-3), else in
+// fp32: half the partial traffic in the common case, no range or precision
+// limit in the others
+constexpr float kHalfBound = 4.0f;
 
 struct AttnArgs {
   const uint16_t *q, *k, *v;
@@ -63,7 +68,9 @@ struct AttnArgs {
   int negate_q;    // sm_scale < 0: negate Q (exact) and use |sm_scale|
   void *out;
   int out_bf16;
-  float *ws_o, *ws_ml;
+  uint16_t *ws_h;  // split partials O/l in fp16 [slot][D] (rows whose |O/l| stays within kHalfBound)
+  float *ws_ml;    // (m, l) per slot; l is stored as -1 - l when the row's O/l went to ws_o
+  float *ws_o;     // split partials O/l in fp32 [slot][D], for the other rows
   int S, chunk_tiles;
   int xcd_remap;   // block ids are laid out so one (b, g) stays on one XCD
   const int32_t *order;  // or null: workgroup i runs unit order[i] (one split, one row group)
@@ -541,6 +548,15 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   // row sum's half swap).
   auto emit = [&](bool nan) __attribute__((always_inline)) {
     const float l_tot = swap_halves_sum(l);
+    // the row's largest |O| (both halves of the wavefront take part)
+    float amax = 0.f;
+    if (a.S > 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[db][e]));
+      amax = swap_halves_max(amax);
+    }
     if (!row_ok) return;
     if (a.S == 1) {
       const int64_t base = ((static_cast<int64_t>(b) * a.N + node) * a.Hq + head) * D;
@@ -556,15 +572,32 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
         }
     } else {
       const int64_t slot = (static_cast<int64_t>(bh) * a.S + s) * a.rows_pad + row;
+      // the partial is O/l (0 for a row with nothing visible in this split)
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const bool half = amax * inv <= kHalfBound;  // false for inf or NaN too
+      if (half) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<float4 *>(a.ws_o + slot * D + db * 32 + 8 * i + 4 * h) =
-              make_float4(o[db][4 * i], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]);
+          for (int i = 0; i < 4; ++i) {
+            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+            f16x4 hv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hv[j] = static_cast<_Float16>(o[db][4 * i + j] * inv);
+            *reinterpret_cast<f16x4 *>(a.ws_h + slot * D + db * 32 + 8 * i + 4 * h) = hv;
+          }
+      } else {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4 *>(a.ws_o + slot * D + db * 32 + 8 * i + 4 * h) =
+                make_float4(o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+                            o[db][4 * i + 3] * inv);
+      }
       if (h == 0) {
         a.ws_ml[slot * 2] = nan ? NAN : m_ref;
-        a.ws_ml[slot * 2 + 1] = l_tot;
+        a.ws_ml[slot * 2 + 1] = half ? l_tot : -1.f - l_tot;
       }
     }
   };
@@ -707,12 +740,14 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   if (!emitted || (bad && !emitted_nan)) emit(bad);
 }
 
-// Merges the S partial (m, l, o) triples of each row in a fixed split order.
-// A row is D/4 lanes, each owning four consecutive d (one 16-byte load per
-// partial), so a wavefront holds 64*4/D rows. Partials are read eight splits
-// at a time with every load of a batch issued before any is used; the
-// running maximum is raised between batches (one batch when S <= 8, which is
-// then the plain max-then-sum merge).
+// Merges the S partials (m, l, O/l) of each row in a fixed split order: the
+// output is sum_s e^(m_s - M) l_s (O/l)_s / sum_s e^(m_s - M) l_s. A row is
+// D/4 lanes, each owning four consecutive d (one 8-byte fp16 load per
+// partial, a 16-byte fp32 load for the rare rows kept wide), so a wavefront
+// holds 64*4/D rows. Partials are read eight splits at a time with every
+// load of a batch issued before any is used; the running maximum is raised
+// between batches (one batch when S <= 8, which is then the plain
+// max-then-sum merge).
 template <int D>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   constexpr int LPR = D / 4;     // lanes per row
@@ -733,17 +768,31 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   float M = -INFINITY, lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   bool bad = false;
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   for (int s0 = 0; s0 < a.S; s0 += kBatch) {
     float2 ml[kBatch];
     float4 ov[kBatch];
+    f16x4 hv[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       ml[q] = make_float2(-INFINITY, 0.f);
-      ov[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      hv[q] = f16x4{};
       if (s0 + q < a.S) {
         const int64_t slot = slot0 + static_cast<int64_t>(s0 + q) * a.rows_pad;
         ml[q] = *reinterpret_cast<const float2 *>(a.ws_ml + slot * 2);
+        hv[q] = *reinterpret_cast<const f16x4 *>(a.ws_h + slot * D + 4 * sub);
+      }
+    }
+    // O/l of each split: fp16, or fp32 for the rows the split kept wide
+    // (marked by a negative l; rare, so their second read is taken apart)
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      ov[q] = make_float4(static_cast<float>(hv[q][0]), static_cast<float>(hv[q][1]), static_cast<float>(hv[q][2]),
+                          static_cast<float>(hv[q][3]));
+      if (ml[q].y < 0.f) {
+        const int64_t slot = slot0 + static_cast<int64_t>(s0 + q) * a.rows_pad;
         ov[q] = *reinterpret_cast<const float4 *>(a.ws_o + slot * D + 4 * sub);
+        ml[q].y = -1.f - ml[q].y;
       }
     }
     float Mb = M;
@@ -763,8 +812,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const float wgt = ml[q].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[q].x - M);
-      lsum = fmaf(wgt, ml[q].y, lsum);
+      // weight of the split's O/l: e^(m - M) * l
+      const float wgt = ml[q].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[q].x - M) * ml[q].y;
+      lsum += wgt;
       acc.x = fmaf(wgt, ov[q].x, acc.x);
       acc.y = fmaf(wgt, ov[q].y, acc.y);
       acc.z = fmaf(wgt, ov[q].z, acc.z);
@@ -872,8 +922,11 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
   if (p.chunk_tiles < 1) p.chunk_tiles = 1;
   p.S = (tiles + p.chunk_tiles - 1) / p.chunk_tiles;
   if (p.S < 1) p.S = 1;
-  p.ws_bytes =
-      p.S > 1 ? static_cast<size_t>(B) * Hkv * p.S * p.row_blocks * p.row_block * (D + 2) * sizeof(float) : 0;
+  // per partial slot: O/l in fp16 and in fp32 (one of the two is written),
+  // and (m, l)
+  p.ws_bytes = p.S > 1 ? static_cast<size_t>(B) * Hkv * p.S * p.row_blocks * p.row_block *
+                             (D * sizeof(uint16_t) + D * sizeof(float) + 2 * sizeof(float))
+                       : 0;
   // many one-workgroup units (the key-split shape: short rows, many
   // sequences) whose prefix lengths may differ: dispatch the longest first
   p.order = (p.ksplit && p.S == 1 && base > cu_count) ? 1 : 0;
@@ -916,8 +969,10 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   a.chunk_tiles = plan.chunk_tiles;
   a.state = ctx->d_state;
   if (plan.S > 1) {
-    a.ws_o = static_cast<float *>(workspace);
-    a.ws_ml = a.ws_o + static_cast<int64_t>(B) * Hkv * plan.S * a.rows_pad * D;
+    const int64_t slots = static_cast<int64_t>(B) * Hkv * plan.S * a.rows_pad;
+    a.ws_h = static_cast<uint16_t *>(workspace);
+    a.ws_ml = reinterpret_cast<float *>(a.ws_h + slots * D);
+    a.ws_o = a.ws_ml + slots * 2;
   }
   const int blocks = B * Hkv * plan.row_blocks * plan.S;
   a.xcd_remap = (blocks % 8) == 0;
