@@ -33,6 +33,8 @@
 //   agrees with exact arithmetic whenever its margin exceeds ~1e-15.
 #include <math.h>
 
+#include <type_traits>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -384,24 +386,31 @@ __device__ inline double exp_fast(double x) {
 // 2^(j/64) from a table the workgroup fills once (exp_table_init, exp_fast of
 // j ln2/64), e^r from its Taylor series to degree 5 (truncation below 4e-17
 // relative). Within a few ulp of e^x (2 ulp worst over 2e7 sampled
-// arguments in [-700, 0]); arguments below -745.2 give 0.
+// arguments in [-700, 0]). The nearest integer k = 64 n + j comes from
+// adding 1.5 * 2^52 (its low bits are then k in two's complement) and 2^n
+// from its exponent bits, so the per-token work has no fp64 rounding,
+// conversion or ldexp instruction; for x below -708.39 (2^n below the normal
+// range) and for x = -inf the result is 0, under 2.3e-308 from e^x.
 __device__ inline void exp_table_init(double *tab, int tid) {
   if (tid < 64) tab[tid] = exp_fast(tid * (kLn2Hi / 64.0) + tid * (kLn2Lo / 64.0));
 }
 
 __device__ inline double exp_tab(double x, const double *tab) {
-  if (!(x > -745.2)) return 0.0;
-  const double k = rint(x * (kLog2eD * 64.0));
+  constexpr double kShift = 6755399441055744.0;  // 1.5 * 2^52
+  const double ks = fma(x, kLog2eD * 64.0, kShift);
+  const double k = ks - kShift;
+  const int ki = static_cast<int>(__double_as_longlong(ks));  // k for |k| < 2^31
   double r = fma(-k, kLn2Hi / 64.0, x);  // exact: k has at most 17 bits, the head 32
   r = fma(-k, kLn2Lo / 64.0, r);
-  const int ki = static_cast<int>(k);
   double p = 1.0 / 120.0;
   p = fma(p, r, 1.0 / 24.0);
   p = fma(p, r, 1.0 / 6.0);
   p = fma(p, r, 0.5);
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
-  return ldexp(tab[ki & 63] * p, ki >> 6);
+  const int e = (ki >> 6) + 1023;  // biased exponent of 2^n
+  const double two_n = __longlong_as_double(static_cast<long long>(e) << 52);
+  return (e > 0 && x > -745.2) ? tab[ki & 63] * p * two_n : 0.0;
 }
 
 // x / T in fp64 from a precomputed 1/T and one FMA correction step (exact
@@ -494,24 +503,8 @@ struct RowStat {
   double m, Z, invZ;
 };
 
-__device__ inline RowStat merge_stats(const double *stats, int64_t row, int which, int chunks, const double *tab) {
-  const double *s = stats + (row * 2 + which) * chunks * 2;
-  double M = -INFINITY;
-  for (int c = 0; c < chunks; ++c) M = fmax(M, s[2 * c]);
-  double Z = 0.0;
-  for (int c = 0; c < chunks; ++c) {
-    if (s[2 * c + 1] > 0.0) Z += s[2 * c + 1] * exp_tab(s[2 * c] - M, tab);
-  }
-  return RowStat{M, Z, 1.0 / Z};
-}
-
-__device__ inline double prob_at(const float *row, int x, double T, double invT, const RowStat &st,
-                                const double *tab) {
-  return exp_tab(div_t(row[x], T, invT) - st.m, tab) * st.invZ;
-}
-
 constexpr int kPathThreads = 512;
-constexpr int kBlk = 16;          // tokens per register block of a row sweep
+constexpr int kBlk = 8;           // tokens per register block of a row sweep
 constexpr int kMaxGrid = 256;     // workgroups of a path pass that exchange partial sums
 constexpr int kMaxExchanges = 128;  // exchanges per sequence: < N stored residuals + 2 draw passes
 constexpr int kCounterStride = 16;  // one 128-byte line per sequence counter
@@ -535,7 +528,7 @@ struct Pi {
 // two per-sequence rows) and the next sibling is tested against it. The
 // final draw - from the last rejected sibling's residual (built on the fly)
 // or from pi - sweeps the slices once in contiguous token-order segments
-// (16-token register blocks, next block's loads issued before the current
+// (8-token register blocks, next block's loads issued before the current
 // block's exponentials). Every sweep ends in an exchange: each workgroup
 // publishes its slice's mass, pi's old and new weight at the next sibling's
 // token, and its last positive token through device-scope atomics, counts
@@ -543,7 +536,7 @@ struct Pi {
 // fixed order, so every workgroup reaches the same decisions. For the draw,
 // the first slice (then segment) whose running sum passes theta is found,
 // and only that segment is swept again, one token per lane of a wavefront.
-template <bool kVec>
+template <bool kVec, bool kUnitT>
 __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
     const int32_t *__restrict__ parents, const int32_t *__restrict__ sizes, const float *__restrict__ uniforms,
@@ -559,97 +552,29 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   __shared__ unsigned long long s_child[128][2];  // children of each node: ids 0..63, 64..127
   __shared__ double s_part[kMaxGrid], s_xnew[kMaxGrid], s_xold[kMaxGrid];
   __shared__ int s_xlp[kMaxGrid];
+  // the exchange's fixed-order reductions over the K slices: total mass, the
+  // new and old weights at the next sibling's token, the last positive token,
+  // and each slice's exclusive prefix of the mass
+  __shared__ double s_sum, s_sum_new, s_sum_old, s_pre[kMaxGrid], s_inc[kMaxGrid];
+  __shared__ int s_glast;
   __shared__ double s_tab[64];
   const int b = blockIdx.x / K, kk = blockIdx.x % K;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t base = static_cast<int64_t>(b) * N;
-  if (wid == 0) {
-    exp_table_init(s_tab, lane);  // wavefront 0 fills it and uses it first
-    // validation with the same precedence as a serial check: a node count
-    // outside [1, N], a bad parent among the present nodes, then a draft
-    // token outside [0, V). Lane i holds nodes i and i + 64.
-    const int nb = sizes ? sizes[b] : N;
-    const bool bad_size = nb < 1 || nb > N;
-    bool tree_bad = false, tok_bad = false;
-    int p[2], t[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = lane + 64 * h;
-      p[h] = -1;
-      t[h] = 0;
-      if (!bad_size && i < nb) {
-        p[h] = parents[base + i];
-        tree_bad |= p[h] < -1 || p[h] >= i || (i == 0 && p[h] != -1);
-        if (i >= 1) {
-          t[h] = draft_tokens[base + i];
-          tok_bad |= t[h] < 0 || t[h] >= V;
-        }
-      }
-      if (i < N) s_u[i] = static_cast<double>(uniforms[base + i]);
-    }
-    const int err = bad_size                                 ? TV_ERR_INVALID_ARG
-                    : __builtin_amdgcn_ballot_w64(tree_bad) ? TV_ERR_INVALID_TREE
-                    : __builtin_amdgcn_ballot_w64(tok_bad)  ? TV_ERR_INVALID_ARG
-                                                            : 0;
-    // row statistics of every present node, then its first test's p(t_c)
-    // (under its parent's target row) and q_c(t_c)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = lane + 64 * h;
-      if (!err && i < nb) {
-        s_tst[i] = merge_stats(stats, base + i, 0, chunks, s_tab);
-        s_dst[i] = i >= 1 ? merge_stats(stats, base + i, 1, chunks, s_tab) : RowStat{0.0, 1.0, 1.0};
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int i = lane + 64 * h;
-      if (!err && i >= 1 && i < nb) {
-        s_tok[i] = t[h];
-        if (p[h] >= 0) {  // a node without a parent (forest) is never tested
-          s_pa[i] = prob_at(target + (base + p[h]) * V, t[h], T, invT, s_tst[p[h]], s_tab);
-          s_qa[i] = prob_at(draft + (base + i) * V, t[h], T, invT, s_dst[i], s_tab);
-        }
-      }
-    }
-    for (int n = 0; n < (err ? 0 : nb); ++n) {
-      const uint64_t k0 = __builtin_amdgcn_ballot_w64(lane >= 1 && lane < nb && p[0] == n);
-      const uint64_t k1 = __builtin_amdgcn_ballot_w64(lane + 64 < nb && p[1] == n);
-      if (lane == 0) {
-        s_child[n][0] = k0;
-        s_child[n][1] = k1;
-      }
-    }
-    if (lane == 0) {
-      s_err = err;
-      s_pick = 0x7FFFFFFF;
-      s_cross = 0x7FFFFFFF;
-      s_lp = -1;
-      s_wt_new = 0.0;
-      s_wt_old = 0.0;
-      s_path[0] = 0;
-    }
-  }
-  __syncthreads();
-  if (s_err) {
-    if (kk == 0) {
-      if (tid == 0) {
-        raise_error(state, s_err);
-        accept_len[b] = -1;
-        bonus[b] = -1;
-      }
-      for (int i = tid; i < N; i += kPathThreads) path[base + i] = -1;
-    }
-    return;
-  }
+  // a logit over T (exact when T = 1, the kUnitT form)
+  auto scaled = [&](float v) __attribute__((always_inline)) -> double {
+    if constexpr (kUnitT)
+      return static_cast<double>(v);
+    else
+      return div_t(v, T, invT);
+  };
+  const int nb = sizes ? sizes[b] : N;
+  const bool bad_size = nb < 1 || nb > N;
   // this workgroup's slice, split into contiguous per-thread segments
   // (multiples of 4 tokens)
   const int v0 = min(kk * slice, V), v1 = min(v0 + slice, V);
   const int seg = ((v1 - v0 + 4 * kPathThreads - 1) / (4 * kPathThreads)) * 4;
   const int x0 = min(v0 + tid * seg, v1), x1 = min(x0 + seg, v1);
-  double *const buf0 = wbuf + static_cast<int64_t>(b) * 2 * V;
-  double *const buf1 = buf0 + V;
-
   auto load_block = [&](const float *row, int xb, float (&v)[kBlk]) __attribute__((always_inline)) {
     if (kVec) {  // V % 4 == 0 and xb % 4 == 0: a float4 is either all in [x0, x1) or all out
 #pragma unroll
@@ -671,49 +596,207 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) v[i] = xb + i < x1 ? w[xb + i] : 0.0;
   };
+  exp_table_init(s_tab, tid);
+  // thread i < nb (i >= 1) reads node i's parent and token, and, when both are
+  // in range, the two logits of its first test (target row of the parent and
+  // its own draft row at its token): random reads whose latency then overlaps
+  // the statistics merge below
+  float l_pa = 0.f, l_qa = 0.f;
+  int my_p = -1;
+  if (!bad_size && tid >= 1 && tid < nb) {
+    my_p = parents[base + tid];
+    const int t = draft_tokens[base + tid];
+    if (my_p >= 0 && my_p < tid && t >= 0 && t < V) {
+      l_pa = target[(base + my_p) * V + t];
+      l_qa = draft[(base + tid) * V + t];
+    }
+  }
+  if (wid == 0) {
+    // validation with the same precedence as a serial check: a node count
+    // outside [1, N], a bad parent among the present nodes, then a draft
+    // token outside [0, V). Lane i holds nodes i and i + 64.
+    bool tree_bad = false, tok_bad = false;
+    int p[2], t[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      p[h] = -1;
+      t[h] = 0;
+      if (!bad_size && i < nb) {
+        p[h] = parents[base + i];
+        tree_bad |= p[h] < -1 || p[h] >= i || (i == 0 && p[h] != -1);
+        if (i >= 1) {
+          t[h] = draft_tokens[base + i];
+          tok_bad |= t[h] < 0 || t[h] >= V;
+        }
+      }
+      if (i < N) s_u[i] = static_cast<double>(uniforms[base + i]);
+      if (i >= 1 && i < nb) s_tok[i] = t[h];
+    }
+    const int err = bad_size                                 ? TV_ERR_INVALID_ARG
+                    : __builtin_amdgcn_ballot_w64(tree_bad) ? TV_ERR_INVALID_TREE
+                    : __builtin_amdgcn_ballot_w64(tok_bad)  ? TV_ERR_INVALID_ARG
+                                                            : 0;
+    for (int n = 0; n < (err ? 0 : nb); ++n) {
+      const uint64_t k0 = __builtin_amdgcn_ballot_w64(lane >= 1 && lane < nb && p[0] == n);
+      const uint64_t k1 = __builtin_amdgcn_ballot_w64(lane + 64 < nb && p[1] == n);
+      if (lane == 0) {
+        s_child[n][0] = k0;
+        s_child[n][1] = k1;
+      }
+    }
+    if (lane == 0) {
+      s_err = err;
+      s_pick = 0x7FFFFFFF;
+      s_cross = 0x7FFFFFFF;
+      s_lp = -1;
+      s_wt_new = 0.0;
+      s_wt_old = 0.0;
+      s_path[0] = 0;
+    }
+  }
+  __syncthreads();  // s_tab, s_child, s_err
+  // first blocks of a target row and a draft row loaded ahead of their sweep,
+  // tagged with their node: the root's row and its first child's row after
+  // the statistics merge, the next sibling's row during each sweep
+  float ppre[kBlk], qpre[kBlk];
+  int ppre_node = -1, qpre_node = -1;
+  // statistics of every present row (target and draft of each node) from
+  // its chunks' (max, sum of exp): four threads per row, each taking every
+  // fourth chunk, combined in a fixed butterfly so that all four, and every
+  // workgroup of the sequence, hold the same values
+  if (!bad_size) {
+    const int sub = tid & 3;
+    for (int r = tid >> 2; r < 2 * nb; r += kPathThreads / 4) {
+      const int node = r >> 1, which = r & 1;
+      const double *st = stats + ((base + node) * 2 + which) * chunks * 2;
+      double M = -INFINITY;
+      for (int c = sub; c < chunks; c += 4) M = fmax(M, st[2 * c]);
+      M = fmax(M, __shfl_xor(M, 1));
+      M = fmax(M, __shfl_xor(M, 2));
+      double Z = 0.0;
+      for (int c = sub; c < chunks; c += 4)
+        if (st[2 * c + 1] > 0.0) Z += st[2 * c + 1] * exp_tab(st[2 * c] - M, s_tab);
+      Z += __shfl_xor(Z, 1);
+      Z += __shfl_xor(Z, 2);
+      if (sub == 0) {
+        if (which == 0)
+          s_tst[node] = RowStat{M, Z, 1.0 / Z};
+        else
+          s_dst[node] = node >= 1 ? RowStat{M, Z, 1.0 / Z} : RowStat{0.0, 1.0, 1.0};
+      }
+    }
+  }
+  if (!s_err) {
+    load_block(target + base * V, x0, ppre);
+    ppre_node = 0;
+    if (s_child[0][0] | s_child[0][1]) {
+      const int c0 = s_child[0][0] ? __builtin_ctzll(s_child[0][0]) : 64 + __builtin_ctzll(s_child[0][1]);
+      load_block(draft + (base + c0) * V, x0, qpre);
+      qpre_node = c0;
+    }
+  }
+  __syncthreads();  // s_tst, s_dst, s_err
+  // each present node's first test: p(t_c) under its parent's target row
+  // and q_c(t_c) (a node without a parent, in a forest, is never tested)
+  if (!s_err && tid >= 1 && tid < nb && my_p >= 0) {
+    s_pa[tid] = exp_tab(scaled(l_pa) - s_tst[my_p].m, s_tab) * s_tst[my_p].invZ;
+    s_qa[tid] = exp_tab(scaled(l_qa) - s_dst[tid].m, s_tab) * s_dst[tid].invZ;
+  }
+  __syncthreads();
+  if (s_err) {
+    if (kk == 0) {
+      if (tid == 0) {
+        raise_error(state, s_err);
+        accept_len[b] = -1;
+        bonus[b] = -1;
+      }
+      for (int i = tid; i < N; i += kPathThreads) path[base + i] = -1;
+    }
+    return;
+  }
+  double *const buf0 = wbuf + static_cast<int64_t>(b) * 2 * V;
+  double *const buf1 = buf0 + V;
+
   // pi's weight of one token (the target row's probability, or the stored
   // residual's entry)
   auto base_weight = [&](const RowStat &sp, const Pi &pi, float pl, double wl) __attribute__((always_inline)) {
-    return pi.w ? wl : exp_tab(div_t(pl, T, invT) - sp.m, s_tab) * sp.invZ;  // padding (-inf) gives 0
+    return pi.w ? wl : exp_tab(scaled(pl) - sp.m, s_tab) * sp.invZ;  // padding (-inf) gives 0
   };
   // with a sibling's draft row: the residual max(0, pi - q) with pi normalised
   auto resid_weight = [&](double w, const Pi &pi, const RowStat &sq, float ql) __attribute__((always_inline)) {
-    return fmax(0.0, w * pi.invM - exp_tab(div_t(ql, T, invT) - sq.m, s_tab) * sq.invZ);
+    return fmax(0.0, w * pi.invM - exp_tab(scaled(ql) - sq.m, s_tab) * sq.invZ);
   };
   // one sweep of this thread's segment; stores every weight into dst if
   // given; the thread holding token tnext records pi's old and new weight
-  // there
-  auto sweep = [&](const float *P, const RowStat &sp, const Pi &pi, const float *Q, const RowStat &sq, double *dst,
-                   int tnext, double &local, int &lastpos) __attribute__((always_inline)) {
+  // there. The form (pi stored or a target row, with or without a sibling's
+  // draft row, with or without dst) is chosen once per sweep, so a block of
+  // 8 tokens is straight-line code: its 8 (or 16) exponentials overlap, and
+  // per-token conditions are selects (tokens past the segment weigh 0).
+  auto sweep_form = [&](auto has_w, auto has_q, auto has_dst, const float *P, int pnode, const RowStat &sp,
+                        const Pi &pi, const float *Q, int qnode, const RowStat &sq, const float *Qnext,
+                        int qnext_node, double *dst, int tnext, double &local, int &lastpos)
+      __attribute__((always_inline)) {
+    constexpr bool kW = decltype(has_w)::value, kQ = decltype(has_q)::value, kDst = decltype(has_dst)::value;
     local = 0.0;
     lastpos = -1;
     float pv[kBlk], qv[kBlk], pn[kBlk], qn[kBlk];
     double wv[kBlk], wn[kBlk];
-    if (pi.w)
+    if constexpr (kW) {
       load_wblock(pi.w, x0, wv);
-    else
+    } else if (pnode == ppre_node) {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) pv[i] = ppre[i];
+    } else {
       load_block(P, x0, pv);
-    if (Q) load_block(Q, x0, qv);
+    }
+    if constexpr (kQ) {
+      if (qnode == qpre_node) {
+#pragma unroll
+        for (int i = 0; i < kBlk; ++i) qv[i] = qpre[i];
+      } else {
+        load_block(Q, x0, qv);
+      }
+    }
+    // the next sibling's row: its first block loads while this sweep computes
+    if (Qnext) {
+      load_block(Qnext, x0, qpre);
+      qpre_node = qnext_node;
+    }
+    double w0_at = 0.0, w_at = 0.0;
     for (int xb = x0; xb < x1; xb += kBlk) {
       if (xb + kBlk < x1) {
-        if (pi.w)
+        if constexpr (kW)
           load_wblock(pi.w, xb + kBlk, wn);
         else
           load_block(P, xb + kBlk, pn);
-        if (Q) load_block(Q, xb + kBlk, qn);
+        if constexpr (kQ) load_block(Q, xb + kBlk, qn);
       }
+      double wb[kBlk];
 #pragma unroll
       for (int i = 0; i < kBlk; ++i) {
-        const double w0 = base_weight(sp, pi, pv[i], wv[i]);
-        const double w = Q ? resid_weight(w0, pi, sq, qv[i]) : w0;
+        double w0;
+        if constexpr (kW)
+          w0 = wv[i];
+        else
+          w0 = exp_tab(scaled(pv[i]) - sp.m, s_tab) * sp.invZ;  // padding (-inf) gives 0
+        double w = w0;
+        if constexpr (kQ) w = fmax(0.0, w0 * pi.invM - exp_tab(scaled(qv[i]) - sq.m, s_tab) * sq.invZ);
+        wb[i] = w;
         local += w;
-        if (w > 0.0) lastpos = xb + i;
-        if (xb + i < x1) {
-          if (dst) dst[xb + i] = w;
-          if (xb + i == tnext) {
-            s_wt_old = w0;
-            s_wt_new = w;
-          }
+        lastpos = w > 0.0 ? xb + i : lastpos;
+        const bool at = xb + i == tnext;
+        w0_at = at ? w0 : w0_at;
+        w_at = at ? w : w_at;
+      }
+      if constexpr (kDst) {
+        if (xb + kBlk <= x1) {
+#pragma unroll
+          for (int i = 0; i < kBlk; ++i) dst[xb + i] = wb[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < kBlk; ++i)
+            if (xb + i < x1) dst[xb + i] = wb[i];
         }
       }
 #pragma unroll
@@ -722,6 +805,32 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
         qv[i] = qn[i];
         wv[i] = wn[i];
       }
+    }
+    if (tnext >= x0 && tnext < x1) {
+      s_wt_old = w0_at;
+      s_wt_new = w_at;
+    }
+  };
+  auto sweep = [&](const float *P, int pnode, const RowStat &sp, const Pi &pi, const float *Q, int qnode,
+                   const RowStat &sq, const float *Qnext, int qnext_node, double *dst, int tnext, double &local,
+                   int &lastpos) __attribute__((always_inline)) {
+    using T0 = std::false_type;
+    using T1 = std::true_type;
+    if (dst) {  // a rejected sibling with siblings left: always a draft row, pi either form
+      if (pi.w)
+        sweep_form(T1(), T1(), T1(), P, pnode, sp, pi, Q, qnode, sq, Qnext, qnext_node, dst, tnext, local, lastpos);
+      else
+        sweep_form(T0(), T1(), T1(), P, pnode, sp, pi, Q, qnode, sq, Qnext, qnext_node, dst, tnext, local, lastpos);
+    } else if (Q) {
+      if (pi.w)
+        sweep_form(T1(), T1(), T0(), P, pnode, sp, pi, Q, qnode, sq, Qnext, qnext_node, dst, tnext, local, lastpos);
+      else
+        sweep_form(T0(), T1(), T0(), P, pnode, sp, pi, Q, qnode, sq, Qnext, qnext_node, dst, tnext, local, lastpos);
+    } else {
+      if (pi.w)
+        sweep_form(T1(), T0(), T0(), P, pnode, sp, pi, Q, qnode, sq, Qnext, qnext_node, dst, tnext, local, lastpos);
+      else
+        sweep_form(T0(), T0(), T0(), P, pnode, sp, pi, Q, qnode, sq, Qnext, qnext_node, dst, tnext, local, lastpos);
     }
   };
   // exclusive prefix of the segment sums within the workgroup and the
@@ -736,7 +845,9 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     double excl = __shfl_up(incl, 1);
     if (lane == 0) excl = 0.0;
     if (lane == 63) s_wave[wid] = incl;
-    if (lastpos >= 0) atomicMax(&s_lp, lastpos);
+    int lp = lastpos;
+    for (int d = 32; d >= 1; d >>= 1) lp = max(lp, __shfl_xor(lp, d));
+    if (lane == 0 && lp >= 0) atomicMax(&s_lp, lp);
     __syncthreads();
     if (tid == 0) {
       double run = 0.0;
@@ -804,6 +915,37 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     }
     ++nx;
     __syncthreads();
+    // wavefront 0, lane i = slice i (K <= 64): the slices' masses as an
+    // inclusive scan (the total is the last lane's), the weight sums and the
+    // last positive token, each in a fixed order
+    if (wid == 0 && s_ok) {
+      const bool in = lane < K;
+      double m = in ? s_part[lane] : 0.0, wn = in ? s_xnew[lane] : 0.0, wo = in ? s_xold[lane] : 0.0;
+      int lp = in ? s_xlp[lane] : -1;
+      double incl = m;
+      for (int d = 1; d < 64; d <<= 1) {
+        const double t = __shfl_up(incl, d);
+        if (lane >= d) incl += t;
+      }
+      for (int d = 32; d >= 1; d >>= 1) {
+        wn += __shfl_xor(wn, d);
+        wo += __shfl_xor(wo, d);
+        lp = max(lp, __shfl_xor(lp, d));
+      }
+      double excl = __shfl_up(incl, 1);
+      if (lane == 0) excl = 0.0;
+      if (in) {
+        s_pre[lane] = excl;
+        s_inc[lane] = incl;
+      }
+      if (lane == K - 1) s_sum = incl;
+      if (lane == 0) {
+        s_sum_new = wn;
+        s_sum_old = wo;
+        s_glast = lp;
+      }
+    }
+    __syncthreads();
     return s_ok != 0;
   };
 
@@ -840,15 +982,13 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       double local, prefix;
       int lastpos;
       const int next = kids0 ? __builtin_ctzll(kids0) : 64 + __builtin_ctzll(kids1);
-      sweep(P, sp, pi, draft + (base + c) * V, sq, dst, s_tok[next], local, lastpos);
+      // the next sibling's row is swept next (rejected with siblings left, or
+      // as the final draw's residual)
+      sweep(P, node, sp, pi, draft + (base + c) * V, c, sq, draft + (base + next) * V, next, dst, s_tok[next], local,
+            lastpos);
       scan(local, lastpos, prefix);
       if (!(ok = exchange())) break;
-      double total = 0.0, wnew = 0.0, wold = 0.0;
-      for (int i = 0; i < K; ++i) {
-        total += s_part[i];
-        wnew += s_xnew[i];
-        wold += s_xold[i];
-      }
+      const double total = s_sum, wnew = s_sum_new, wold = s_sum_old;
       if (total > 0.0) {
         pi = Pi{dst, 1.0 / total};
         wt = wnew;
@@ -875,27 +1015,17 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       const float *Qp = pass == 0 ? Q : nullptr;
       double local, prefix;
       int lastpos;
-      sweep(P, sp, pi, Qp, sq, nullptr, -1, local, lastpos);
+      sweep(P, node, sp, pi, Qp, pass == 0 ? pend : -1, sq, nullptr, -1, nullptr, -1, local, lastpos);
       scan(local, lastpos, prefix);
       if (!(ok = exchange())) break;
-      double total = 0.0;
-      int glast = -1;
-      for (int i = 0; i < K; ++i) {
-        total += s_part[i];
-        glast = max(glast, s_xlp[i]);
-      }
+      const double total = s_sum;
+      const int glast = s_glast;
       if (Qp && !(total > 0.0)) continue;  // no residual mass: draw from pi instead
       const double theta = u * total;
       // the first slice whose running sum passes theta holds the draw
-      int cross_wg = -1;
-      double wg_prefix = 0.0, run = 0.0;
-      for (int i = 0; i < K; ++i) {
-        if (cross_wg < 0 && run + s_part[i] > theta) {
-          cross_wg = i;
-          wg_prefix = run;
-        }
-        run += s_part[i];
-      }
+      const uint64_t crossing = __builtin_amdgcn_ballot_w64(lane < K && s_inc[min(lane, K - 1)] > theta);
+      const int cross_wg = crossing ? static_cast<int>(__builtin_ctzll(crossing)) : -1;
+      const double wg_prefix = cross_wg >= 0 ? s_pre[cross_wg] : 0.0;
       writer = cross_wg >= 0 ? cross_wg : 0;
       pick = glast;  // rounding left no crossing: the last token of positive weight
       if (cross_wg == kk) {
@@ -1031,14 +1161,21 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
   // workgroup held back past the bounded wait (another stream's pass holding
   // part of the chip at the same time) makes the call report TV_ERR_HIP
   // rather than hang.
-  const void *path_fn = vec ? reinterpret_cast<const void *>(stochastic_path_kernel<true>)
-                            : reinterpret_cast<const void *>(stochastic_path_kernel<false>);
+  const void *forms[4] = {reinterpret_cast<const void *>(stochastic_path_kernel<false, false>),
+                          reinterpret_cast<const void *>(stochastic_path_kernel<false, true>),
+                          reinterpret_cast<const void *>(stochastic_path_kernel<true, false>),
+                          reinterpret_cast<const void *>(stochastic_path_kernel<true, true>)};
+  const void *path_fn = forms[(vec ? 2 : 0) + (T == 1.0 ? 1 : 0)];
   int K = 1;
   if (B <= kMaxGrid && V >= 2 * 4096) {
-    if (ctx->path_blocks_per_cu == 0) {
-      int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, path_fn, kPathThreads, 0) != hipSuccess || nb < 1) nb = -1;
-      ctx->path_blocks_per_cu = nb;
+    if (ctx->path_blocks_per_cu == 0) {  // the least over the four forms
+      int least = 1 << 30;
+      for (const void *fn : forms) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kPathThreads, 0) != hipSuccess || nb < 1) nb = -1;
+        least = min(least, nb);
+      }
+      ctx->path_blocks_per_cu = least;
     }
     if (ctx->path_blocks_per_cu > 0) {
       // split when every sequence gets at least two workgroups
