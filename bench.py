@@ -57,6 +57,9 @@ def parse():
                     help="stop after the timed region (steps and call blocks; no mask-cost, decode, cold-cache, "
                          "builder, commit or other-workload timings), so that a trace sees the step's kernels only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
+    ap.add_argument("--power-seconds", type=int, default=3,
+                    help="seconds of back-to-back tv_attention calls during which amd-smi samples package power and "
+                         "clocks (0 to skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one device-to-device copy of this many MiB (an HBM counter "
                          "calibration point for rocprofv3 --pmc runs)")
@@ -469,6 +472,60 @@ class Setup:
 ATTN_KERNEL = "tv_attention: attn_mfma_kernel (+ attn_combine_kernel when the keys are split)"
 
 
+def power_sample(torch, call, seconds):
+    """Runs `call` back to back for about `seconds` + 2 s while amd-smi samples
+    the package power and the graphics clock of every XCD once a second
+    (`amd-smi metric -p -c`), and reads the board's power cap (`rocm-smi
+    --showmaxpower`). Returns None when the tools are missing."""
+    import shutil
+    import subprocess
+
+    if shutil.which("amd-smi") is None:
+        return None
+    smp = subprocess.Popen(["amd-smi", "metric", "-p", "-c", "--csv", "-w", "1", "-W", str(int(seconds))],
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds + 2.0:
+        for _ in range(50):
+            call()
+        n += 50
+    torch.cuda.synchronize()
+    try:
+        out = smp.communicate(timeout=30)[0]
+    except subprocess.TimeoutExpired:
+        smp.kill()
+        return None
+    hdr, rows = None, []
+    for line in out.splitlines():
+        f = [x.strip() for x in line.split(",")]
+        if "socket_power" in f:
+            hdr = f
+        elif hdr and len(f) == len(hdr):
+            r = dict(zip(hdr, f))
+            try:
+                clk = [float(r[f"gfx_{i}_clk"]) for i in range(8) if f"gfx_{i}_clk" in r and r[f"gfx_{i}_clk"] != "N/A"]
+                rows.append((float(r["socket_power"]), sum(clk) / len(clk) if clk else None))
+            except (KeyError, ValueError):
+                pass
+    if len(rows) < 2:
+        return None
+    rows = rows[1:]  # the first sample can precede the load
+    cap = None
+    if shutil.which("rocm-smi"):
+        txt = subprocess.run(["rocm-smi", "--showmaxpower"], capture_output=True, text=True).stdout
+        for line in txt.splitlines():
+            if "Max Graphics Package Power" in line:
+                try:
+                    cap = float(line.rsplit(":", 1)[1])
+                except ValueError:
+                    pass
+    return {"socket_power_w": [p for p, _ in rows], "gfx_clock_mhz": [c for _, c in rows],
+            "power_cap_w": cap, "calls": n,
+            "note": "amd-smi metric -p -c once a second while the call runs back to back (the first sample "
+                    "dropped); gfx_clock_mhz = mean over the XCDs of each sample"}
+
+
 def extra_config(torch, tv, cfg, n):
     """Attention and acceptance of another workload, as extra keys of the line."""
     s = Setup(torch, tv, cfg)
@@ -578,6 +635,9 @@ def main():
         print(json.dumps(result), flush=True)
         return
     result["mask_overhead"] = s.mask_cost()
+    # the package power and clock while tv_attention runs back to back
+    if args.power_seconds > 0:
+        result["power"] = power_sample(torch, s.attention, args.power_seconds)
     # verify premium: the same call for the root row only (N = 1, a plain
     # decode step) over the same KV, blocks of 20 calls, medians of 5 blocks
     q1 = s.q[:, :1].contiguous()

@@ -742,19 +742,19 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 
 // Merges the S partials (m, l, O/l) of each row in a fixed split order: the
 // output is sum_s e^(m_s - M) l_s (O/l)_s / sum_s e^(m_s - M) l_s. A row is
-// D/4 lanes, each owning four consecutive d (one 8-byte fp16 load per
-// partial, a 16-byte fp32 load for the rare rows kept wide), so a wavefront
-// holds 64*4/D rows. Partials are read eight splits at a time with every
-// load of a batch issued before any is used; the running maximum is raised
-// between batches (one batch when S <= 8, which is then the plain
-// max-then-sum merge).
+// D/8 lanes, each owning eight consecutive d (one 16-byte fp16 load per
+// partial, two 16-byte fp32 loads for the rare rows kept wide), so a
+// wavefront holds 64*8/D rows. Partials are read eight splits at a time with
+// every load of a batch issued before any is used; the running maximum is
+// raised between batches (one batch when S <= 8, which is then the plain
+// max-then-sum merge). The rows of one (b, g) run on the XCD whose L2 took
+// that unit's partials.
 template <int D>
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
-  constexpr int LPR = D / 4;     // lanes per row
+  constexpr int LPR = D / 8;     // lanes per row, eight d each
   constexpr int RPW = 64 / LPR;  // rows per wavefront
   constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63, sub = lane % LPR;
-  // the rows of one (b, g) on the XCD whose L2 took that unit's partials
   int64_t blk = blockIdx.x;
   if (a.xcd_remap && (gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
   const int64_t r = (blk * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
@@ -766,32 +766,35 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
   if (row >= nb * a.G) return;  // an absent node's row has no output
   const int64_t slot0 = static_cast<int64_t>(bh) * a.S * a.rows_pad + row;
   float M = -INFINITY, lsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   bool bad = false;
-  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   for (int s0 = 0; s0 < a.S; s0 += kBatch) {
     float2 ml[kBatch];
-    float4 ov[kBatch];
-    f16x4 hv[kBatch];
+    f16x8 hv[kBatch];
+    float ov[kBatch][8];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       ml[q] = make_float2(-INFINITY, 0.f);
-      hv[q] = f16x4{};
+      hv[q] = f16x8{};
       if (s0 + q < a.S) {
         const int64_t slot = slot0 + static_cast<int64_t>(s0 + q) * a.rows_pad;
         ml[q] = *reinterpret_cast<const float2 *>(a.ws_ml + slot * 2);
-        hv[q] = *reinterpret_cast<const f16x4 *>(a.ws_h + slot * D + 4 * sub);
+        hv[q] = *reinterpret_cast<const f16x8 *>(a.ws_h + slot * D + 8 * sub);
       }
     }
     // O/l of each split: fp16, or fp32 for the rows the split kept wide
     // (marked by a negative l; rare, so their second read is taken apart)
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      ov[q] = make_float4(static_cast<float>(hv[q][0]), static_cast<float>(hv[q][1]), static_cast<float>(hv[q][2]),
-                          static_cast<float>(hv[q][3]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ov[q][e] = static_cast<float>(hv[q][e]);
       if (ml[q].y < 0.f) {
         const int64_t slot = slot0 + static_cast<int64_t>(s0 + q) * a.rows_pad;
-        ov[q] = *reinterpret_cast<const float4 *>(a.ws_o + slot * D + 4 * sub);
+        const float4 lo = *reinterpret_cast<const float4 *>(a.ws_o + slot * D + 8 * sub);
+        const float4 hi = *reinterpret_cast<const float4 *>(a.ws_o + slot * D + 8 * sub + 4);
+        ov[q][0] = lo.x; ov[q][1] = lo.y; ov[q][2] = lo.z; ov[q][3] = lo.w;
+        ov[q][4] = hi.x; ov[q][5] = hi.y; ov[q][6] = hi.z; ov[q][7] = hi.w;
         ml[q].y = -1.f - ml[q].y;
       }
     }
@@ -804,10 +807,8 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
     if (Mb != M) {  // raise the running maximum (M = -inf holds nothing yet)
       const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
       lsum *= sc;
-      acc.x *= sc;
-      acc.y *= sc;
-      acc.z *= sc;
-      acc.w *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= sc;
       M = Mb;
     }
 #pragma unroll
@@ -815,18 +816,18 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
       // weight of the split's O/l: e^(m - M) * l
       const float wgt = ml[q].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[q].x - M) * ml[q].y;
       lsum += wgt;
-      acc.x = fmaf(wgt, ov[q].x, acc.x);
-      acc.y = fmaf(wgt, ov[q].y, acc.y);
-      acc.z = fmaf(wgt, ov[q].z, acc.z);
-      acc.w = fmaf(wgt, ov[q].w, acc.w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt, ov[q][e], acc[e]);
     }
   }
   const int i = row / a.G, h = g * a.G + row % a.G;
   const int64_t base = ((static_cast<int64_t>(b) * a.N + i) * a.Hq + h) * D;
   const float inv = 1.f / lsum;
-  float v4[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-  if (bad) v4[0] = v4[1] = v4[2] = v4[3] = NAN;
-  store_out(a, base, 4 * sub, v4);
+  float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  float w4[4] = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  if (bad) v4[0] = v4[1] = v4[2] = v4[3] = w4[0] = w4[1] = w4[2] = w4[3] = NAN;
+  store_out(a, base, 8 * sub, v4);
+  store_out(a, base, 8 * sub + 4, w4);
 }
 
 // Orders the (b, g) units of a one-split plan by their number of 64-key tiles,
@@ -993,7 +994,7 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
     launch_dw<64>(plan.qb, plan.ksplit, flat, grid, block, ctx->stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
-    const int rows_per_wg = 4 * (64 / (D / 4));  // four wavefronts, 64*4/D rows each
+    const int rows_per_wg = 4 * (64 / (D / 8));  // four wavefronts, 64*8/D rows each
     const dim3 cgrid(static_cast<unsigned>((static_cast<int64_t>(B) * Hkv * a.rows + rows_per_wg - 1) / rows_per_wg));
     if (D == 128)
       hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, ctx->stream, a);
