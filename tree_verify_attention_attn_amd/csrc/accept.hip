@@ -519,10 +519,10 @@ struct Pi {
 
 // K workgroups per sequence (K = 1 when the batch alone fills the chip),
 // each owning a contiguous slice of the vocabulary. Wavefront 0 of every
-// workgroup validates the tree, computes for every node c its first test's
-// p(t_c) (under its parent's target row) and q_c(t_c), and the children of
-// every node as a bit mask; all threads of all K workgroups then take the
-// same walk from these copies. The current node's children are tested in
+// workgroup validates the tree and builds the children of every node as a
+// bit mask; all threads merge the row statistics and compute for every node
+// c its first test's p(t_c) (under its parent's target row) and q_c(t_c);
+// all threads of all K workgroups then take the same walk from these copies. The current node's children are tested in
 // id order; a rejection followed by another sibling stores the residual
 // max(0, pi - q_c) of the vocabulary (each workgroup its slice, in one of
 // two per-sequence rows) and the next sibling is tested against it. The
@@ -532,8 +532,9 @@ struct Pi {
 // block's exponentials). Every sweep ends in an exchange: each workgroup
 // publishes its slice's mass, pi's old and new weight at the next sibling's
 // token, and its last positive token through device-scope atomics, counts
-// itself in, and waits (bounded) until all K have; sums are then taken in a
-// fixed order, so every workgroup reaches the same decisions. For the draw,
+// itself in, and waits (bounded) until all K have; wavefront 0 then reduces
+// the K slices in a fixed order, so every workgroup reaches the same
+// decisions. T = 1 has a form of its own (no division of the logits). For the draw,
 // the first slice (then segment) whose running sum passes theta is found,
 // and only that segment is swept again, one token per lane of a wavefront.
 template <bool kVec, bool kUnitT>
