@@ -53,6 +53,7 @@ constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 // fp32: half the partial traffic in the common case, no range or precision
 // limit in the others
 constexpr float kHalfBound = 4.0f;
+constexpr double kMallBytes = 256.0 * 1024 * 1024;  // the MI355X Infinity Cache
 
 struct AttnArgs {
   const uint16_t *q, *k, *v;
@@ -120,12 +121,22 @@ __device__ inline i32x4 page_rsrc(const uint16_t *base, int64_t pid, int page_el
 // 16-byte-per-lane load from a buffer straight into LDS: lane i's data lands
 // at lds_addr + 16 i. Issued as inline assembly so that the compiler does not
 // serialise the multi-stage pipeline with conservative waits; completion is
-// tracked by the explicit vmcnt waits in the tile loop.
+// tracked by the explicit vmcnt waits in the tile loop. NT marks the load
+// non-temporal (streamed, not kept in the caches): the form for calls whose
+// K/V stream is larger than the 256 MB Infinity Cache, where nothing it would
+// keep survives to the next call anyway.
+template <bool NT>
 __device__ inline void dma16(uint32_t lds_addr, int voff, i32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
 }
 
 template <int N>
@@ -155,7 +166,7 @@ __device__ inline uint32_t lds_addr_of(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
 }
 
-template <int D, int NW, int STAGES, bool FLAT, bool KSPLIT>
+template <int D, int NW, int STAGES, bool FLAT, bool KSPLIT, bool NT>
 __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 16;             // 16-wide d steps of S^T = K Q^T
   constexpr int DB = D / 32;             // 32-wide d blocks of O^T
@@ -345,12 +356,12 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
       if constexpr (FLAT) {
         int voff = it.poff[p] + dma_off[q];
         if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = static_cast<int>(0x80000000u);
-        dma16(dst0 + q * 1024, voff, pool_rsrc[it.part]);
+        dma16<NT>(dst0 + q * 1024, voff, pool_rsrc[it.part]);
       } else {
         const bool ok = it.poff[p] >= 0;
         int voff = dma_off[q];
         if (!full && tile0 + row0 + q * RPI + lane_row >= T) voff = 0x7FFFFFF0;
-        dma16(dst0 + q * 1024, voff,
+        dma16<NT>(dst0 + q * 1024, voff,
               page_rsrc(it.part ? a.v : a.k, ok ? it.poff[p] : 0, page_elems, ok ? page_bytes : 0));
       }
     }
@@ -878,24 +889,25 @@ __global__ void __launch_bounds__(kOrderThreads) order_units_kernel(const int32_
 
 constexpr int kStages = 4;
 
-template <int D, bool FLAT>
+template <int D, bool FLAT, bool NT>
 void launch_w(int qb, bool ksplit, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
   if (ksplit)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT, true, NT>), grid, block, 0, st, a);
   else if (qb == 8)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 8, kStages, FLAT, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 8, kStages, FLAT, false, NT>), grid, block, 0, st, a);
   else if (qb == 4)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 4, kStages, FLAT, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 4, kStages, FLAT, false, NT>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 2, kStages, FLAT, false, NT>), grid, block, 0, st, a);
 }
 
 template <int D>
-void launch_dw(int qb, bool ksplit, bool flat, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
+void launch_dw(int qb, bool ksplit, bool flat, bool nt, dim3 grid, dim3 block, hipStream_t st, const AttnArgs &a) {
   if (flat)
-    launch_w<D, true>(qb, ksplit, grid, block, st, a);
+    nt ? launch_w<D, true, true>(qb, ksplit, grid, block, st, a) : launch_w<D, true, false>(qb, ksplit, grid, block, st, a);
   else
-    launch_w<D, false>(qb, ksplit, grid, block, st, a);
+    nt ? launch_w<D, false, true>(qb, ksplit, grid, block, st, a)
+       : launch_w<D, false, false>(qb, ksplit, grid, block, st, a);
 }
 
 }  // namespace
@@ -931,6 +943,10 @@ AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int 
   // many one-workgroup units (the key-split shape: short rows, many
   // sequences) whose prefix lengths may differ: dispatch the longest first
   p.order = (p.ksplit && p.S == 1 && base > cu_count) ? 1 : 0;
+  // K/V loads marked non-temporal when the call's K/V stream (at the longest
+  // prefix) exceeds the 256 MB Infinity Cache
+  const double kv_bytes = static_cast<double>(B) * Hkv * (static_cast<double>(max_prefix_len) + N) * D * 2.0 * 2.0;
+  p.nt = kv_bytes > kMallBytes ? 1 : 0;
   if (p.order) p.ws_bytes = static_cast<size_t>(B) * Hkv * sizeof(int32_t);
   return p;
 }
@@ -989,9 +1005,9 @@ tv_status launch_attention(tv_ctx *ctx, const AttnPlan &plan, const void *q, con
   // then fit the 32-bit VGPR offset with room for the out-of-range marker)
   const bool flat = num_pages * static_cast<int64_t>(Hkv) * kPage * D * 2 <= 0x7FFF0000LL;
   if (D == 128)
-    launch_dw<128>(plan.qb, plan.ksplit, flat, grid, block, ctx->stream, a);
+    launch_dw<128>(plan.qb, plan.ksplit, flat, plan.nt, grid, block, ctx->stream, a);
   else
-    launch_dw<64>(plan.qb, plan.ksplit, flat, grid, block, ctx->stream, a);
+    launch_dw<64>(plan.qb, plan.ksplit, flat, plan.nt, grid, block, ctx->stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (plan.S > 1) {
     const int rows_per_wg = 4 * (64 / (D / 8));  // four wavefronts, 64*8/D rows each

@@ -79,6 +79,7 @@ struct AttnPlan {
   int row_block;    // query rows (node, head-in-group) per workgroup
   int row_blocks;   // ceil(G*N / row_block)
   int order;        // 1: workgroups take (sequence, KV head) units longest first (order in the workspace)
+  int nt;           // 1: K/V loads non-temporal (the K/V stream exceeds the Infinity Cache)
   size_t ws_bytes;  // fp32 partials + (m, l), or the unit order
 };
 AttnPlan plan_attention(int cu_count, int B, int N, int Hq, int Hkv, int D, int max_prefix_len);
