@@ -185,7 +185,8 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   // swizzled chunk positions (see swz), conflict-free without padding
   __shared__ __align__(1024) uint8_t smem[STAGES][2][TILE_BYTES];
   __shared__ int s_bad;
-  __shared__ int s_pid[kMaxChunkTiles * (kKeys / kPage)];  // page ids of this split's tiles
+  // this split's pages: their byte offsets in the pool (FLAT) or their ids
+  __shared__ int s_pid[kMaxChunkTiles * (kKeys / kPage)];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so DMA operands stay scalar
@@ -307,15 +308,16 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     pool_rsrc[0] = page_rsrc(a.k, 0, 0, pool_bytes);
     pool_rsrc[1] = page_rsrc(a.v, 0, 0, pool_bytes);
   }
-  // page ids of tile j for this wavefront, read from LDS (the value is
-  // uniform; it is read ahead of the issue so that the LDS latency is hidden)
+  // page entries (byte offsets or ids) of tile j for this wavefront, read
+  // from LDS (the value is uniform; it is read ahead of the issue so that
+  // the LDS latency is hidden)
   auto fetch = [&](int j, int (&pid)[PPW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < PPW; ++p) pid[p] = s_pid[j * (kKeys / kPage) + (w * IPW * RPI) / kPage + p];
   };
   // A DMA item (tile j, part) is issued in three steps: fetch (LDS read of its
-  // page ids, placed before a barrier so that its latency is hidden), resolve
-  // (page ids to wave-uniform page offsets, right after the barrier, when no
+  // page entries, placed before a barrier so that its latency is hidden),
+  // resolve (to wave-uniform page offsets, right after the barrier, when no
   // other LDS read is outstanding, so the wait for the read is free) and
   // issue_range (the DMA instructions, spread over the phase; no waits).
   struct DmaItem {
@@ -332,12 +334,13 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int p = 0; p < PPW; ++p) {
         const int pid = __builtin_amdgcn_readfirstlane(pidv[p]);
-        const bool ok = static_cast<uint32_t>(pid) < npages32;
-        if (part == 0) load_bad |= (tile0 + w * IPW * RPI + p * kPage < T) && !ok;
-        if constexpr (FLAT)
-          it.poff[p] = ok ? pid * page_bytes : static_cast<int>(0x80000000u);
-        else
+        if constexpr (FLAT) {
+          it.poff[p] = pid;  // already the byte offset (bad pages were found in the prologue)
+        } else {
+          const bool ok = static_cast<uint32_t>(pid) < npages32;
+          if (part == 0) load_bad |= (tile0 + w * IPW * RPI + p * kPage < T) && !ok;
           it.poff[p] = ok ? pid : -1;
+        }
       }
     }
     return it;
@@ -349,6 +352,16 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     const int row0 = w * IPW * RPI;  // first key row of this wavefront's instructions
     const bool full = tile0 + row0 + IPW * RPI <= T;
     const uint32_t dst0 = smem_base + ((it.j % STAGES) * 2 + it.part) * TILE_BYTES + w * IPW * 1024;
+    if constexpr (FLAT) {
+      if (full) {  // every key row of this wavefront's share is inside the sequence
+#pragma unroll
+        for (int q = 0; q < IPW; ++q) {
+          if (q < q0 || q >= q1) continue;
+          dma16<NT>(dst0 + q * 1024, it.poff[q * PPW / IPW] + dma_off[q], pool_rsrc[it.part]);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int q = 0; q < IPW; ++q) {
       if (q < q0 || q >= q1) continue;
@@ -372,17 +385,35 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
     issue_range(resolve(j, part, true, pid), 0, IPW);
   };
 
-  // page ids of this split's tiles, copied once into LDS so that the DMA issue
-  // path never waits on a memory round trip (-1 past the sequence's pages)
+  // this split's pages, copied once into LDS so that the DMA issue path never
+  // waits on a memory round trip: with one resource per pool as byte offsets
+  // (past the resource for a page past the sequence's end or outside the
+  // pool), and the workgroup learns here whether the sequence has a bad page;
+  // otherwise as page ids (-1 past the sequence's end)
   {
     const int p0 = t_begin * (kKeys / kPage);
     const int used = min(t_end * (kKeys / kPage), (T + kPage - 1) / kPage) - p0;
+    int bad_here = 0;
 #pragma unroll
     for (int e = 0; e < kPidPerThread; ++e) {
       const int i = tid + e * 64 * NW;
-      if (i < ntiles * (kKeys / kPage)) s_pid[i] = i < used ? pid_in[e] : -1;
+      if (i < ntiles * (kKeys / kPage)) {
+        if constexpr (FLAT) {
+          // the page's byte offset in the pool, or an offset past the pool's
+          // resource (loads of zeros) for a page outside the pool or past the
+          // sequence; a page inside the sequence that is not in the pool is bad
+          const bool ok = static_cast<uint32_t>(pid_in[e]) < npages32;
+          bad_here |= i < used && !ok;
+          s_pid[i] = i < used && ok ? pid_in[e] * page_bytes : static_cast<int>(0x80000000u);
+        } else {
+          s_pid[i] = i < used ? pid_in[e] : -1;
+        }
+      }
     }
-    __syncthreads();
+    if constexpr (FLAT)
+      load_bad = __syncthreads_or(bad_here) != 0;
+    else
+      __syncthreads();
   }
 
   // per-lane LDS byte offsets of the fragment reads (swizzled chunk positions)
@@ -663,6 +694,10 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   // DMA instructions of this wavefront issued after its group holding K_j
   // and V_{j-1} (what half-step 2j+1 needs) and before that half-step
   auto wait_for = [&](int j) __attribute__((always_inline)) {
+    if (j >= 0 && j + 2 < n_t) {  // every group of the last two iterations is in flight
+      wait_vmcnt<4 * IPW>();
+      return;
+    }
     switch ((parts(j + 1) + parts(j) + parts(j + 2) + parts(j + 1)) / IPW) {
       case 0: wait_vmcnt<0>(); break;
       case 1: wait_vmcnt<IPW>(); break;
