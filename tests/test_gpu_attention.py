@@ -326,6 +326,42 @@ def test_bad_page_variants(case):
     assert np.isfinite(out[0]).all()
 
 
+@pytest.mark.parametrize("case", ["ping-pong", "key-split", "splits"])
+def test_entries_past_each_sequence_are_ignored(case):
+    # page-table entries past a sequence's last page (L_b + N keys) are never
+    # read: filling them with ids outside the pool, negative ids or the
+    # largest int changes neither the status nor a bit of the output, in the
+    # ping-pong template, the key-split template and a plan with key splits
+    if case == "ping-pong":
+        w = small("random", N=40, L=(100, 400), B=3, seed=11)
+    elif case == "key-split":
+        w = small("random", N=5, Hq=4, Hkv=1, L=(30, 700), B=3, seed=12)
+    else:
+        w = small("random", N=20, L=(1500, 3000), B=2, seed=13)
+    dw = DevWorkload(w, logits=False)
+    mask = tv.tv_build_mask(dw.parents)[0]
+    clean = host(dw.attention(mask))
+    assert tv.tv_device_error(DEV) == 0
+    junk = w.page_table.copy()
+    fills = np.array([w.num_pages + 1000, -7, 2**31 - 1], np.int64)
+    planted = 0
+    for b in range(w.B):
+        used = (int(w.prefix_lens[b]) + w.N + 15) // 16
+        n = junk.shape[1] - used
+        junk[b, used:] = np.resize(fills, n).astype(np.int32)
+        planted += n
+    assert planted > 0
+    st, _ = oracle.status_attention(w.q, w.k_pages, w.v_pages, junk, w.prefix_lens, None, B=w.B, N=w.N, Hq=w.Hq,
+                                    Hkv=w.Hkv, D=w.D, sm_scale=w.sm_scale)
+    assert st == oracle.OK
+    print(f"[attention] entries past each sequence, {case}: {planted} planted, prefix lengths "
+          f"{w.prefix_lens.tolist()}", flush=True)
+    dw.page_table = dev(junk)
+    got = host(dw.attention(mask))
+    assert tv.tv_device_error(DEV) == 0
+    assert np.array_equal(got, clean), "entries past the sequence changed the output"
+
+
 def test_split_partials_wide_rows():
     # a split plan (several key splits per sequence) where the KV head 1's
     # values are scaled by 64 (exact in bf16): its rows' partials O/l exceed
