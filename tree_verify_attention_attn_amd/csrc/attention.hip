@@ -119,7 +119,8 @@ __device__ inline i32x4 page_rsrc(const uint16_t *base, int64_t pid, int page_el
 }
 
 // 16-byte-per-lane load from a buffer straight into LDS: lane i's data lands
-// at lds_addr + 16 i. Issued as inline assembly so that the compiler does not
+// at lds_addr + 16 i (the LDS address goes in M0, which the compiler sets
+// from the operand). Issued as inline assembly so that the compiler does not
 // serialise the multi-stage pipeline with conservative waits; completion is
 // tracked by the explicit vmcnt waits in the tile loop. NT marks the load
 // non-temporal (streamed, not kept in the caches): the form for calls whose
@@ -128,15 +129,9 @@ __device__ inline i32x4 page_rsrc(const uint16_t *base, int64_t pid, int page_el
 template <bool NT>
 __device__ inline void dma16(uint32_t lds_addr, int voff, i32x4 rsrc) {
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-                 :
-                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
 template <int N>
@@ -174,7 +169,6 @@ __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu
   constexpr int CPR = D / 8;             // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;          // key rows per 1 KB DMA instruction
   constexpr int IPW = CPR / NW;          // K (and V) DMA instructions per wavefront per tile
-  constexpr int DPW = 2 * IPW;           // DMA instructions per wavefront per tile
   constexpr int TILE_BYTES = kKeys * RB; // one K (or V) tile
   constexpr int ROWS_WG = KSPLIT ? 32 : 32 * NW;  // key split: every wavefront holds the same 32 rows
   constexpr int WROW = KSPLIT ? 0 : 32;          // row offset between wavefronts
