@@ -251,7 +251,7 @@ __device__ void greedy_path_seq(int b, int lane, unsigned long long *keys, int c
   unsigned long long khi = 0ull, klo = 0ull;  // key = (brev(word 0), brev(word 1))
 #pragma unroll
   for (int k = 0; k < H; ++k)
-    if (ok[k] && __popcll(a0[k]) + __popcll(a1[k]) == dmax) {
+    if (ok[k] && static_cast<int>(__popcll(a0[k]) + __popcll(a1[k])) == dmax) {
       const unsigned long long h = __brevll(a0[k]), l = __brevll(a1[k]);
       if (h > khi || (h == khi && l > klo)) {
         khi = h;
