@@ -1,0 +1,56 @@
+"""GPU parity on seeded random shapes: tv_attention compared in full with the
+fp64 oracle, over combinations the fixed cases do not pair up (head dim 64 or
+128, KV heads 1-4, GQA group 1-8, 1-128 tree nodes, prefix ranges from empty
+to about 1,600 keys, random / chain / star / forest trees, batch 1-4), each
+with and without per-sequence node counts.
+
+The shapes come from a fixed seed, so every run checks the same cases; a
+failure message names the shape.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tvgen
+import tree_verify_attention_attn_amd as tv
+from gpu_util import DEV, DevWorkload, check_attention, dev, host
+
+pytestmark = pytest.mark.gpu
+
+NCASES = 24
+
+
+def shape(i):
+    r = np.random.default_rng(4200 + i)
+    Hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4, 8]))
+    lo = int(r.integers(0, 1200))
+    return dict(B=int(r.integers(1, 5)), Hq=Hkv * G, Hkv=Hkv, D=int(r.choice([64, 128])),
+                L=(lo, lo + int(r.integers(0, 400))), N=int(r.integers(1, 129)),
+                tree=str(r.choice(["random", "chain", "star", "forest"])), max_depth=int(r.integers(1, 10)),
+                pages="permuted")
+
+
+@pytest.mark.parametrize("sized", [False, True], ids=["all-nodes", "node-counts"])
+@pytest.mark.parametrize("i", range(NCASES))
+def test_attention_random_shape(i, sized):
+    sh = shape(i)
+    w = tvgen.make_workload(1, seed=5000 + i, with_logits=False, overrides=sh)
+    sizes = None
+    if sized:  # each sequence's node count, uniform in [1, N]
+        sizes = np.random.default_rng(6000 + i).integers(1, w.N + 1, size=w.B).astype(np.int32)
+    what = (f"case {i}: B{w.B} Hq{w.Hq}/Hkv{w.Hkv} D{w.D} N{w.N} tree={sh['tree']} "
+            f"prefix lengths {w.prefix_lens.tolist()} node counts {None if sizes is None else sizes.tolist()}")
+    print(f"[random shapes] {what}", flush=True)
+    dw = DevWorkload(w, logits=False)
+    mask, _ = tv.tv_build_mask(dw.parents, tree_sizes=None if sizes is None else dev(sizes))
+    out = host(tv.tv_attention(dw.q, dw.k, dw.v, dw.page_table, dw.prefix_lens, w.max_prefix_len, mask,
+                               float(w.sm_scale), tree_sizes=None if sizes is None else dev(sizes)))
+    assert tv.tv_device_error(DEV) == 0
+    ref = oracle.attention(w, oracle.build_mask(w.parents, tree_sizes=sizes)[0], tree_sizes=sizes)
+    if sizes is None:
+        check_attention(out, ref, what=what)
+    else:  # only present nodes have outputs
+        for b in range(w.B):
+            n = int(sizes[b])
+            check_attention(out[b, :n], ref[b, :n], what=f"{what}, sequence {b}")
