@@ -2,6 +2,8 @@
 import numpy as np
 import torch
 
+import oracle
+
 import tree_verify_attention_attn_amd as tv
 
 DEV = torch.device("cuda:0")
@@ -74,3 +76,25 @@ def check_attention(got, ref, tight=None, what=""):
     if tight is not None:
         assert err.max() <= tight, f"{what}: max abs err {err.max():.3e} above the {tight} guard"
     return dict(max_abs=float(err.max()), max_rel=max_rel, pass_frac=float(ok.mean()))
+
+
+def stochastic_compare(w, what, T=None):
+    """Sampled acceptance on the GPU against the oracle: bit-exact paths,
+    accepted lengths and bonus tokens, with no decision near a coin flip."""
+    T = w.temperature if T is None else T
+    dw = DevWorkload(w, kv=False)
+    got = dw.accept(tv.STOCHASTIC)
+    assert tv.tv_device_error(DEV) == 0, what
+    ref = oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms, T)
+    m = ref["margins"]
+    near = (m <= 1e-9).any(1)
+    print(f"[accept] {what}: B={w.B} N={w.N} V={w.V} min margin {m.min():.3e}, near-tie sequences "
+          f"{int(near.sum())}, accept_len histogram {np.bincount(ref['accept_len']).tolist()}", flush=True)
+    # every decision of the seeded inputs is far from a coin flip, so any
+    # difference is a bug, not rounding
+    assert int(near.sum()) == 0, f"{what}: sequences with a decision margin <= 1e-9: {np.argwhere(near)[:5, 0]}"
+    for k in ("accept_len", "path", "bonus"):
+        g = host(got[k])
+        bad = np.argwhere((g != ref[k]).reshape(w.B, -1).any(1))
+        assert bad.size == 0, f"{what}: {k} differs for sequences {bad[:5, 0].tolist()}"
+    return ref

@@ -11,7 +11,7 @@ import pytest
 import oracle
 import tvgen
 import tree_verify_attention_attn_amd as tv
-from gpu_util import DEV, DevWorkload, dev, host
+from gpu_util import DEV, DevWorkload, dev, host, stochastic_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -221,26 +221,6 @@ def test_stochastic_variants(variant):
         assert (host(got[k]) == ref[k]).all(), k
     if variant == "p-equals-q":
         assert (ref["accept_len"] == w.N).all()
-
-
-def stochastic_compare(w, what, T=None):
-    T = w.temperature if T is None else T
-    dw = DevWorkload(w, kv=False)
-    got = dw.accept(tv.STOCHASTIC)
-    assert tv.tv_device_error(DEV) == 0, what
-    ref = oracle.accept_stochastic(w.target_logits, w.draft_logits, w.draft_tokens, w.parents, w.uniforms, T)
-    m = ref["margins"]
-    near = (m <= 1e-9).any(1)
-    print(f"[accept] {what}: B={w.B} N={w.N} V={w.V} min margin {m.min():.3e}, near-tie sequences "
-          f"{int(near.sum())}, accept_len histogram {np.bincount(ref['accept_len']).tolist()}", flush=True)
-    # every decision of the seeded inputs is far from a coin flip, so any
-    # difference is a bug, not rounding
-    assert int(near.sum()) == 0, f"{what}: sequences with a decision margin <= 1e-9: {np.argwhere(near)[:5, 0]}"
-    for k in ("accept_len", "path", "bonus"):
-        g = host(got[k])
-        bad = np.argwhere((g != ref[k]).reshape(w.B, -1).any(1))
-        assert bad.size == 0, f"{what}: {k} differs for sequences {bad[:5, 0].tolist()}"
-    return ref
 
 
 def test_stochastic_tree_full_size():

@@ -2,7 +2,9 @@
 fp64 oracle, over combinations the fixed cases do not pair up (head dim 64 or
 128, KV heads 1-4, GQA group 1-8, 1-128 tree nodes, prefix ranges from empty
 to about 1,600 keys, random / chain / star / forest trees, batch 1-4), each
-with and without per-sequence node counts.
+with and without per-sequence node counts; and sampled acceptance, bit-exact
+against the oracle, over random batch, node count, vocabulary size (and so
+the number of workgroups per sequence), tree kind and temperature.
 
 The shapes come from a fixed seed, so every run checks the same cases; a
 failure message names the shape.
@@ -13,7 +15,7 @@ import pytest
 import oracle
 import tvgen
 import tree_verify_attention_attn_amd as tv
-from gpu_util import DEV, DevWorkload, check_attention, dev, host
+from gpu_util import DEV, DevWorkload, check_attention, dev, host, stochastic_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -54,3 +56,28 @@ def test_attention_random_shape(i, sized):
         for b in range(w.B):
             n = int(sizes[b])
             check_attention(out[b, :n], ref[b, :n], what=f"{what}, sequence {b}")
+
+
+def stochastic_shape(i):
+    r = np.random.default_rng(7300 + i)
+    tree = str(r.choice(["random", "dynamic", "star", "chain", "forest"]))
+    sh = dict(B=int(r.integers(1, 41)), N=int(r.integers(2, 65)), V=int(r.integers(500, 70001)), tree=tree,
+              mode="stochastic", T=float(r.choice([0.6, 1.0, 1.7])))
+    if tree in ("random", "dynamic"):
+        sh.update(max_depth=int(r.integers(2, 9)), topk=int(r.integers(2, 11)))
+    return sh
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_stochastic_random_shape(i):
+    sh = stochastic_shape(i)
+    w = tvgen.make_workload(2, seed=8000 + i, with_kv=False, overrides=sh)
+    # draft rows near their parent's target row for every other sequence
+    # (long accepted paths), the others drawn apart (many rejected siblings)
+    near = tvgen.normal_f32(8000 + i, 95, w.draft_logits.shape, sigma=0.3)
+    for b in range(0, w.B, 2):
+        for c in range(1, w.N):
+            pr = w.parents[b, c]
+            if pr >= 0:
+                w.draft_logits[b, c] = w.target_logits[b, pr] + near[b, c]
+    stochastic_compare(w, f"case {i}: {sh}")
