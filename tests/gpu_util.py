@@ -98,3 +98,18 @@ def stochastic_compare(w, what, T=None):
         bad = np.argwhere((g != ref[k]).reshape(w.B, -1).any(1))
         assert bad.size == 0, f"{what}: {k} differs for sequences {bad[:5, 0].tolist()}"
     return ref
+
+
+KEYS = ("accept_len", "path", "bonus", "target_argmax")
+
+
+def greedy_compare(w, what):
+    """Greedy acceptance on the GPU against the oracle, bit-exact."""
+    dw = DevWorkload(w, kv=False)
+    got = dw.accept(tv.GREEDY)
+    assert tv.tv_device_error(DEV) == 0
+    ref = oracle.accept_greedy(w.target_logits, w.draft_tokens, w.parents)
+    for k in KEYS:
+        g = host(got[k])
+        assert (g == ref[k]).all(), f"{what}: {k} differs at {np.argwhere(g != ref[k])[:5].tolist()}"
+    return ref

@@ -11,22 +11,10 @@ import pytest
 import oracle
 import tvgen
 import tree_verify_attention_attn_amd as tv
-from gpu_util import DEV, DevWorkload, dev, host, stochastic_compare
+from gpu_util import DEV, KEYS, DevWorkload, dev, greedy_compare, host, stochastic_compare
 
 pytestmark = pytest.mark.gpu
 
-KEYS = ("accept_len", "path", "bonus", "target_argmax")
-
-
-def greedy_compare(w, what):
-    dw = DevWorkload(w, kv=False)
-    got = dw.accept(tv.GREEDY)
-    assert tv.tv_device_error(DEV) == 0
-    ref = oracle.accept_greedy(w.target_logits, w.draft_tokens, w.parents)
-    for k in KEYS:
-        g = host(got[k])
-        assert (g == ref[k]).all(), f"{what}: {k} differs at {np.argwhere(g != ref[k])[:5].tolist()}"
-    return ref
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])

@@ -2,7 +2,9 @@
 fp64 oracle, over combinations the fixed cases do not pair up (head dim 64 or
 128, KV heads 1-4, GQA group 1-8, 1-128 tree nodes, prefix ranges from empty
 to about 1,600 keys, random / chain / star / forest trees, batch 1-4), each
-with and without per-sequence node counts; and sampled acceptance, bit-exact
+with and without per-sequence node counts; greedy acceptance, bit-exact, over
+random batch, 1-128 nodes, vocabulary size and planted matches (so both the
+one-launch and the two-pass form); and sampled acceptance, bit-exact
 against the oracle, over random batch, node count, vocabulary size (and so
 the number of workgroups per sequence), tree kind and temperature.
 
@@ -15,7 +17,7 @@ import pytest
 import oracle
 import tvgen
 import tree_verify_attention_attn_amd as tv
-from gpu_util import DEV, DevWorkload, check_attention, dev, host, stochastic_compare
+from gpu_util import DEV, DevWorkload, check_attention, dev, greedy_compare, host, stochastic_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +83,20 @@ def test_stochastic_random_shape(i):
             if pr >= 0:
                 w.draft_logits[b, c] = w.target_logits[b, pr] + near[b, c]
     stochastic_compare(w, f"case {i}: {sh}")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_greedy_random_shape(i):
+    r = np.random.default_rng(9100 + i)
+    tree = str(r.choice(["random", "star", "chain", "forest"]))
+    if i % 2 == 0:  # at most 256 workgroups (B * N <= 128, V <= 16384): the one-launch form
+        N = int(r.integers(1, 65))
+        B = int(r.integers(1, 128 // N + 1))
+        V = int(r.integers(2, 16385))
+    else:  # the argmax pass and the path pass, at most 120 MB of logits
+        B, N = int(r.integers(1, 65)), int(r.integers(1, 129))
+        V = min(int(r.integers(2, 200001)), max(2, 30_000_000 // (B * N)))
+    sh = dict(B=B, N=N, V=V, tree=tree, max_depth=int(r.integers(1, 10)))
+    w = tvgen.make_workload(1, seed=9000 + i, with_kv=False, overrides=sh)
+    tvgen.plant_random(w, float(r.choice([0.0, 0.5, 0.9])), seed=9000 + i)
+    greedy_compare(w, f"case {i}: {sh}")
