@@ -243,9 +243,10 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  *   from max(0, p - q) at the rejection (p if its mass is 0), or from
  *   p_{N-1} when every draft is accepted.
  * Adds sum(accept_len) and B to the context's tau counters. Requires
- * 1 <= N <= 128 when B > 0, V >= 1, and B * N * ceil(V / 8192) <= 2^24 - 1
- * (one 256-thread workgroup per row and 8192-token chunk on a 1-D grid);
- * larger calls return TV_ERR_UNSUPPORTED.
+ * 1 <= N <= 128 when B > 0, V >= 1, and B * N * ceil(V / C) <= 2^24 - 1
+ * with C = 16384 in GREEDY mode and 8192 in STOCHASTIC mode (one 256-thread
+ * workgroup per row and C-token chunk on a 1-D grid); larger calls return
+ * TV_ERR_UNSUPPORTED.
  * In STOCHASTIC mode a small batch splits each sequence's vocabulary over
  * several workgroups that exchange partial sums and wait for each other
  * (bounded); the grid fits the device when nothing else runs on it. Two

@@ -60,10 +60,10 @@ def test_greedy_large_batch():
     greedy_compare(w, "B70000")
 
 
-@pytest.mark.parametrize("B,N,V", [(128, 2, 8), (129, 2, 8), (2, 128, 8192), (2, 128, 8193), (1, 15, 1024),
-                                   (3, 64, 24577)])
+@pytest.mark.parametrize("B,N,V", [(128, 2, 8), (129, 2, 8), (2, 128, 8193), (2, 128, 16384), (2, 128, 16385),
+                                   (1, 15, 1024), (3, 64, 24577)])
 def test_greedy_one_launch_limit(B, N, V):
-    # with at most 256 argmax workgroups (rows x 8192-token chunks), the
+    # with at most 256 argmax workgroups (rows x 16384-token chunks), the
     # argmax pass's last workgroup of each sequence runs the path logic (one
     # launch); above, the path pass runs on its own
     w = tvgen.make_workload(1, seed=B + N + V, with_kv=False,
@@ -119,7 +119,7 @@ def test_calls_on_two_streams_are_ordered():
 
 
 def test_greedy_grid_limit_is_reported():
-    # one workgroup per (row, 8192-token chunk) on a 1-D grid of at most
+    # one workgroup per (row, 16384-token chunk) on a 1-D grid of at most
     # 2^32 - 1 work-items: larger calls are refused before any launch
     w = tvgen.make_workload(1, with_kv=False, overrides=dict(B=2, N=4, V=16))
     dw = DevWorkload(w, kv=False)
@@ -128,6 +128,16 @@ def test_greedy_grid_limit_is_reported():
     ws = dev(np.zeros(64, np.uint8))
     st = lib.tv_accept(tv._ctx(DEV), p(dw.target_logits), None, p(dw.draft_tokens), p(dw.parents), None, None,
                        1 << 20, 128, 128256, tv.GREEDY, 1.0, p(out[0]), p(out[1]), p(out[2]), p(out[3]), p(ws), 64)
+    assert st == tv.UNSUPPORTED
+    # 2^24 - 1 rows of 16384 tokens: one greedy chunk per row fits the grid
+    # (the call then stops at the too-small workspace), two stochastic chunks
+    # per row do not
+    rows, V = (1 << 24) - 1, 16384
+    st = lib.tv_accept(tv._ctx(DEV), p(dw.target_logits), None, p(dw.draft_tokens), p(dw.parents), None, None,
+                       rows, 1, V, tv.GREEDY, 1.0, p(out[0]), p(out[1]), p(out[2]), p(out[3]), p(ws), 64)
+    assert st == tv.WORKSPACE
+    st = lib.tv_accept(tv._ctx(DEV), p(dw.target_logits), p(dw.target_logits), p(dw.draft_tokens), p(dw.parents),
+                       None, p(ws), rows, 1, V, tv.STOCHASTIC, 1.0, p(out[0]), p(out[1]), p(out[2]), None, p(ws), 64)
     assert st == tv.UNSUPPORTED
 
 

@@ -89,10 +89,10 @@ def test_stochastic_random_shape(i):
 def test_greedy_random_shape(i):
     r = np.random.default_rng(9100 + i)
     tree = str(r.choice(["random", "star", "chain", "forest"]))
-    if i % 2 == 0:  # at most 256 workgroups (B * N <= 128, V <= 16384): the one-launch form
+    if i % 2 == 0:  # at most 256 workgroups (B * N <= 128, V <= 32768): the one-launch form
         N = int(r.integers(1, 65))
         B = int(r.integers(1, 128 // N + 1))
-        V = int(r.integers(2, 16385))
+        V = int(r.integers(2, 32769))
     else:  # the argmax pass and the path pass, at most 120 MB of logits
         B, N = int(r.integers(1, 65)), int(r.integers(1, 129))
         V = min(int(r.integers(2, 200001)), max(2, 30_000_000 // (B * N)))

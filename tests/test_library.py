@@ -31,8 +31,9 @@ def test_status_strings_and_host_queries():
     lib = tv.library()
     for s in range(6):
         assert lib.tv_status_string(s)
-    # accept workspace: greedy = B*N*chunks 64-bit keys, stochastic = B*N*2*chunks*(m, Z) doubles
-    chunks = (128256 + 8191) // 8192
+    # accept workspace: greedy = B*N*chunks 64-bit keys (16384-token chunks),
+    # stochastic = B*N*2*chunks*(m, Z) doubles (8192-token chunks)
+    chunks = (128256 + 16383) // 16384
     assert tv.tv_accept_workspace_bytes(8, 64, 128256, tv.GREEDY) == 8 * 64 * chunks * 8
     assert tv.tv_accept_workspace_bytes(128, 5, 32000, tv.STOCHASTIC) == \
         (128 * 5 * 2 * 4 * 2 + 128 * 2 * 32000) * 8 + (128 * 16 + 128 * 256 * 4) * 8

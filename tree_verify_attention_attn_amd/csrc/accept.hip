@@ -4,7 +4,7 @@
 // with the draft tokens and keep the longest accepted path; Sonar page, four
 // stages: the logits after the accepted prefix give one more token):
 //   pass 1  vocab-chunked argmax per (sequence, node) row. Each workgroup
-//           reduces a 8192-entry chunk to one packed 64-bit key
+//           reduces a 16384-entry chunk to one packed 64-bit key
 //           (order-preserving float bits << 32 | ~index), so a plain max picks
 //           the largest value and, among equal values, the lowest index.
 //   pass 2  one wavefront per sequence, lane = node: merge the chunk keys,
@@ -41,7 +41,8 @@ namespace tv {
 
 namespace {
 
-constexpr int kChunk = 8192;  // vocab entries per pass-1 workgroup
+constexpr int kChunk = 8192;  // vocab entries per stochastic pass-1 workgroup
+constexpr int kGChunk = 16384;  // vocab entries per greedy argmax workgroup
 constexpr int kMaxFusedGrid = 256;  // pass-1 workgroups up to which both greedy passes are one launch
 constexpr int kThreads = 256;
 
@@ -76,7 +77,7 @@ __device__ inline unsigned long long block_argmax(const float *p, int x0, int x1
     // all of the thread's 16-byte loads are issued before any is used
     // (streaming loads: each logit is read once)
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int kIt = kChunk / (kThreads * 4);
+    constexpr int kIt = kGChunk / (kThreads * 4);
     f32x4 v[kIt];
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
@@ -113,8 +114,8 @@ __global__ void __launch_bounds__(kThreads) argmax_chunk_kernel(const float *__r
   const int chunk = static_cast<int>(blockIdx.x % static_cast<unsigned>(chunks));
   const int64_t row = blockIdx.x / static_cast<unsigned>(chunks);
   if (row % N >= present_nodes(sizes, row / N, N)) return;  // an absent node: its row is never read
-  const int x0 = chunk * kChunk;
-  const unsigned long long best = block_argmax<kVec>(logits + row * V, x0, min(x0 + kChunk, V), red);
+  const int x0 = chunk * kGChunk;
+  const unsigned long long best = block_argmax<kVec>(logits + row * V, x0, min(x0 + kGChunk, V), red);
   if (threadIdx.x == 0) keys[row * chunks + chunk] = best;
 }
 
@@ -331,8 +332,8 @@ __global__ void __launch_bounds__(kThreads) argmax_path_kernel(
   const int b = static_cast<int>(row / N);
   const int present = present_nodes(sizes, b, N);
   if (row % N >= present) return;  // an absent node: its row is never read and it is not counted
-  const int x0 = chunk * kChunk;
-  const unsigned long long best = block_argmax<kVec>(logits + row * V, x0, min(x0 + kChunk, V), red);
+  const int x0 = chunk * kGChunk;
+  const unsigned long long best = block_argmax<kVec>(logits + row * V, x0, min(x0 + kGChunk, V), red);
   if (threadIdx.x == 0) {
     atomicExch(keys + row * chunks + chunk, best);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the key is in place before this workgroup is counted
@@ -1102,9 +1103,8 @@ size_t stats_doubles(int B, int N, int V) {
 }
 
 size_t accept_ws_bytes(int B, int N, int V, tv_accept_mode mode) {
-  const int chunks = (V + kChunk - 1) / kChunk;
-  const size_t rows = static_cast<size_t>(B) * N;
-  if (mode == TV_GREEDY) return rows * chunks * sizeof(unsigned long long);
+  if (mode == TV_GREEDY)
+    return static_cast<size_t>(B) * N * ((V + kGChunk - 1) / kGChunk) * sizeof(unsigned long long);
   const size_t sync = static_cast<size_t>(B) * kCounterStride + static_cast<size_t>(kMaxExchanges) * kMaxGrid * 4;
   return (stats_doubles(B, N, V) + static_cast<size_t>(B) * 2 * V) * sizeof(double) +
          sync * sizeof(unsigned long long);
@@ -1115,11 +1115,11 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
                         const float *uniforms, int B, int N, int V, tv_accept_mode mode, float temperature,
                         int32_t *accept_len, int32_t *path, int32_t *bonus, int32_t *target_argmax,
                         void *workspace) {
-  const int chunks = (V + kChunk - 1) / kChunk;
   const dim3 blk(kThreads);
   const bool vec = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0 &&
                    (draft_logits == nullptr || (reinterpret_cast<uintptr_t>(draft_logits) & 15) == 0);
   if (mode == TV_GREEDY) {
+    const int chunks = (V + kGChunk - 1) / kGChunk;
     auto *keys = static_cast<unsigned long long *>(workspace);
     const dim3 g1(static_cast<unsigned>(static_cast<int64_t>(B) * N * chunks));
     // one launch when the grid is small: the last workgroup of each sequence
@@ -1151,6 +1151,7 @@ tv_status launch_accept(tv_ctx *ctx, const float *target_logits, const float *dr
                          ctx->d_state);
     return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
   }
+  const int chunks = (V + kChunk - 1) / kChunk;
   auto *stats = static_cast<double *>(workspace);
   double *wbuf = stats + stats_doubles(B, N, V);
   auto *sync = reinterpret_cast<unsigned long long *>(wbuf + static_cast<size_t>(B) * 2 * V);

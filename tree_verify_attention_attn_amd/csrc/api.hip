@@ -193,8 +193,10 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
   if (N > 128) return TV_ERR_UNSUPPORTED;
   if (!target_logits || !draft_tokens || !parents || !accept_len || !path || !bonus_token) return TV_ERR_INVALID_ARG;
   if (mode == TV_STOCHASTIC && (!draft_logits || !uniforms)) return TV_ERR_INVALID_ARG;
-  // one workgroup of 256 threads per (row, 8192-token chunk), on a 1-D grid
-  if (static_cast<int64_t>(B) * N * ((static_cast<int64_t>(V) + 8191) / 8192) * 256 > 0xFFFFFFFFLL)
+  // one workgroup of 256 threads per (row, chunk) on a 1-D grid; a chunk is
+  // 16384 tokens for the greedy argmax, 8192 for the stochastic statistics
+  const int64_t chunk = mode == TV_GREEDY ? 16384 : 8192;
+  if (static_cast<int64_t>(B) * N * ((static_cast<int64_t>(V) + chunk - 1) / chunk) * 256 > 0xFFFFFFFFLL)
     return TV_ERR_UNSUPPORTED;
   const size_t need = accept_ws_bytes(B, N, V, mode);
   if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
