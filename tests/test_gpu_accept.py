@@ -190,7 +190,8 @@ def test_stochastic_cfg5_full_size():
         assert (host(got[k]) == ref[k]).all(), k
 
 
-@pytest.mark.parametrize("variant", ["p-equals-q", "small-vocab", "temperature", "odd-vocab"])
+@pytest.mark.parametrize("variant", ["p-equals-q", "small-vocab", "temperature", "odd-vocab", "masked-vocab",
+                                     "masked-vocab-temperature"])
 def test_stochastic_variants(variant):
     over = dict(B=64)
     T = 1.0
@@ -200,12 +201,29 @@ def test_stochastic_variants(variant):
         over.update(V=12345, N=3)
     if variant == "temperature":
         over.update(V=5000)
+    if variant.startswith("masked-vocab"):
+        over.update(V=20000, N=5)
     w = tvgen.make_workload(5, seed=55, with_kv=False, overrides=over)
     if variant == "p-equals-q":
         w.draft_logits[:, 1:] = w.target_logits[:, :-1]
-    if variant == "temperature":
+    if variant in ("temperature", "masked-vocab-temperature"):
         T = 0.7
         w.temperature = T
+    if variant.startswith("masked-vocab"):
+        # every seventh token banned (-inf in both distributions) in every
+        # other sequence, and in the others one token per row far below the
+        # row's maximum, so that its exponential underflows; neither is ever
+        # a drafted token
+        for b in range(w.B):
+            if b % 2 == 0:
+                ban = np.arange(3, w.V, 7)
+                ban = ban[~np.isin(ban, w.draft_tokens[b])]
+                w.target_logits[b][:, ban] = -np.inf
+                w.draft_logits[b][:, ban] = -np.inf
+            else:
+                low = next(x for x in range(11, w.V) if x not in w.draft_tokens[b])
+                w.target_logits[b][:, low] = -1e4
+                w.draft_logits[b][:, low] = -1e4
     dw = DevWorkload(w, kv=False)
     got = dw.accept(tv.STOCHASTIC)
     assert tv.tv_device_error(DEV) == 0

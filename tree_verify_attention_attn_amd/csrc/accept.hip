@@ -414,6 +414,26 @@ __device__ inline double exp_tab(double x, const double *tab) {
   return (e > 0 && x > -745.2) ? tab[ki & 63] * p * two_n : 0.0;
 }
 
+// exp_tab for arguments known to lie in [-707, 0]: 2^n is then a normal
+// number and so is the result, so the range test is left out and 2^n is
+// applied by one ldexp (the same bits as the product with 2^n). NaN in, NaN
+// out.
+__device__ inline double exp_tab_normal(double x, const double *tab) {
+  constexpr double kShift = 6755399441055744.0;  // 1.5 * 2^52
+  const double ks = fma(x, kLog2eD * 64.0, kShift);
+  const double k = ks - kShift;
+  const int ki = static_cast<int>(__double_as_longlong(ks));
+  double r = fma(-k, kLn2Hi / 64.0, x);
+  r = fma(-k, kLn2Lo / 64.0, r);
+  double p = 1.0 / 120.0;
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(tab[ki & 63] * p, ki >> 6);
+}
+
 // x / T in fp64 from a precomputed 1/T and one FMA correction step (exact
 // when T = 1)
 __device__ inline double div_t(double x, double T, double invT) {
@@ -469,9 +489,12 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
   }
   // x -> x / T is monotonic, so the maximum of the scaled logits is the
   // scaled maximum logit (found in fp32)
-  float mf = -INFINITY;
+  float mf = -INFINITY, mnf = INFINITY;
 #pragma unroll
-  for (int it = 0; it < kPer; ++it) mf = fmaxf(mf, v[it]);
+  for (int it = 0; it < kPer; ++it) {
+    mf = fmaxf(mf, v[it]);
+    mnf = fminf(mnf, v[it]);
+  }
   for (int m = 32; m >= 1; m >>= 1) mf = fmaxf(mf, __shfl_xor(mf, m));
   __shared__ float redf[kThreads / 64];
   __shared__ double s_tab[64];
@@ -481,13 +504,32 @@ __global__ void __launch_bounds__(kThreads) softmax_chunk_kernel(const float *__
   mf = redf[0];
   for (int i = 1; i < kThreads / 64; ++i) mf = fmaxf(mf, redf[i]);
   const double mx = div_t(mf, T, invT);
+  // every argument of this thread at or above -707 (padding, infinities and
+  // far-below values fail; NaN, which fminf skips, makes the sum NaN): no
+  // range test. Taken per wavefront, and redone with the test by a thread
+  // whose sum is not finite, so every term is what exp_tab gives.
+  const bool normal = div_t(mnf, T, invT) - mx >= -707.0;
   double zs = 0.0;
-  if (T == 1.0) {  // x / 1 = x exactly
+  if (__all(normal)) {
+    if (T == 1.0) {
 #pragma unroll 8
-    for (int it = 0; it < kPer; ++it) zs += exp_tab(static_cast<double>(v[it]) - mx, s_tab);
+      for (int it = 0; it < kPer; ++it) zs += exp_tab_normal(static_cast<double>(v[it]) - mx, s_tab);
+    } else {
+#pragma unroll 8
+      for (int it = 0; it < kPer; ++it) zs += exp_tab_normal(div_t(v[it], T, invT) - mx, s_tab);
+    }
   } else {
+    zs = NAN;
+  }
+  if (!(zs <= 1e300)) {
+    zs = 0.0;
+    if (T == 1.0) {  // x / 1 = x exactly
 #pragma unroll 8
-    for (int it = 0; it < kPer; ++it) zs += exp_tab(div_t(v[it], T, invT) - mx, s_tab);  // -inf (padding) gives 0
+      for (int it = 0; it < kPer; ++it) zs += exp_tab(static_cast<double>(v[it]) - mx, s_tab);
+    } else {
+#pragma unroll 8
+      for (int it = 0; it < kPer; ++it) zs += exp_tab(div_t(v[it], T, invT) - mx, s_tab);  // -inf (padding) gives 0
+    }
   }
   for (int m = 32; m >= 1; m >>= 1) zs += __shfl_xor(zs, m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = zs;
