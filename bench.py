@@ -459,11 +459,12 @@ class Setup:
     def mask_cost(self):
         """tv_attention with the tree mask against the same call with
         tree_mask = NULL (every tree key visible), interleaved in blocks of 20
-        calls so that clock drift affects both alike; medians of 5 blocks."""
+        calls, the order of the two blocks alternating from round to round so
+        that clock drift and position affect both alike; medians of 6 blocks."""
         masked, unmasked = [], []
-        for _ in range(5):
-            masked.append(block_us(self.torch, lambda: self.attention("tree"), 20))
-            unmasked.append(block_us(self.torch, lambda: self.attention(None), 20))
+        for r in range(6):
+            for m in (("tree", None) if r % 2 == 0 else (None, "tree")):
+                (masked if m else unmasked).append(block_us(self.torch, lambda: self.attention(m), 20))
         t_m, t_u = float(np.median(masked)), float(np.median(unmasked))
         return {"masked_us": t_m, "unmasked_us": t_u, "overhead": t_m / t_u - 1.0,
                 "note": "tv_attention with the tree mask vs tree_mask=NULL on the same KV"}
