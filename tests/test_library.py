@@ -85,3 +85,37 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         tv.tv_build_tree(torch.zeros(1, dtype=torch.int32), torch.zeros((1, 2, 3), dtype=torch.int32),
                          torch.zeros((1, 2, 3)), 3, 0.0, 2)
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    # include/treeverify.h is a plain C header: C99, C11 and C++17, pedantic,
+    # every warning an error
+    import subprocess
+
+    src = tmp_path / "uses_header.c"
+    src.write_text('#include "treeverify.h"\n'
+                   "int main(void) {\n"
+                   "  tv_ctx *ctx = 0;\n"
+                   "  (void)ctx;\n"
+                   "  return tv_status_string(TV_OK)[0] == 0 && tv_tree_budget(1, 64) == 0;\n"
+                   "}\n")
+    inc = os.path.join(ROOT, "include")
+    for cmd in (["gcc", "-std=c99"], ["gcc", "-std=c11"], ["g++", "-std=c++17", "-x", "c++"]):
+        r = subprocess.run(cmd + ["-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only", "-I", inc, str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, (cmd, r.stderr)
+
+
+def test_c_caller_links_and_reports_usage(tmp_path):
+    # the plain-C caller the GPU tests run builds against the library and the
+    # HIP runtime; without arguments it prints its usage before any HIP call
+    import subprocess
+
+    import c_caller_build
+
+    out = str(tmp_path / "c_caller")
+    r = subprocess.run(c_caller_build.command(out), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, LD_LIBRARY_PATH=c_caller_build.LIBDIR)
+    r = subprocess.run([out], capture_output=True, text=True, timeout=60, env=env)
+    assert r.returncode == 2 and "usage" in r.stderr
