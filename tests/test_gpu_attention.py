@@ -246,11 +246,12 @@ def test_binding_checks_arguments():
     assert tv.tv_device_error(DEV) == 0
 
 
-@pytest.mark.parametrize("N,L,slot", [(10, (38, 40), 1), (10, (38, 40), 2), (10, (70, 90), 1), (10, (70, 90), 2),
-                                       (40, (10, 20), 2), (40, (150, 200), 2)],
+@pytest.mark.parametrize("N,L,slot,split", [(10, (38, 40), 1, False), (10, (38, 40), 2, False),
+                                             (10, (400, 450), 1, True), (10, (400, 450), 2, True),
+                                             (40, (10, 20), 2, False), (40, (400, 450), 2, True)],
                          ids=["one-split-first-half", "one-split-second-half", "split-first-half",
                               "split-second-half", "8-waves-one-split-second-half", "8-waves-split-second-half"])
-def test_bad_page_seen_by_either_half(N, L, slot):
+def test_bad_page_seen_by_either_half(N, L, slot, split):
     # a bad page id is found by the wavefronts whose share of the tile it
     # falls in: page slot 1 of a tile by the first half of the workgroup,
     # slot 2 by the second. The first half writes its rows before the final
@@ -259,6 +260,9 @@ def test_bad_page_seen_by_either_half(N, L, slot):
     # directly) and for several (partials merged afterwards), with two
     # wavefronts per workgroup (40 rows) and with eight (160 rows)
     w = small("random", N=N, L=L, B=2)
+    # the plan splits keys exactly when it asks for a workspace
+    need = tv.tv_attention_workspace_bytes(DEV, w.B, w.N, w.Hq, w.Hkv, w.D, w.max_prefix_len)
+    assert (need > 0) == split, need
     bad = w.page_table.copy()
     bad[1, slot] = w.num_pages + 5
     st, _ = oracle.status_attention(w.q, w.k_pages, w.v_pages, bad, w.prefix_lens, None, B=w.B, N=w.N, Hq=w.Hq,
