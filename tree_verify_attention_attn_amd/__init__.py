@@ -97,6 +97,17 @@ def library() -> ctypes.CDLL:
     return _load()
 
 
+# the current stream's raw handle: torch's own fast accessor where it exists
+# (about 0.1 us), else the public one, which builds a Stream object (about 1 us)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_stream(idx: int) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(idx)
+    return torch.cuda.current_stream(idx).cuda_stream
+
+
 def _ctx(device: torch.device):
     """Per-device context, rebound to torch's current stream on every call."""
     if device.type != "cuda":
@@ -105,7 +116,7 @@ def _ctx(device: torch.device):
     lib = _load()
     if idx not in _ctxs:
         h = ctypes.c_void_p()
-        st0 = torch.cuda.current_stream(idx).cuda_stream
+        st0 = _current_stream(idx)
         s = lib.tv_create(ctypes.byref(h), idx, ctypes.c_void_p(st0))
         if s != OK:
             raise TVError(s, "tv_create")
@@ -114,7 +125,7 @@ def _ctx(device: torch.device):
         _ctxs[idx] = h
         _bound[idx] = st0
     h = _ctxs[idx]
-    st = torch.cuda.current_stream(idx).cuda_stream
+    st = _current_stream(idx)
     if _bound.get(idx) != st:  # rebinding orders the new stream after the old one's queued work
         s = lib.tv_set_stream(h, ctypes.c_void_p(st))
         if s != OK:
