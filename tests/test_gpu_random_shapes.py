@@ -67,6 +67,8 @@ def stochastic_shape(i):
               mode="stochastic", T=float(r.choice([0.6, 1.0, 1.7])))
     if tree in ("random", "dynamic"):
         sh.update(max_depth=int(r.integers(2, 9)), topk=int(r.integers(2, 11)))
+    if tree == "dynamic":  # at most the nodes a tree of this depth and top-k holds
+        sh["N"] = min(sh["N"], sum(sh["topk"] ** e for e in range(sh["max_depth"] + 1)))
     return sh
 
 
