@@ -245,8 +245,9 @@ size_t tv_accept_workspace_bytes(int32_t B, int32_t N, int32_t V, tv_accept_mode
  * Adds sum(accept_len) and B to the context's tau counters. Requires
  * 1 <= N <= 128 when B > 0, V >= 1, and B * N * ceil(V / C) <= 2^24 - 1
  * with C = 16384 in GREEDY mode and 8192 in STOCHASTIC mode (one 256-thread
- * workgroup per row and C-token chunk on a 1-D grid); larger calls return
- * TV_ERR_UNSUPPORTED.
+ * workgroup per row and C-token chunk on a 1-D grid), and in STOCHASTIC mode
+ * also B <= 2^23 - 1 (one 512-thread workgroup per sequence); larger calls
+ * return TV_ERR_UNSUPPORTED.
  * In STOCHASTIC mode a small batch splits each sequence's vocabulary over
  * several workgroups that exchange partial sums and wait for each other
  * (bounded); the grid fits the device when nothing else runs on it. Two

@@ -139,6 +139,12 @@ def test_greedy_grid_limit_is_reported():
     st = lib.tv_accept(tv._ctx(DEV), p(dw.target_logits), p(dw.target_logits), p(dw.draft_tokens), p(dw.parents),
                        None, p(ws), rows, 1, V, tv.STOCHASTIC, 1.0, p(out[0]), p(out[1]), p(out[2]), None, p(ws), 64)
     assert st == tv.UNSUPPORTED
+    # 2^23 sequences of one node over a 16-token vocabulary: the chunk grid
+    # fits, the path pass's one 512-thread workgroup per sequence does not
+    st = lib.tv_accept(tv._ctx(DEV), p(dw.target_logits), p(dw.target_logits), p(dw.draft_tokens), p(dw.parents),
+                       None, p(ws), 1 << 23, 1, 16, tv.STOCHASTIC, 1.0, p(out[0]), p(out[1]), p(out[2]), None, p(ws),
+                       64)
+    assert st == tv.UNSUPPORTED
 
 
 @pytest.mark.parametrize("N,V", [(1, 50), (6, 1), (1, 1), (1, 128256)])

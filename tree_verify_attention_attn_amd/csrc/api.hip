@@ -198,6 +198,8 @@ tv_status tv_accept(tv_ctx *ctx, const float *target_logits, const float *draft_
   const int64_t chunk = mode == TV_GREEDY ? 16384 : 8192;
   if (static_cast<int64_t>(B) * N * ((static_cast<int64_t>(V) + chunk - 1) / chunk) * 256 > 0xFFFFFFFFLL)
     return TV_ERR_UNSUPPORTED;
+  // the stochastic path pass: at least one 512-thread workgroup per sequence
+  if (mode == TV_STOCHASTIC && static_cast<int64_t>(B) * 512 > 0xFFFFFFFFLL) return TV_ERR_UNSUPPORTED;
   const size_t need = accept_ws_bytes(B, N, V, mode);
   if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
   return launch_accept(ctx, target_logits, draft_logits, draft_tokens, parents, tree_sizes, uniforms, B, N, V, mode,
