@@ -548,6 +548,40 @@ struct RowStat {
 
 constexpr int kPathThreads = 512;
 constexpr int kBlk = 8;           // tokens per register block of a row sweep
+constexpr int kWaves = kPathThreads / 64;
+constexpr int kRound = 64 * kBlk;  // tokens a wavefront sweeps per round (one block per lane)
+constexpr int kRecords = 64;       // per-wavefront mass records of a sweep
+constexpr int kLaneRounds = 8;     // rounds whose per-lane block sums a sweep keeps in LDS
+
+// x moved across lanes by the DPP control `ctrl` (rows or banks masked off, and
+// lanes with no source when bound_ctrl is set, read 0)
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ inline double dpp_f64(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), kCtrl, kRowMask, 0xf, kBound);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), kCtrl, kRowMask, 0xf, kBound);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// inclusive scan over the 64 lanes of a wavefront in a fixed order: within
+// each 16-lane row by shifts of 1, 2, 4 and 8, then row 0's total into row
+// 1, row 2's into row 3, and the first half's total into the second half
+__device__ inline double wave_incl_dpp(double x) {
+  x += dpp_f64<0x111, 0xf, true>(x);  // row_shr:1
+  x += dpp_f64<0x112, 0xf, true>(x);  // row_shr:2
+  x += dpp_f64<0x114, 0xf, true>(x);  // row_shr:4
+  x += dpp_f64<0x118, 0xf, true>(x);  // row_shr:8
+  x += dpp_f64<0x142, 0xa, false>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_f64<0x143, 0xc, false>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+__device__ inline double lane_f64(double x, int src) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), src);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), src);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
 constexpr int kMaxGrid = 256;     // workgroups of a path pass that exchange partial sums
 constexpr int kMaxExchanges = 128;  // exchanges per sequence: < N stored residuals + 2 draw passes
 constexpr int kCounterStride = 16;  // one 128-byte line per sequence counter
@@ -588,8 +622,13 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     double *__restrict__ wbuf,
     unsigned long long *__restrict__ sync, int K, int slice, int32_t *__restrict__ accept_len,
     int32_t *__restrict__ path, int32_t *__restrict__ bonus, unsigned long long *state) {
-  __shared__ int s_err, s_ok, s_pick, s_cross, s_cross_last, s_lp;
-  __shared__ double s_wave[kPathThreads / 64], s_wpre[kPathThreads / 64], s_total, s_cprefix, s_wt_new, s_wt_old;
+  __shared__ int s_err, s_ok, s_pick, s_lp;
+  __shared__ double s_wave[kWaves], s_wpre[kWaves], s_total, s_wt_new, s_wt_old;
+  // each wavefront's mass in records of rec_rounds consecutive rounds, and
+  // its last token of positive weight (the last sweep's)
+  __shared__ double s_wrec[kWaves][kRecords];
+  __shared__ double s_lsum[kLaneRounds][kPathThreads];  // each lane's block sum of the first rounds
+  __shared__ int s_wlp[kWaves];
   __shared__ double s_pa[128], s_qa[128], s_u[128];
   __shared__ RowStat s_tst[128], s_dst[128];  // merged statistics of every target and draft row
   __shared__ int s_tok[128], s_path[128];
@@ -614,11 +653,20 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   };
   const int nb = sizes ? sizes[b] : N;
   const bool bad_size = nb < 1 || nb > N;
-  // this workgroup's slice, split into contiguous per-thread segments
-  // (multiples of 4 tokens)
+  // this workgroup's slice [v0, v1): each wavefront owns a contiguous range
+  // of `rounds` rounds; in round r lane l takes the kBlk tokens at
+  // wa0 + r kRound + l kBlk, so a wavefront's loads are contiguous and the
+  // token order is (wavefront, round, lane, token). A sweep records each
+  // wavefront's mass per group of rec_rounds rounds, so that the final draw
+  // finds the token where the running sum passes theta by recomputing one
+  // round of one wavefront.
   const int v0 = min(kk * slice, V), v1 = min(v0 + slice, V);
-  const int seg = ((v1 - v0 + 4 * kPathThreads - 1) / (4 * kPathThreads)) * 4;
-  const int x0 = min(v0 + tid * seg, v1), x1 = min(x0 + seg, v1);
+  const int rounds = (v1 - v0 + kWaves * kRound - 1) / (kWaves * kRound);
+  const int rec_rounds = max(1, (rounds + kRecords - 1) / kRecords);
+  auto range0 = [&](int w) { return min(v0 + w * rounds * kRound, v1); };
+  const int wa0 = range0(wid), wa1 = range0(wid + 1);
+  const int x0 = wa0 + lane * kBlk;  // this lane's block in round 0
+  const int x1 = wa1;                // every load of the wavefront stops here
   auto load_block = [&](const float *row, int xb, float (&v)[kBlk]) __attribute__((always_inline)) {
     if (kVec) {  // V % 4 == 0 and xb % 4 == 0: a float4 is either all in [x0, x1) or all out
 #pragma unroll
@@ -692,7 +740,6 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     if (lane == 0) {
       s_err = err;
       s_pick = 0x7FFFFFFF;
-      s_cross = 0x7FFFFFFF;
       s_lp = -1;
       s_wt_new = 0.0;
       s_wt_old = 0.0;
@@ -762,16 +809,16 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   double *const buf0 = wbuf + static_cast<int64_t>(b) * 2 * V;
   double *const buf1 = buf0 + V;
 
-  // pi's weight of one token (the target row's probability, or the stored
-  // residual's entry)
-  auto base_weight = [&](const RowStat &sp, const Pi &pi, float pl, double wl) __attribute__((always_inline)) {
-    return pi.w ? wl : exp_tab(scaled(pl) - sp.m, s_tab) * sp.invZ;  // padding (-inf) gives 0
+  // a token's weight under pi when pi is a target row (padding, -inf, gives
+  // 0), and the residual max(0, pi - q) with pi normalised; the sweeps and
+  // the final draw's recomputation share these forms
+  auto block_w0 = [&](float pl, const RowStat &sp) __attribute__((always_inline)) {
+    return exp_tab(scaled(pl) - sp.m, s_tab) * sp.invZ;
   };
-  // with a sibling's draft row: the residual max(0, pi - q) with pi normalised
-  auto resid_weight = [&](double w, const Pi &pi, const RowStat &sq, float ql) __attribute__((always_inline)) {
-    return fmax(0.0, w * pi.invM - exp_tab(scaled(ql) - sq.m, s_tab) * sq.invZ);
+  auto block_resid = [&](double w0, const Pi &pi, float ql, const RowStat &sq) __attribute__((always_inline)) {
+    return fmax(0.0, w0 * pi.invM - exp_tab(scaled(ql) - sq.m, s_tab) * sq.invZ);
   };
-  // one sweep of this thread's segment; stores every weight into dst if
+  // one sweep of this wavefront's range; stores every weight into dst if
   // given; the thread holding token tnext records pi's old and new weight
   // there. The form (pi stored or a target row, with or without a sibling's
   // draft row, with or without dst) is chosen once per sweep, so a block of
@@ -784,6 +831,8 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     constexpr bool kW = decltype(has_w)::value, kQ = decltype(has_q)::value, kDst = decltype(has_dst)::value;
     local = 0.0;
     lastpos = -1;
+    const int nr = wa0 < wa1 ? rounds : 0;  // a wavefront with an empty range has no rounds
+    double rec = 0.0;
     float pv[kBlk], qv[kBlk], pn[kBlk], qn[kBlk];
     double wv[kBlk], wn[kBlk];
     if constexpr (kW) {
@@ -808,30 +857,43 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       qpre_node = qnext_node;
     }
     double w0_at = 0.0, w_at = 0.0;
-    for (int xb = x0; xb < x1; xb += kBlk) {
-      if (xb + kBlk < x1) {
+    bool have_at = false;
+    for (int r = 0; r < nr; ++r) {
+      const int xb = x0 + r * kRound;
+      if (r + 1 < nr) {
         if constexpr (kW)
-          load_wblock(pi.w, xb + kBlk, wn);
+          load_wblock(pi.w, xb + kRound, wn);
         else
-          load_block(P, xb + kBlk, pn);
-        if constexpr (kQ) load_block(Q, xb + kBlk, qn);
+          load_block(P, xb + kRound, pn);
+        if constexpr (kQ) load_block(Q, xb + kRound, qn);
       }
       double wb[kBlk];
+      double bs = 0.0;
 #pragma unroll
       for (int i = 0; i < kBlk; ++i) {
         double w0;
         if constexpr (kW)
           w0 = wv[i];
         else
-          w0 = exp_tab(scaled(pv[i]) - sp.m, s_tab) * sp.invZ;  // padding (-inf) gives 0
+          w0 = block_w0(pv[i], sp);
         double w = w0;
-        if constexpr (kQ) w = fmax(0.0, w0 * pi.invM - exp_tab(scaled(qv[i]) - sq.m, s_tab) * sq.invZ);
+        if constexpr (kQ) w = block_resid(w0, pi, qv[i], sq);
         wb[i] = w;
-        local += w;
+        bs += w;
         lastpos = w > 0.0 ? xb + i : lastpos;
         const bool at = xb + i == tnext;
+        have_at |= at;
         w0_at = at ? w0 : w0_at;
         w_at = at ? w : w_at;
+      }
+      // the round's mass over the wavefront (the same fixed-order scan the
+      // final draw repeats), added to the current record
+      if (r < kLaneRounds) s_lsum[r][tid] = bs;
+      rec += lane_f64(wave_incl_dpp(bs), 63);
+      if ((r + 1) % rec_rounds == 0 || r + 1 == nr) {
+        if (lane == 0) s_wrec[wid][r / rec_rounds] = rec;
+        local += rec;
+        rec = 0.0;
       }
       if constexpr (kDst) {
         if (xb + kBlk <= x1) {
@@ -850,7 +912,7 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
         wv[i] = wn[i];
       }
     }
-    if (tnext >= x0 && tnext < x1) {
+    if (have_at) {
       s_wt_old = w0_at;
       s_wt_new = w_at;
     }
@@ -877,21 +939,17 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
         sweep_form(T0(), T0(), T0(), P, pnode, sp, pi, Q, qnode, sq, Qnext, qnext_node, dst, tnext, local, lastpos);
     }
   };
-  // exclusive prefix of the segment sums within the workgroup and the
-  // workgroup's total: a fixed-order scan within each wavefront, then over
-  // the wavefront totals in order
-  auto scan = [&](double local, int lastpos, double &prefix) __attribute__((always_inline)) {
-    double incl = local;
-    for (int d = 1; d < 64; d <<= 1) {
-      const double t = __shfl_up(incl, d);
-      if (lane >= d) incl += t;
-    }
-    double excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = 0.0;
-    if (lane == 63) s_wave[wid] = incl;
+  // the workgroup's total and each wavefront's exclusive prefix, summed over
+  // the wavefront masses in order; the last token of positive weight of
+  // each wavefront and of the workgroup
+  auto scan = [&](double wave_mass, int lastpos) __attribute__((always_inline)) {
     int lp = lastpos;
     for (int d = 32; d >= 1; d >>= 1) lp = max(lp, __shfl_xor(lp, d));
-    if (lane == 0 && lp >= 0) atomicMax(&s_lp, lp);
+    if (lane == 0) {
+      s_wave[wid] = wave_mass;
+      s_wlp[wid] = lp;
+      if (lp >= 0) atomicMax(&s_lp, lp);
+    }
     __syncthreads();
     if (tid == 0) {
       double run = 0.0;
@@ -902,7 +960,6 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       s_total = run;
     }
     __syncthreads();
-    prefix = s_wpre[wid] + excl;
   };
   // the exchange among the K workgroups of this sequence; fills s_part,
   // s_xnew, s_xold, s_xlp with every slice's values (thread 0 publishes this
@@ -1023,14 +1080,14 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       }
       double *dst = pi.w == buf0 ? buf1 : buf0;
       const RowStat sq = s_dst[c];
-      double local, prefix;
+      double local;
       int lastpos;
       const int next = kids0 ? __builtin_ctzll(kids0) : 64 + __builtin_ctzll(kids1);
       // the next sibling's row is swept next (rejected with siblings left, or
       // as the final draw's residual)
       sweep(P, node, sp, pi, draft + (base + c) * V, c, sq, draft + (base + next) * V, next, dst, s_tok[next], local,
             lastpos);
-      scan(local, lastpos, prefix);
+      scan(local, lastpos);
       if (!(ok = exchange())) break;
       const double total = s_sum, wnew = s_sum_new, wold = s_sum_old;
       if (total > 0.0) {
@@ -1057,10 +1114,10 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const double u = s_u[N - 1];
     for (int pass = 0; pass < 2; ++pass) {
       const float *Qp = pass == 0 ? Q : nullptr;
-      double local, prefix;
+      double local;
       int lastpos;
       sweep(P, node, sp, pi, Qp, pass == 0 ? pend : -1, sq, nullptr, -1, nullptr, -1, local, lastpos);
-      scan(local, lastpos, prefix);
+      scan(local, lastpos);
       if (!(ok = exchange())) break;
       const double total = s_sum;
       const int glast = s_glast;
@@ -1073,40 +1130,69 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       writer = cross_wg >= 0 ? cross_wg : 0;
       pick = glast;  // rounding left no crossing: the last token of positive weight
       if (cross_wg == kk) {
-        // the first segment of this slice whose running sum passes theta
-        const double pre = wg_prefix + prefix;
-        if (pre + local > theta) atomicMin(&s_cross, tid);
-        __syncthreads();
-        if (tid == s_cross) {
-          s_cprefix = pre;
-          s_cross_last = lastpos;
-        }
-        __syncthreads();
-        // wavefront 0 re-sweeps the crossing segment one token per lane: a
-        // fixed-order scan of the weights gives each token's running sum
-        const int cross = s_cross;
-        if (wid == 0 && cross != 0x7FFFFFFF) {
-          const int cx0 = min(v0 + cross * seg, v1), cx1 = min(cx0 + seg, v1);
-          double carry = s_cprefix;
-          int found = -1;
-          for (int xb = cx0; xb < cx1 && found < 0; xb += 64) {
-            const int x = xb + lane;
-            double w = 0.0;
-            if (x < cx1) {
-              w = base_weight(sp, pi, pi.w ? 0.f : P[x], pi.w ? pi.w[x] : 0.0);
-              if (Qp) w = resid_weight(w, pi, sq, Qp[x]);
+        // wavefront 0 narrows the crossing down: the first wavefront range,
+        // then record, round, lane and token whose running sum passes theta
+        // (each level's sums in the order the sweep formed them); where
+        // rounding leaves no crossing inside the range found, the range's
+        // last token of positive weight
+        if (wid == 0) {
+          const uint64_t wr_hit = __builtin_amdgcn_ballot_w64(
+              lane < kWaves && wg_prefix + s_wpre[min(lane, kWaves - 1)] + s_wave[min(lane, kWaves - 1)] > theta);
+          if (wr_hit) {
+            const int wc = static_cast<int>(__builtin_ctzll(wr_hit));
+            const int ca0 = range0(wc), ca1 = range0(wc + 1);
+            double run = wg_prefix + s_wpre[wc];
+            int found = -1;
+            const int nrec = (rounds + rec_rounds - 1) / rec_rounds;
+            for (int q = 0; q < nrec && found < 0; ++q) {
+              const double rm = s_wrec[wc][q];
+              if (!(run + rm > theta)) {
+                run += rm;
+                continue;
+              }
+              for (int r = q * rec_rounds; r < min((q + 1) * rec_rounds, rounds) && found < 0; ++r) {
+                const int xr = ca0 + r * kRound;  // the round's first token
+                // a token's weight, as the sweep formed it (0 past the range)
+                auto token_w = [&](int x) __attribute__((always_inline)) -> double {
+                  if (x >= ca1) return 0.0;
+                  const double w0 = pi.w ? pi.w[x] : block_w0(P[x], sp);
+                  return Qp ? block_resid(w0, pi, Qp[x], sq) : w0;
+                };
+                // each lane's block sum: kept by the sweep for the first
+                // rounds, recomputed in the same order otherwise
+                double bs = 0.0;
+                if (r < kLaneRounds) {
+                  bs = s_lsum[r][wc * 64 + lane];
+                } else {
+#pragma unroll
+                  for (int i = 0; i < kBlk; ++i) bs += token_w(xr + lane * kBlk + i);
+                }
+                const double incl = wave_incl_dpp(bs);
+                const uint64_t lhit = __builtin_amdgcn_ballot_w64(run + incl > theta);
+                if (lhit) {
+                  // the crossing block: lanes 0..kBlk-1 recompute its tokens,
+                  // whose running sum is then taken in token order
+                  const int lc = static_cast<int>(__builtin_ctzll(lhit));
+                  const int xl = xr + lc * kBlk;
+                  const double wi = lane < kBlk ? token_w(xl + lane) : 0.0;
+                  double c = run + (lc > 0 ? lane_f64(incl, lc - 1) : 0.0);
+                  int f = -1, lpos = -1;
+#pragma unroll
+                  for (int i = 0; i < kBlk; ++i) {
+                    const double w = lane_f64(wi, i);
+                    c += w;
+                    lpos = w > 0.0 ? xl + i : lpos;
+                    if (f < 0 && c > theta) f = xl + i;
+                  }
+                  found = f >= 0 ? f : (lpos >= 0 ? lpos : s_wlp[wc]);
+                }
+                run += lane_f64(incl, 63);
+              }
+              if (found < 0) found = s_wlp[wc];
             }
-            double rs = w;
-            for (int d = 1; d < 64; d <<= 1) {
-              const double t = __shfl_up(rs, d);
-              if (lane >= d) rs += t;
-            }
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(x < cx1 && carry + rs > theta);
-            if (hit) found = xb + __builtin_ctzll(hit);
-            carry += __shfl(rs, 63);
+            if (found < 0) found = s_wlp[wc];
+            if (lane == 0 && found >= 0) s_pick = found;
           }
-          const int pk = found >= 0 ? found : s_cross_last;  // no crossing after rounding: segment's last positive
-          if (lane == 0 && pk >= 0) s_pick = pk;
         }
         __syncthreads();
         if (s_pick != 0x7FFFFFFF) pick = s_pick;
