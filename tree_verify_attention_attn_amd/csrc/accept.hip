@@ -703,6 +703,22 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       l_qa = draft[(base + tid) * V + t];
     }
   }
+  // the chunk statistics of each thread's first row (see the merge below),
+  // loaded now so that their latency overlaps the validation
+  constexpr int kPreChunks = 4;  // per thread: chunks sub, sub + 4, ...
+  const int sub = tid & 3;
+  const bool pre_ok = !bad_size && (tid >> 2) < 2 * nb && chunks <= 4 * kPreChunks;
+  double pre_m[kPreChunks], pre_s[kPreChunks];
+  if (pre_ok) {
+    const int r = tid >> 2;
+    const double *st = stats + ((base + (r >> 1)) * 2 + (r & 1)) * chunks * 2;
+#pragma unroll
+    for (int j = 0; j < kPreChunks; ++j) {
+      const int c = sub + 4 * j;
+      pre_m[j] = c < chunks ? st[2 * c] : -INFINITY;
+      pre_s[j] = c < chunks ? st[2 * c + 1] : 0.0;
+    }
+  }
   if (wid == 0) {
     // validation with the same precedence as a serial check: a node count
     // outside [1, N], a bad parent among the present nodes, then a draft
@@ -757,17 +773,26 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   // fourth chunk, combined in a fixed butterfly so that all four, and every
   // workgroup of the sequence, hold the same values
   if (!bad_size) {
-    const int sub = tid & 3;
     for (int r = tid >> 2; r < 2 * nb; r += kPathThreads / 4) {
       const int node = r >> 1, which = r & 1;
       const double *st = stats + ((base + node) * 2 + which) * chunks * 2;
       double M = -INFINITY;
-      for (int c = sub; c < chunks; c += 4) M = fmax(M, st[2 * c]);
-      M = fmax(M, __shfl_xor(M, 1));
-      M = fmax(M, __shfl_xor(M, 2));
       double Z = 0.0;
-      for (int c = sub; c < chunks; c += 4)
-        if (st[2 * c + 1] > 0.0) Z += st[2 * c + 1] * exp_tab(st[2 * c] - M, s_tab);
+      if (pre_ok && r == (tid >> 2)) {
+#pragma unroll
+        for (int j = 0; j < kPreChunks; ++j) M = fmax(M, pre_m[j]);
+        M = fmax(M, __shfl_xor(M, 1));
+        M = fmax(M, __shfl_xor(M, 2));
+#pragma unroll
+        for (int j = 0; j < kPreChunks; ++j)
+          if (pre_s[j] > 0.0) Z += pre_s[j] * exp_tab(pre_m[j] - M, s_tab);
+      } else {
+        for (int c = sub; c < chunks; c += 4) M = fmax(M, st[2 * c]);
+        M = fmax(M, __shfl_xor(M, 1));
+        M = fmax(M, __shfl_xor(M, 2));
+        for (int c = sub; c < chunks; c += 4)
+          if (st[2 * c + 1] > 0.0) Z += st[2 * c + 1] * exp_tab(st[2 * c] - M, s_tab);
+      }
       Z += __shfl_xor(Z, 1);
       Z += __shfl_xor(Z, 2);
       if (sub == 0) {
