@@ -323,6 +323,18 @@ def test_stochastic_star_sliced_vocab(B, V):
     stochastic_compare(w, f"star-sliced-B{B}-V{V}")
 
 
+@pytest.mark.parametrize("V", [300000, 266241])
+def test_stochastic_one_slice_many_rounds(V):
+    # enough sequences that each one's vocabulary is one workgroup's slice,
+    # and a vocabulary long enough that a wavefront sweeps more than 64 rounds
+    # of 512 tokens: the final draw finds its round among records of two
+    # rounds and recomputes the lanes' block sums (kept in LDS only for the
+    # first rounds); an odd V takes the scalar loads
+    w = tvgen.make_workload(5, seed=64, with_kv=False, overrides=dict(B=136, N=2, V=V))
+    ref = stochastic_compare(w, f"one-slice-B136-V{V}")
+    assert (ref["accept_len"] == 1).any() and (ref["accept_len"] == 2).any()
+
+
 def test_tau_accumulates_over_calls():
     tv.tv_tau_reset(DEV)
     lens = []
