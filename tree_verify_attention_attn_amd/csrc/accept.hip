@@ -599,21 +599,24 @@ struct Pi {
 // workgroup validates the tree and builds the children of every node as a
 // bit mask; all threads merge the row statistics and compute for every node
 // c its first test's p(t_c) (under its parent's target row) and q_c(t_c);
-// all threads of all K workgroups then take the same walk from these copies. The current node's children are tested in
-// id order; a rejection followed by another sibling stores the residual
-// max(0, pi - q_c) of the vocabulary (each workgroup its slice, in one of
-// two per-sequence rows) and the next sibling is tested against it. The
-// final draw - from the last rejected sibling's residual (built on the fly)
-// or from pi - sweeps the slices once in contiguous token-order segments
-// (8-token register blocks, next block's loads issued before the current
-// block's exponentials). Every sweep ends in an exchange: each workgroup
+// all threads of all K workgroups then take the same walk from these copies.
+// The current node's children are tested in id order; a rejection followed
+// by another sibling stores the residual max(0, pi - q_c) of the vocabulary
+// (each workgroup its slice, in one of two per-sequence rows) and the next
+// sibling is tested against it. The final draw - from the last rejected
+// sibling's residual (built on the fly) or from pi - sweeps the slices once.
+// A sweep gives each wavefront a contiguous range of its workgroup's slice,
+// taken in rounds in which lane l holds the 8-token block at 8 l, so every
+// wavefront load is contiguous (the next round's loads are issued before the
+// current round's exponentials). Every sweep ends in an exchange: each workgroup
 // publishes its slice's mass, pi's old and new weight at the next sibling's
 // token, and its last positive token through device-scope atomics, counts
 // itself in, and waits (bounded) until all K have; wavefront 0 then reduces
 // the K slices in a fixed order, so every workgroup reaches the same
-// decisions. T = 1 has a form of its own (no division of the logits). For the draw,
-// the first slice (then segment) whose running sum passes theta is found,
-// and only that segment is swept again, one token per lane of a wavefront.
+// decisions. T = 1 has a form of its own (no division of the logits). For the
+// draw, the first slice whose running sum passes theta is found, then in it
+// the wavefront range, round, lane and token, from the masses the sweep kept;
+// only the 8 weights of one block are computed again.
 template <bool kVec, bool kUnitT>
 __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
@@ -848,7 +851,7 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   // there. The form (pi stored or a target row, with or without a sibling's
   // draft row, with or without dst) is chosen once per sweep, so a block of
   // 8 tokens is straight-line code: its 8 (or 16) exponentials overlap, and
-  // per-token conditions are selects (tokens past the segment weigh 0).
+  // per-token conditions are selects (tokens past the range weigh 0).
   auto sweep_form = [&](auto has_w, auto has_q, auto has_dst, const float *P, int pnode, const RowStat &sp,
                         const Pi &pi, const float *Q, int qnode, const RowStat &sq, const float *Qnext,
                         int qnext_node, double *dst, int tnext, double &local, int &lastpos)
