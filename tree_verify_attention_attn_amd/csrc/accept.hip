@@ -771,6 +771,11 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   // the statistics merge, the next sibling's row during each sweep
   float ppre[kBlk], qpre[kBlk];
   int ppre_node = -1, qpre_node = -1;
+  // the lane's round-0 block of the residual the last storing sweep wrote:
+  // the next sweep over that residual reads exactly these tokens of it, so
+  // it takes them from here instead of from memory
+  double wcache[kBlk];
+  const double *wcache_row = nullptr;
   // statistics of every present row (target and draft of each node) from
   // its chunks' (max, sum of exp): four threads per row, each taking every
   // fourth chunk, combined in a fixed butterfly so that all four, and every
@@ -864,7 +869,12 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     float pv[kBlk], qv[kBlk], pn[kBlk], qn[kBlk];
     double wv[kBlk], wn[kBlk];
     if constexpr (kW) {
-      load_wblock(pi.w, x0, wv);
+      if (pi.w == wcache_row) {
+#pragma unroll
+        for (int i = 0; i < kBlk; ++i) wv[i] = wcache[i];
+      } else {
+        load_wblock(pi.w, x0, wv);
+      }
     } else if (pnode == ppre_node) {
 #pragma unroll
       for (int i = 0; i < kBlk; ++i) pv[i] = ppre[i];
@@ -924,6 +934,10 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
         rec = 0.0;
       }
       if constexpr (kDst) {
+        if (r == 0) {
+#pragma unroll
+          for (int i = 0; i < kBlk; ++i) wcache[i] = wb[i];
+        }
         if (xb + kBlk <= x1) {
 #pragma unroll
           for (int i = 0; i < kBlk; ++i) dst[xb + i] = wb[i];
@@ -944,6 +958,7 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
       s_wt_old = w0_at;
       s_wt_new = w_at;
     }
+    if constexpr (kDst) wcache_row = nr > 0 ? dst : nullptr;
   };
   auto sweep = [&](const float *P, int pnode, const RowStat &sp, const Pi &pi, const float *Q, int qnode,
                    const RowStat &sq, const float *Qnext, int qnext_node, double *dst, int tnext, double &local,
