@@ -636,8 +636,6 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   __shared__ RowStat s_tst[128], s_dst[128];  // merged statistics of every target and draft row
   __shared__ int s_tok[128], s_path[128];
   __shared__ unsigned long long s_child[128][2];  // children of each node: ids 0..63, 64..127
-  __shared__ double s_part[kMaxGrid], s_xnew[kMaxGrid], s_xold[kMaxGrid];
-  __shared__ int s_xlp[kMaxGrid];
   // the exchange's fixed-order reductions over the K slices: total mass, the
   // new and old weights at the next sibling's token, the last positive token,
   // and each slice's exclusive prefix of the mass
@@ -1004,91 +1002,92 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     }
     __syncthreads();
   };
-  // the exchange among the K workgroups of this sequence; fills s_part,
-  // s_xnew, s_xold, s_xlp with every slice's values (thread 0 publishes this
-  // workgroup's and resets the per-sweep records); false if a peer never
+  // the exchange among the K workgroups of this sequence: every slice's mass
+  // (as exclusive and inclusive prefixes), weight sums and last positive
+  // token into LDS, and the per-sweep records reset; false if a peer never
   // arrived
   int nx = 0;
   auto exchange = [&]() __attribute__((always_inline)) {
-    if (K == 1) {
-      if (tid == 0) {
-        s_part[0] = s_total;
-        s_xnew[0] = s_wt_new;
-        s_xold[0] = s_wt_old;
-        s_xlp[0] = s_lp;
-        s_wt_new = 0.0;
-        s_wt_old = 0.0;
-        s_lp = -1;
-        s_ok = 1;
-      }
-    } else {
-      unsigned long long *cnt = sync + static_cast<int64_t>(b) * kCounterStride;
-      unsigned long long *slots = sync + static_cast<int64_t>(B) * kCounterStride +
-                                  (static_cast<int64_t>(nx) * kMaxGrid + static_cast<int64_t>(b) * K) * 4;
-      if (tid == 0) {
-        unsigned long long *mine = slots + kk * 4;
-        atomicExch(mine + 0, static_cast<unsigned long long>(__double_as_longlong(s_total)));
-        atomicExch(mine + 1, static_cast<unsigned long long>(__double_as_longlong(s_wt_new)));
-        atomicExch(mine + 2, static_cast<unsigned long long>(__double_as_longlong(s_wt_old)));
-        atomicExch(mine + 3, static_cast<unsigned long long>(static_cast<long long>(s_lp)));
-        s_wt_new = 0.0;
-        s_wt_old = 0.0;
-        s_lp = -1;
-        // the four values are in place before this workgroup is counted in
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        atomicAdd(cnt, 1ull);
-        const unsigned long long want = static_cast<unsigned long long>(K) * (nx + 1);
-        int ok = 0;
-        for (int it = 0; it < kSpinLimit; ++it) {
-          if (atomicAdd(cnt, 0ull) >= want) {
-            ok = 1;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
+    // wavefront 0 publishes this workgroup's values, gathers every slice's
+    // (lane i = slice i, K <= 64) and reduces them; the other wavefronts
+    // wait at the closing barrier
+    if (wid == 0) {
+      double m = 0.0, wn = 0.0, wo = 0.0;
+      int lp = -1, ok = 1;
+      if (K == 1) {
+        if (lane == 0) {
+          m = s_total;
+          wn = s_wt_new;
+          wo = s_wt_old;
+          lp = s_lp;
         }
+      } else {
+        unsigned long long *cnt = sync + static_cast<int64_t>(b) * kCounterStride;
+        unsigned long long *slots = sync + static_cast<int64_t>(B) * kCounterStride +
+                                    (static_cast<int64_t>(nx) * kMaxGrid + static_cast<int64_t>(b) * K) * 4;
+        if (lane == 0) {
+          unsigned long long *mine = slots + kk * 4;
+          atomicExch(mine + 0, static_cast<unsigned long long>(__double_as_longlong(s_total)));
+          atomicExch(mine + 1, static_cast<unsigned long long>(__double_as_longlong(s_wt_new)));
+          atomicExch(mine + 2, static_cast<unsigned long long>(__double_as_longlong(s_wt_old)));
+          atomicExch(mine + 3, static_cast<unsigned long long>(static_cast<long long>(s_lp)));
+          // the four values are in place before this workgroup is counted in
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          atomicAdd(cnt, 1ull);
+          const unsigned long long want = static_cast<unsigned long long>(K) * (nx + 1);
+          ok = 0;
+          for (int it = 0; it < kSpinLimit; ++it) {
+            if (atomicAdd(cnt, 0ull) >= want) {
+              ok = 1;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        ok = __shfl(ok, 0);
+        if (ok && lane < K) {
+          auto *theirs = slots + lane * 4;
+          m = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 0, 0ull)));
+          wn = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 1, 0ull)));
+          wo = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 2, 0ull)));
+          lp = static_cast<int>(static_cast<long long>(atomicAdd(theirs + 3, 0ull)));
+        }
+      }
+      if (lane == 0) {  // the per-sweep records start again
+        s_wt_new = 0.0;
+        s_wt_old = 0.0;
+        s_lp = -1;
         s_ok = ok;
       }
-      __syncthreads();
-      if (s_ok && tid < K) {
-        auto *theirs = slots + tid * 4;
-        s_part[tid] = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 0, 0ull)));
-        s_xnew[tid] = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 1, 0ull)));
-        s_xold[tid] = __longlong_as_double(static_cast<long long>(atomicAdd(theirs + 2, 0ull)));
-        s_xlp[tid] = static_cast<int>(static_cast<long long>(atomicAdd(theirs + 3, 0ull)));
+      if (ok) {
+        // the slices' masses as an inclusive scan (the total is the last
+        // lane's), the weight sums and the last positive token, each in a
+        // fixed order
+        double incl = m;
+        for (int d = 1; d < 64; d <<= 1) {
+          const double t = __shfl_up(incl, d);
+          if (lane >= d) incl += t;
+        }
+        for (int d = 32; d >= 1; d >>= 1) {
+          wn += __shfl_xor(wn, d);
+          wo += __shfl_xor(wo, d);
+          lp = max(lp, __shfl_xor(lp, d));
+        }
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = 0.0;
+        if (lane < K) {
+          s_pre[lane] = excl;
+          s_inc[lane] = incl;
+        }
+        if (lane == K - 1) s_sum = incl;
+        if (lane == 0) {
+          s_sum_new = wn;
+          s_sum_old = wo;
+          s_glast = lp;
+        }
       }
     }
     ++nx;
-    __syncthreads();
-    // wavefront 0, lane i = slice i (K <= 64): the slices' masses as an
-    // inclusive scan (the total is the last lane's), the weight sums and the
-    // last positive token, each in a fixed order
-    if (wid == 0 && s_ok) {
-      const bool in = lane < K;
-      double m = in ? s_part[lane] : 0.0, wn = in ? s_xnew[lane] : 0.0, wo = in ? s_xold[lane] : 0.0;
-      int lp = in ? s_xlp[lane] : -1;
-      double incl = m;
-      for (int d = 1; d < 64; d <<= 1) {
-        const double t = __shfl_up(incl, d);
-        if (lane >= d) incl += t;
-      }
-      for (int d = 32; d >= 1; d >>= 1) {
-        wn += __shfl_xor(wn, d);
-        wo += __shfl_xor(wo, d);
-        lp = max(lp, __shfl_xor(lp, d));
-      }
-      double excl = __shfl_up(incl, 1);
-      if (lane == 0) excl = 0.0;
-      if (in) {
-        s_pre[lane] = excl;
-        s_inc[lane] = incl;
-      }
-      if (lane == K - 1) s_sum = incl;
-      if (lane == 0) {
-        s_sum_new = wn;
-        s_sum_old = wo;
-        s_glast = lp;
-      }
-    }
     __syncthreads();
     return s_ok != 0;
   };
