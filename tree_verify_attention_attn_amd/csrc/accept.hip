@@ -616,7 +616,8 @@ struct Pi {
 // decisions. T = 1 has a form of its own (no division of the logits). For the
 // draw, the first slice whose running sum passes theta is found, then in it
 // the wavefront range, round, lane and token, from the masses the sweep kept;
-// only the 8 weights of one block are computed again.
+// only the 8 weights of one block are computed again (and, past the rounds
+// whose lane sums the sweep keeps, that round's lane sums).
 template <bool kVec, bool kUnitT>
 __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
     const float *__restrict__ target, const float *__restrict__ draft, const int32_t *__restrict__ draft_tokens,
@@ -658,9 +659,11 @@ __global__ void __launch_bounds__(kPathThreads) stochastic_path_kernel(
   // of `rounds` rounds; in round r lane l takes the kBlk tokens at
   // wa0 + r kRound + l kBlk, so a wavefront's loads are contiguous and the
   // token order is (wavefront, round, lane, token). A sweep records each
-  // wavefront's mass per group of rec_rounds rounds, so that the final draw
-  // finds the token where the running sum passes theta by recomputing one
-  // round of one wavefront.
+  // wavefront's mass per group of rec_rounds rounds (and, for the first
+  // kLaneRounds rounds, every lane's block sum), so that the final draw finds
+  // the token where the running sum passes theta by recomputing one block of
+  // one wavefront (past those rounds, the lane sums of the rounds of one
+  // record).
   const int v0 = min(kk * slice, V), v1 = min(v0 + slice, V);
   const int rounds = (v1 - v0 + kWaves * kRound - 1) / (kWaves * kRound);
   const int rec_rounds = max(1, (rounds + kRecords - 1) / kRecords);
