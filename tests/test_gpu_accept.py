@@ -335,6 +335,20 @@ def test_stochastic_one_slice_many_rounds(V):
     assert (ref["accept_len"] == 1).any() and (ref["accept_len"] == 2).any()
 
 
+@pytest.mark.parametrize("B,N,V", [(130, 16, 20000), (100, 8, 100000)])
+def test_stochastic_star_multi_round_slices(B, N, V):
+    # stored residuals swept in several rounds per wavefront: one workgroup
+    # per sequence with 5 rounds (B = 130), and two per sequence with 13
+    # rounds, past the rounds whose lane sums the sweep keeps (B = 100); the
+    # first round of a stored residual comes from registers, the others from
+    # memory
+    w = tvgen.make_workload(5, seed=65, with_kv=False, overrides=dict(B=B, N=N, V=V, tree="star"))
+    w.draft_logits *= 2.5
+    w.draft_tokens[:, 1:] = tvgen.gumbel_argmax(65, 98, w.draft_logits, 1.0)[:, 1:]
+    ref = stochastic_compare(w, f"star-rounds-B{B}-N{N}-V{V}")
+    assert (ref["accept_len"] == 1).any()
+
+
 def test_tau_accumulates_over_calls():
     tv.tv_tau_reset(DEV)
     lens = []
